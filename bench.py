@@ -1,0 +1,349 @@
+"""Benchmark of the dynamic-FP8 hot path on one MI355X.
+
+One step runs every step of the path over the five synthetic workloads, inputs
+already resident in HBM:
+  linear_tensorwise  fp8_linear_fwd, X [256,512] W [512,512], one scale each, fp32 out
+  linear_rowwise     Llama3-8B MLP (tokens 8192, K 4096, N 14336): rowwise quant of X, W
+                     (e4m3) and grad_out (e5m2), per-column transposed quant of W, FP8
+                     forward and grad-input GEMMs, BF16 weight-gradient GEMM
+  expert_colwise     per-expert column scales + transposed cast, 32 x [2048,7168]
+  moe_grouped        rowwise quant of A [131072,7168] and of W [32][2048][7168] (per
+                     expert column), FP8 grouped GEMM over int32[33] offsets -> bf16
+  moe_block_mx       1x128 / 128x128 blockwise and MX quant, 16 experts, K 5120, N 8192,
+                     and the blockwise and MX grouped GEMMs
+Every launch is bracketed by HIP events on the stream it runs on. The JSON line
+reports the fused-quantization throughput (algorithmic bytes of all quantization
+calls / their summed event time, 3 B per element + 8 B per fp32 scale group or 1 B
+per E8M0 group) as `value`, the grouped-GEMM throughput (2*M*N*K / event time) of
+the moe_grouped GEMM as `gemm_value`, per-call figures under `rows`, the roofline of
+the dominant kernel and the oracle's CPU throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+EPS = 1e-12
+
+METRIC = "fused FP8 quant GB/s (% HBM peak); FP8 grouped-GEMM TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """A list of named calls; each call is timed with a pair of HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.calls = []  # (name, kind, work, fn); kind: quant (bytes) / gemm8 / gemm16 (flops) / latency
+
+    def add(self, name, kind, work, fn):
+        self.calls.append((name, kind, float(work), fn))
+
+    def run(self, stream, record=None):
+        torch = self.torch
+        for i, (name, kind, work, fn) in enumerate(self.calls):
+            if record is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                record[i].append((e0, e1))
+            else:
+                fn()
+
+
+def build_step(f, torch, dev, wls, dev_of):
+    """Allocates outputs and returns a Step whose calls cover every step of the path."""
+    st = Step(torch)
+    E4, E5 = f.E4M3_NATIVE, f.E5M2_NATIVE
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+
+    # ---- linear_tensorwise: the whole fp8_linear_fwd call (latency-bound) ----
+    w1 = wls["linear_tensorwise"]
+    x1, wt1 = dev_of(w1.tensors["x"]), dev_of(w1.tensors["w"])
+    M1, K1, N1 = x1.shape[0], x1.shape[1], wt1.shape[0]
+    ws1 = torch.empty(f.fp8_linear_ws_bytes(M1, N1, K1, f.RECIPE_TENSORWISE), **u8)
+    y1 = torch.empty((M1, N1), **f32)
+    st.add("linear_tensorwise.fwd", "latency", 2.0 * M1 * N1 * K1,
+           lambda: f.fp8_linear_fwd(x1, wt1, f.RECIPE_TENSORWISE, EPS, f.OUT_F32, y1, ws1))
+
+    # ---- linear_rowwise: forward and backward of the Llama3-8B MLP projection ----
+    w2 = wls["linear_rowwise"]
+    x2, wt2, g2 = dev_of(w2.tensors["x"]), dev_of(w2.tensors["w"]), dev_of(w2.tensors["gy"])
+    M, K = x2.shape
+    N = wt2.shape[0]
+    qx, sx, ix = torch.empty((M, K), **u8), torch.empty(M, **f32), torch.empty(M, **f32)
+    qw, sw, iw = torch.empty((N, K), **u8), torch.empty(N, **f32), torch.empty(N, **f32)
+    qg, sg, ig = torch.empty((M, N), **u8), torch.empty(M, **f32), torch.empty(M, **f32)
+    qwt, swc, iwc = torch.empty((K, N), **u8), torch.empty(K, **f32), torch.empty(K, **f32)
+    colws = torch.empty(max(f.fp8_quant_col_ws_bytes(1, N, K), 4), **u8)
+    y2 = torch.empty((M, N), **bf)
+    gx2 = torch.empty((M, K), **bf)
+    gw2 = torch.empty((N, K), **bf)
+    st.add("linear_rowwise.quant_row_x", "quant", 3 * M * K + 8 * M,
+           lambda: f.fp8_quant_row(x2, E4, EPS, qx, sx, ix))
+    st.add("linear_rowwise.quant_row_w", "quant", 3 * N * K + 8 * N,
+           lambda: f.fp8_quant_row(wt2, E4, EPS, qw, sw, iw))
+    st.add("linear_rowwise.gemm_fwd", "gemm8", 2.0 * M * N * K,
+           lambda: f.fp8_scaled_mm(qx, E4, qw, E4, f.SCALE_ROW, ix, iw, f.OUT_BF16, y2))
+    st.add("linear_rowwise.quant_row_gy_e5m2", "quant", 3 * M * N + 8 * M,
+           lambda: f.fp8_quant_row(g2, E5, EPS, qg, sg, ig))
+    st.add("linear_rowwise.quant_col_w", "quant", 3 * N * K + 8 * K,
+           lambda: f.fp8_quant_col(wt2, E4, EPS, qwt, swc, iwc, colws))
+    st.add("linear_rowwise.gemm_dgrad", "gemm8", 2.0 * M * N * K,
+           lambda: f.fp8_scaled_mm(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2, use_fast_accum=False))
+    st.add("linear_rowwise.wgrad_bf16", "gemm16", 2.0 * M * N * K,
+           lambda: f.fp8_wgrad_bf16(g2, x2, gw2))
+
+    # ---- expert_colwise ----
+    w3 = wls["expert_colwise"]
+    we3 = dev_of(w3.tensors["w"])
+    E3, R3, C3 = we3.shape
+    qt3 = torch.empty((E3, C3, R3), **u8)
+    s3, i3 = torch.empty((E3, C3), **f32), torch.empty((E3, C3), **f32)
+    st.add("expert_colwise.quant_col", "quant", 3 * E3 * R3 * C3 + 8 * E3 * C3,
+           lambda: f.fp8_quant_col(we3, E4, EPS, qt3, s3, i3, None))
+
+    # ---- moe_grouped ----
+    w4 = wls["moe_grouped"]
+    a4, we4 = dev_of(w4.tensors["a"]), dev_of(w4.tensors["w"])
+    off4 = torch.from_numpy(w4.meta["offsets"]).to(dev)
+    Mt, K4 = a4.shape
+    E4n, N4, _ = we4.shape
+    qa4, sa4, ia4 = torch.empty((Mt, K4), **u8), torch.empty(Mt, **f32), torch.empty(Mt, **f32)
+    qw4, sw4, iw4 = torch.empty((E4n, N4, K4), **u8), torch.empty((E4n, N4), **f32), torch.empty((E4n, N4), **f32)
+    out4 = torch.empty((Mt, N4), **bf)
+    st.add("moe_grouped.quant_row_a", "quant", 3 * Mt * K4 + 8 * Mt,
+           lambda: f.fp8_quant_row(a4, E4, EPS, qa4, sa4, ia4))
+    st.add("moe_grouped.quant_expert_cols_w", "quant", 3 * E4n * N4 * K4 + 8 * E4n * N4,
+           lambda: f.fp8_quant_row(we4, E4, EPS, qw4, sw4, iw4))
+    st.add("moe_grouped.grouped_gemm", "gemm8", 2.0 * Mt * N4 * K4,
+           lambda: f.fp8_grouped_mm(qa4, E4, qw4, E4, f.SCALE_ROW, ia4, iw4, off4, f.OUT_BF16, out4))
+
+    # ---- moe_block_mx ----
+    w5 = wls["moe_block_mx"]
+    a5, we5 = dev_of(w5.tensors["a"]), dev_of(w5.tensors["w"])
+    off5 = torch.from_numpy(w5.meta["offsets"]).to(dev)
+    M5, K5 = a5.shape
+    E5n, N5, _ = we5.shape
+    qa5, qw5 = torch.empty((M5, K5), **u8), torch.empty((E5n, N5, K5), **u8)
+    sa5, ia5 = torch.empty((M5, K5 // 128), **f32), torch.empty((M5, K5 // 128), **f32)
+    sw5, iw5 = torch.empty((E5n, N5 // 128, K5 // 128), **f32), torch.empty((E5n, N5 // 128, K5 // 128), **f32)
+    ea5, ew5 = torch.empty((M5, K5 // 32), **u8), torch.empty((E5n, N5, K5 // 32), **u8)
+    qa5m, qw5m = torch.empty((M5, K5), **u8), torch.empty((E5n, N5, K5), **u8)
+    out5 = torch.empty((M5, N5), **bf)
+    out5m = torch.empty((M5, N5), **bf)
+    st.add("moe_block_mx.quant_block_a_1x128", "quant", 3 * M5 * K5 + 8 * M5 * (K5 // 128),
+           lambda: f.fp8_quant_block(a5, 1, 128, E4, EPS, qa5, sa5, ia5))
+    st.add("moe_block_mx.quant_block_w_128x128", "quant", 3 * E5n * N5 * K5 + 8 * E5n * (N5 // 128) * (K5 // 128),
+           lambda: f.fp8_quant_block(we5, 128, 128, E4, EPS, qw5, sw5, iw5))
+    st.add("moe_block_mx.grouped_gemm_block", "gemm8", 2.0 * M5 * N5 * K5,
+           lambda: f.fp8_grouped_mm(qa5, E4, qw5, E4, f.SCALE_BLOCK128, ia5, iw5, off5, f.OUT_BF16, out5))
+    st.add("moe_block_mx.quant_mx_a", "quant", 3 * M5 * K5 + M5 * (K5 // 32),
+           lambda: f.fp8_quant_mx(a5, E4, f.MX_POW2_FLOOR, EPS, qa5m, ea5))
+    st.add("moe_block_mx.quant_mx_w", "quant", 3 * E5n * N5 * K5 + E5n * N5 * (K5 // 32),
+           lambda: f.fp8_quant_mx(we5, E4, f.MX_POW2_FLOOR, EPS, qw5m, ew5))
+    st.add("moe_block_mx.grouped_gemm_mx", "gemm8", 2.0 * M5 * N5 * K5,
+           lambda: f.fp8_grouped_mm(qa5m, E4, qw5m, E4, f.SCALE_MX32, ea5, ew5, off5, f.OUT_BF16, out5m))
+    return st
+
+
+def cpu_baseline(wls, budget_s=20.0):
+    """The oracle as it stands, on a bounded sample of the moe_grouped workload:
+    rowwise quantization of the activation rows, then fp64 grouped-GEMM outputs
+    for a sample of rows, until about budget_s seconds are spent."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.threads_used(0)
+    w = wls["moe_grouped"]
+    a, wt, off = w.tensors["a"], w.tensors["w"], w.meta["offsets"]
+    Mt, K = a.shape
+    E, N, _ = wt.shape
+    # quantization: whole row blocks of A until a quarter of the budget is used
+    rows_done, t_q = 0, 0.0
+    chunk = 8192
+    while t_q < budget_s * 0.25 and rows_done < Mt:
+        blk = np.ascontiguousarray(a[rows_done:rows_done + chunk])
+        t0 = time.perf_counter()
+        oracle.quant_row(blk, "e4m3fn", EPS, threads=threads)
+        t_q += time.perf_counter() - t0
+        rows_done += blk.shape[0]
+    q_bytes = rows_done * (3 * K + 8)
+    # GEMM: output rows of the grouped product (all N columns) on a row sample
+    qa, _, ia = oracle.quant_row(np.ascontiguousarray(a[:16384]), "e4m3fn", EPS, threads=threads)
+    qw, _, iw = oracle.quant_row(wt, "e4m3fn", EPS, threads=threads)
+    sub_off = np.minimum(off, 16384).astype(np.int32)
+    n_rows, t_g = 0, 0.0
+    rng = np.random.default_rng(0)
+    while t_g < budget_s * 0.75 and n_rows < 16384:
+        rows = rng.integers(0, 16384, 16)
+        rr = np.repeat(rows, N)
+        cc = np.tile(np.arange(N), rows.size)
+        t0 = time.perf_counter()
+        oracle.grouped_mm_sample(qa, "e4m3fn", qw, "e4m3fn", oracle.SCALE_ROW, ia, iw, sub_off, rr, cc)
+        t_g += time.perf_counter() - t0
+        n_rows += rows.size
+    flops = 2.0 * n_rows * N * K
+    return {
+        "value": round(q_bytes / t_q / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"moe_grouped: rowwise quantization of the first {rows_done} activation rows "
+                   f"({q_bytes / 1e9:.2f} GB algorithmic) in {t_q:.1f} s; fp64 grouped GEMM of "
+                   f"{n_rows} sampled output rows x {N} columns x K {K} in {t_g:.1f} s"),
+        "gemm_value": round(flops / t_g / 1e12, 6), "gemm_unit": "TFLOP/s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the path has no multi-GPU part).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_dynamic_scaling_amd as f
+    import synth
+
+    f.load()
+    synth.build(force=False)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    e4, e5 = f.fp8_probe(0)
+    t0 = time.perf_counter()
+    names = ["linear_tensorwise", "linear_rowwise", "expert_colwise", "moe_grouped", "moe_block_mx"]
+    if args.only:
+        names = [n for n in names if n in args.only.split(",")]
+    gens = {"linear_tensorwise": synth.linear_tensorwise, "linear_rowwise": synth.linear_rowwise,
+            "expert_colwise": synth.expert_colwise, "moe_grouped": synth.moe_grouped,
+            "moe_block_mx": synth.moe_block_mx}
+    wls = {n: gens[n]() for n in names}
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev_of(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # build the step (only the selected workloads)
+    full = {n: wls.get(n) for n in names}
+    st = build_step_subset(f, torch, dev, full, dev_of)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        st.run(stream)
+    torch.cuda.synchronize()
+    log("warmup done")
+    rec = [[] for _ in st.calls]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        st.run(stream, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    rows = {}
+    q_bytes = q_time = 0.0
+    dom = None
+    for i, (name, kind, work, _) in enumerate(st.calls):
+        ts = np.array([e0.elapsed_time(e1) for e0, e1 in rec[i]]) * 1e-3  # seconds
+        avg = float(ts.mean())
+        r = {"avg_us": round(avg * 1e6, 2), "median_us": round(float(np.median(ts)) * 1e6, 2)}
+        if kind == "quant":
+            r.update(gbs=round(work / avg / 1e9, 1), frac_hbm=round(work / avg / 1e9 / HBM_PEAK_GBS, 4),
+                     bytes=int(work))
+            q_bytes += work
+            q_time += avg
+        elif kind in ("gemm8", "gemm16"):
+            peak = FP8_PEAK_TFLOPS if kind == "gemm8" else BF16_PEAK_TFLOPS
+            r.update(tflops=round(work / avg / 1e12, 1), frac_mfma=round(work / avg / 1e12 / peak, 4),
+                     flops=work)
+        rows[name] = r
+        if kind != "latency" and (dom is None or avg > dom[2]):
+            dom = (name, kind, avg, work)
+
+    out = {"metric": METRIC}
+    out["value"] = round(q_bytes / q_time / 1e9, 1) if q_time > 0 else None
+    out["unit"] = "GB/s"
+    out["n_gpus"] = 1
+    out["steps"] = args.steps
+    out["warmup"] = args.warmup
+    out["ms_per_step"] = round(ms_per_step, 3)
+    out["higher_is_better"] = True
+    out["scaling"] = "weak"
+    out["vs_baseline"] = None
+    out["dtype"] = "fp8-e4m3/e5m2 (fp32 accumulate, bf16 in/out)"
+    out["data"] = "synthetic (seeded; shapes and distributions of the pages' workloads)"
+    out["config"] = {"workload": "+".join(names), "parallelism": "none (1 GPU)",
+                     "e4m3": {0: "e4m3fn", 1: "e4m3fnuz"}.get(e4, e4), "e5m2": {2: "e5m2", 3: "e5m2fnuz"}.get(e5, e5)}
+    out["frac_hbm"] = round(out["value"] / HBM_PEAK_GBS, 4) if out["value"] else None
+    g = rows.get("moe_grouped.grouped_gemm")
+    if g:
+        out["gemm_value"] = g["tflops"]
+        out["gemm_unit"] = "TFLOP/s"
+        out["gemm_frac_mfma"] = g["frac_mfma"]
+    if dom is not None:
+        name, kind, avg, work = dom
+        if kind == "quant":
+            out["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(work / avg / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(work / avg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+        else:
+            peak = FP8_PEAK_TFLOPS if kind == "gemm8" else BF16_PEAK_TFLOPS
+            out["roofline"] = {"kernel": name, "bound": "mfma", "achieved": round(work / avg / 1e12, 1),
+                               "peak": peak, "unit": "TFLOP/s", "frac": round(work / avg / 1e12 / peak, 4),
+                               "traffic": None}
+    out["rows"] = rows
+    if not args.no_cpu_baseline and "moe_grouped" in wls:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(wls, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def build_step_subset(f, torch, dev, wls, dev_of):
+    """build_step restricted to the workloads present in wls (for profiling runs):
+    absent workloads get tiny stand-ins whose calls are then dropped."""
+    import synth
+    full_names = ["linear_tensorwise", "linear_rowwise", "expert_colwise", "moe_grouped", "moe_block_mx"]
+    if set(wls) == set(full_names):
+        return build_step(f, torch, dev, wls, dev_of)
+    small = {
+        "linear_tensorwise": synth.linear_tensorwise,
+        "linear_rowwise": lambda: synth.linear_rowwise(M=64, K=64, N=64),
+        "expert_colwise": lambda: synth.expert_colwise(E=1, R=64, C=64),
+        "moe_grouped": lambda: synth.moe_grouped(tokens=64, topk=2, E=4, N=64, K=64, n_empty=0),
+        "moe_block_mx": lambda: synth.moe_block_mx(E=2, K=256, N=256, rows=64),
+    }
+    allw = {n: (wls[n] if n in wls else small[n]()) for n in full_names}
+    st = build_step(f, torch, dev, allw, dev_of)
+    st.calls = [c for c in st.calls if c[0].split(".")[0] in wls]
+    return st
+
+
+if __name__ == "__main__":
+    main()

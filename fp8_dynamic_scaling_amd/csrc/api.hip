@@ -1,0 +1,300 @@
+// api.hip -- the C ABI (include/fp8dyn.h): host-side validation, format
+// resolution through the per-device probe cache, and dispatch to the kernel
+// launchers. Nothing is launched when validation fails.
+#include <cmath>
+#include <mutex>
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8dyn.h"
+#include "internal.hpp"
+
+using namespace fp8dyn;
+
+namespace {
+
+std::atomic<int> g_last_error{0};
+
+struct ProbeCache {
+  std::mutex mu;
+  bool done[64] = {};
+  fp8_status status[64] = {};
+  fp8_format e4[64] = {};
+  fp8_format e5[64] = {};
+};
+ProbeCache& cache() {
+  static ProbeCache c;
+  return c;
+}
+
+fp8_status dev_err(hipError_t e) {
+  if (e == hipSuccess) return FP8_OK;
+  g_last_error.store((int)e);
+  return FP8_ERR_DEVICE;
+}
+
+fp8_status probe_device(int device, fp8_format* e4, fp8_format* e5) {
+  if (device < 0 || device >= 64) return FP8_ERR_INVALID_ARGUMENT;
+  ProbeCache& c = cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  if (!c.done[device]) {
+    int cur = 0;
+    hipError_t he = hipGetDevice(&cur);
+    if (he != hipSuccess) return dev_err(he);
+    if (cur != device && (he = hipSetDevice(device)) != hipSuccess) return dev_err(he);
+    fp8_status st = FP8_OK;
+    hipDeviceProp_t prop;
+    he = hipGetDeviceProperties(&prop, device);
+    if (he != hipSuccess) {
+      st = dev_err(he);
+    } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      st = FP8_ERR_UNSUPPORTED;
+    } else {
+      float r[6] = {0, 0, 0, 0, 0, 0};
+      he = run_probe(r);
+      if (he != hipSuccess) {
+        st = dev_err(he);
+      } else {
+        // convert side: code of 1.0; matrix-core side: 128 * value(code)^2
+        const bool cvt_e4_ocp = r[0] == 56.0f, cvt_e4_fnuz = r[0] == 64.0f;
+        const bool cvt_e5_ocp = r[1] == 60.0f, cvt_e5_fnuz = r[1] == 64.0f;
+        const bool mma_e4_ocp = r[4] == 128.0f, mma_e4_fnuz = r[4] == 32.0f;
+        const bool mma_e5_ocp = r[5] == 128.0f, mma_e5_fnuz = r[5] == 32.0f;
+        if (cvt_e4_ocp && mma_e4_ocp && cvt_e5_ocp && mma_e5_ocp) {
+          c.e4[device] = FP8_E4M3FN;
+          c.e5[device] = FP8_E5M2;
+        } else if (cvt_e4_fnuz && mma_e4_fnuz && cvt_e5_fnuz && mma_e5_fnuz) {
+          c.e4[device] = FP8_E4M3FNUZ;
+          c.e5[device] = FP8_E5M2FNUZ;
+        } else {
+          st = FP8_ERR_UNSUPPORTED;  // converts and matrix cores disagree
+        }
+      }
+    }
+    if (cur != device) (void)hipSetDevice(cur);
+    c.status[device] = st;
+    c.done[device] = true;
+  }
+  if (c.status[device] != FP8_OK) return c.status[device];
+  if (e4) *e4 = c.e4[device];
+  if (e5) *e5 = c.e5[device];
+  return FP8_OK;
+}
+
+// Resolves a requested format for the current device. Only the device's
+// native variants are produced/consumed by the kernels.
+fp8_status resolve(fp8_format f, bool* is_e5, double* fmax) {
+  if ((int)f < 0 || (int)f > 5) return FP8_ERR_INVALID_ARGUMENT;
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return dev_err(he);
+  fp8_format e4, e5;
+  fp8_status st = probe_device(dev, &e4, &e5);
+  if (st != FP8_OK) return st;
+  if (f == FP8_E4M3_NATIVE) f = e4;
+  if (f == FP8_E5M2_NATIVE) f = e5;
+  if (f == e4) {
+    *is_e5 = false;
+  } else if (f == e5) {
+    *is_e5 = true;
+  } else {
+    return FP8_ERR_UNSUPPORTED;
+  }
+  *fmax = f == FP8_E4M3FN ? 448.0 : (f == FP8_E4M3FNUZ ? 240.0 : 57344.0);
+  return FP8_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool bad_eps(double eps) { return !(std::isfinite(eps) && eps > 0.0); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status s) {
+  switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FP8_ERR_ALIGNMENT: return "alignment or divisibility rule broken";
+    case FP8_ERR_UNSUPPORTED: return "unsupported format, device or shape";
+    case FP8_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8_ERR_DEVICE: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int fp8_last_device_error(void) { return g_last_error.load(); }
+
+double fp8_format_max(fp8_format f) {
+  switch (f) {
+    case FP8_E4M3FN: return 448.0;
+    case FP8_E4M3FNUZ: return 240.0;
+    case FP8_E5M2:
+    case FP8_E5M2FNUZ: return 57344.0;
+    default: {
+      bool e5;
+      double fm;
+      return resolve(f, &e5, &fm) == FP8_OK ? fm : 0.0;
+    }
+  }
+}
+
+fp8_status fp8_probe(int device, fp8_format* e4m3_native, fp8_format* e5m2_native) {
+  return probe_device(device, e4m3_native, e5m2_native);
+}
+
+size_t fp8_quant_tensor_ws_bytes(void) { return 256; }
+
+size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 0 || rows < 0 || cols < 0) return 0;
+  return quant_col_ws_bytes(batch, rows, cols);
+}
+
+static fp8_status check_quant_common(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, double eps,
+                                     const uint8_t* q, const void* scale) {
+  if (batch < 0 || rows < 0 || cols < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (bad_eps(eps)) return FP8_ERR_INVALID_ARGUMENT;
+  if (batch * rows * cols == 0) return FP8_OK;
+  if (!x || !q || !scale) return FP8_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return FP8_ERR_ALIGNMENT;
+  return FP8_OK;
+}
+
+fp8_status fp8_quant_tensor(const uint16_t* x, int64_t n, fp8_format fmt, double eps, uint8_t* q, float* scale,
+                            float* inv_scale, void* ws, size_t ws_bytes, void* stream) {
+  fp8_status st = check_quant_common(x, 1, 1, n, eps, q, scale);
+  if (st != FP8_OK) return st;
+  if (n == 0) return FP8_OK;
+  if (!ws || ws_bytes < fp8_quant_tensor_ws_bytes()) return FP8_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, 1, 1, n, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_tensor(a, ws));
+}
+
+fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
+                         uint8_t* q, float* scale, float* inv_scale, void* stream) {
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
+  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_row(a));
+}
+
+fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
+                         uint8_t* qT, float* scale, float* inv_scale, void* ws, size_t ws_bytes, void* stream) {
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, qT, scale);
+  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  const size_t need = quant_col_ws_bytes(batch, rows, cols);
+  const bool vec_path = cols % 8 == 0 && rows % 16 == 0;
+  if (need > 0 && vec_path) {
+    if (!ws || ws_bytes < need) return FP8_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return FP8_ERR_ALIGNMENT;
+  }
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, qT, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_col(a, ws));
+}
+
+fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
+                           int block_cols, fp8_format fmt, double eps, uint8_t* q, float* scale, float* inv_scale,
+                           void* stream) {
+  if (!((block_rows == 1 || block_rows == 128) && block_cols == 128)) return FP8_ERR_INVALID_ARGUMENT;
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
+  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_block(a, block_rows, block_cols));
+}
+
+fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                        fp8_mx_mode mode, double eps, uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (mode != FP8_MX_POW2_FLOOR && mode != FP8_MX_OCP) return FP8_ERR_INVALID_ARGUMENT;
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, e8m0);
+  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  if (cols % 32 != 0) return FP8_ERR_ALIGNMENT;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, nullptr, nullptr, (hipStream_t)stream};
+  return dev_err(launch_quant_mx(a, e8m0, (int)mode));
+}
+
+static fp8_status check_gemm(const void* a, const void* b, const void* sa, const void* sb, int64_t M, int64_t N,
+                             int64_t K, fp8_scaling scaling, fp8_out out_type, const void* out) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if ((int)scaling < 0 || (int)scaling > 3) return FP8_ERR_INVALID_ARGUMENT;
+  if (out_type != FP8_OUT_BF16 && out_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!out) return FP8_ERR_INVALID_ARGUMENT;
+  if (K > 0 && (!a || !b || !sa || !sb)) return FP8_ERR_INVALID_ARGUMENT;
+  if (K % 16 != 0) return FP8_ERR_ALIGNMENT;
+  if (scaling == FP8_SCALE_BLOCK128 && (K % 128 != 0 || N % 128 != 0)) return FP8_ERR_ALIGNMENT;
+  if (scaling == FP8_SCALE_MX32 && K % 32 != 0) return FP8_ERR_ALIGNMENT;
+  if ((a && !aligned(a, 16)) || (b && !aligned(b, 16)) || !aligned(out, 4)) return FP8_ERR_ALIGNMENT;
+  if (scaling != FP8_SCALE_MX32 && ((sa && !aligned(sa, 4)) || (sb && !aligned(sb, 4)))) return FP8_ERR_ALIGNMENT;
+  return FP8_OK;
+}
+
+fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb, fp8_scaling scaling,
+                         const float* a_inv, const float* b_inv, int64_t M, int64_t N, int64_t K, fp8_out out_type,
+                         void* out, int use_fast_accum, void* stream) {
+  (void)use_fast_accum;  // matrix cores accumulate in fp32 either way
+  if (scaling != FP8_SCALE_TENSOR && scaling != FP8_SCALE_ROW) return FP8_ERR_UNSUPPORTED;
+  fp8_status st = check_gemm(a, b, a_inv, b_inv, M, N, K, scaling, out_type, out);
+  if (st != FP8_OK || M == 0 || N == 0) return st;
+  bool ea, eb;
+  double fm;
+  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
+  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+             (hipStream_t)stream};
+  return dev_err(launch_gemm_fp8(g));
+}
+
+fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb, fp8_scaling scaling,
+                          const void* a_scale, const void* b_scale, const int32_t* offsets, int32_t E, int64_t Mtot,
+                          int64_t N, int64_t K, fp8_out out_type, void* out, void* stream) {
+  if (scaling == FP8_SCALE_TENSOR) return FP8_ERR_UNSUPPORTED;
+  if (E < 1 || E > 1024) return FP8_ERR_INVALID_ARGUMENT;
+  fp8_status st = check_gemm(a, b, a_scale, b_scale, Mtot, N, K, scaling, out_type, out);
+  if (st != FP8_OK || Mtot == 0 || N == 0) return st;
+  if (!offsets) return FP8_ERR_INVALID_ARGUMENT;
+  if (!aligned(offsets, 4)) return FP8_ERR_ALIGNMENT;
+  bool ea, eb;
+  double fm;
+  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
+  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+             (hipStream_t)stream};
+  return dev_err(launch_gemm_fp8(g));
+}
+
+fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N, int64_t K, uint16_t* gw,
+                          void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (N == 0 || K == 0) return FP8_OK;
+  if (!gw || (M > 0 && (!gy || !x))) return FP8_ERR_INVALID_ARGUMENT;
+  if (N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
+  if ((gy && !aligned(gy, 16)) || (x && !aligned(x, 16)) || !aligned(gw, 4)) return FP8_ERR_ALIGNMENT;
+  WgradArgs w{gy, x, M, N, K, gw, (hipStream_t)stream};
+  return dev_err(launch_wgrad_bf16(w));
+}
+
+fp8_status fp8_validate_offsets(const int32_t* host_offsets, int32_t E, int64_t Mtot) {
+  if (!host_offsets || E < 1 || Mtot < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (host_offsets[0] != 0 || host_offsets[E] != Mtot) return FP8_ERR_INVALID_ARGUMENT;
+  for (int32_t e = 0; e < E; ++e)
+    if (host_offsets[e + 1] < host_offsets[e]) return FP8_ERR_INVALID_ARGUMENT;
+  return FP8_OK;
+}
+
+}  // extern "C"

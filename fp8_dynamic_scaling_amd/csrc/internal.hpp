@@ -1,0 +1,66 @@
+// internal.hpp -- launcher interfaces between the C-ABI layer (api.hip) and
+// the kernels. Host-side only declarations; no validation happens below this
+// line, so every launcher assumes arguments the API has already checked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace fp8dyn {
+
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t batch, rows, cols;
+  bool e5;      // e5m2 (else e4m3)
+  double fmax;  // largest finite value of the output format
+  double eps;
+  uint8_t* q;
+  float* scale;
+  float* inv;
+  hipStream_t stream;
+};
+
+hipError_t launch_quant_row(const QuantArgs& a);
+hipError_t launch_quant_col(const QuantArgs& a, void* ws);
+size_t quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
+hipError_t launch_quant_tensor(const QuantArgs& a, void* ws);  // ws >= 256 bytes
+// tensorwise scale, transposed output qT[b][c][r]; needs cols % 8 == 0, rows % 16 == 0
+hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws);
+hipError_t launch_quant_block(const QuantArgs& a, int block_rows, int block_cols);
+hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode);
+
+// Probe kernels: results[0..3] = fp8 codes of 1.0 (e4m3, e5m2) and of the
+// formats' maxima; results[4..5] = matrix-core dot products of 128 copies of
+// the codes 0x38 (e4m3) and 0x3C (e5m2) with themselves.
+hipError_t run_probe(float* host_results);
+
+// GEMMs ------------------------------------------------------------------------
+enum ScaleKind : int { kScaleTensor = 0, kScaleRow = 1, kScaleBlock = 2, kScaleMX = 3 };
+
+struct GemmArgs {
+  const uint8_t* a;   // [Mtot][K]
+  const uint8_t* b;   // [E][N][K]
+  const void* sa;     // per ScaleKind
+  const void* sb;
+  const int32_t* offsets;  // device [E+1], or nullptr for a dense problem (E == 1)
+  int32_t E;
+  int64_t M, N, K;    // M = Mtot
+  bool a_e5, b_e5;
+  int scale_kind;
+  bool out_f32;
+  void* out;          // [M][N]
+  hipStream_t stream;
+};
+hipError_t launch_gemm_fp8(const GemmArgs& g);
+
+struct WgradArgs {
+  const uint16_t* gy;  // [M][N]
+  const uint16_t* x;   // [M][K]
+  int64_t M, N, K;
+  uint16_t* gw;        // [N][K]
+  hipStream_t stream;
+};
+hipError_t launch_wgrad_bf16(const WgradArgs& w);
+
+}  // namespace fp8dyn

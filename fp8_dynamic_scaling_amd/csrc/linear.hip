@@ -1,0 +1,169 @@
+// linear.hip -- one Linear layer, forward and backward, as stream-ordered
+// launches of the quantization kernels and GEMMs ("FP8 Training:
+// Quantization, Autograd, Torchao", section 6: three GEMMs per layer;
+// "FP8 training on AMD GPUs with TorchTitan and TorchAO", Figure 1 caption:
+// the rowwise recipe keeps the weight-gradient GEMM in BF16).
+//
+//   forward   y  = (qx * inv_x) (qw * inv_w)^T    qx, qw: e4m3
+//   backward  gx = (qg * inv_g) (qwT * inv_wc)^T  qg: e5m2 of gy, qwT: e4m3 of w
+//                                                 quantized per column of w and
+//                                                 written transposed [K][N]
+//             gw = gy^T x                         bf16 matrix cores
+// Every FP8 operand is produced directly in the layout its GEMM reads: no
+// transposed copies ("FP8 training on AMD GPUs with TorchTitan and TorchAO",
+// Level 1).
+#include "../../include/fp8dyn.h"
+#include "internal.hpp"
+
+using namespace fp8dyn;
+
+namespace {
+
+struct Bump {
+  uint8_t* base;
+  size_t off = 0;
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  }
+};
+
+struct FwdLayout {
+  void *qx, *qw, *sx, *ix, *sw, *iw, *wsx, *wsw;
+};
+FwdLayout fwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r, size_t* total) {
+  Bump b{ws};
+  FwdLayout L;
+  const bool tw = r == FP8_RECIPE_TENSORWISE;
+  L.qx = b.take((size_t)(M * K));
+  L.qw = b.take((size_t)(N * K));
+  L.sx = b.take(4 * (tw ? 1 : (size_t)M));
+  L.ix = b.take(4 * (tw ? 1 : (size_t)M));
+  L.sw = b.take(4 * (tw ? 1 : (size_t)N));
+  L.iw = b.take(4 * (tw ? 1 : (size_t)N));
+  L.wsx = b.take(256);
+  L.wsw = b.take(256);
+  *total = b.off;
+  return L;
+}
+
+struct BwdLayout {
+  void *qg, *sg, *ig, *qwt, *swc, *iwc, *wsg, *wscol;
+};
+BwdLayout bwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r, size_t* total) {
+  Bump b{ws};
+  BwdLayout L;
+  const bool tw = r == FP8_RECIPE_TENSORWISE;
+  L.qg = b.take((size_t)(M * N));
+  L.sg = b.take(4 * (tw ? 1 : (size_t)M));
+  L.ig = b.take(4 * (tw ? 1 : (size_t)M));
+  L.qwt = b.take((size_t)(K * N));
+  L.swc = b.take(4 * (tw ? 1 : (size_t)K));
+  L.iwc = b.take(4 * (tw ? 1 : (size_t)K));
+  L.wsg = b.take(256);
+  size_t colws = tw ? 256 : quant_col_ws_bytes(1, N, K);
+  L.wscol = b.take(colws > 0 ? colws : 256);
+  *total = b.off;
+  return L;
+}
+
+fp8_status as_status(hipError_t e) {
+  if (e == hipSuccess) return FP8_OK;
+  return FP8_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8_linear_ws_bytes(int64_t M, int64_t N, int64_t K, fp8_recipe recipe) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  size_t f = 0, b = 0;
+  fwd_layout(nullptr, M, N, K, recipe, &f);
+  bwd_layout(nullptr, M, N, K, recipe, &b);
+  return f > b ? f : b;
+}
+
+fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, fp8_recipe recipe,
+                          double eps, fp8_out out_type, void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (recipe != FP8_RECIPE_TENSORWISE && recipe != FP8_RECIPE_ROWWISE_BF16_WGRAD) return FP8_ERR_INVALID_ARGUMENT;
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!y || (K > 0 && (!x || !w))) return FP8_ERR_INVALID_ARGUMENT;
+  if (K % 16 != 0) return FP8_ERR_ALIGNMENT;
+  size_t need = 0;
+  fwd_layout(nullptr, M, N, K, recipe, &need);
+  if (!ws || ws_bytes < need) return FP8_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
+  FwdLayout L = fwd_layout((uint8_t*)ws, M, N, K, recipe, &need);
+  const bool tw = recipe == FP8_RECIPE_TENSORWISE;
+  fp8_status st;
+  if (tw) {
+    if ((st = fp8_quant_tensor(x, M * K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, L.wsx, 256,
+                               stream)) != FP8_OK)
+      return st;
+    if ((st = fp8_quant_tensor(w, N * K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw, L.wsw, 256,
+                               stream)) != FP8_OK)
+      return st;
+  } else {
+    if ((st = fp8_quant_row(x, 1, M, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, stream)) !=
+        FP8_OK)
+      return st;
+    if ((st = fp8_quant_row(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw, stream)) !=
+        FP8_OK)
+      return st;
+  }
+  return fp8_scaled_mm((const uint8_t*)L.qx, FP8_E4M3_NATIVE, (const uint8_t*)L.qw, FP8_E4M3_NATIVE,
+                       tw ? FP8_SCALE_TENSOR : FP8_SCALE_ROW, (const float*)L.ix, (const float*)L.iw, M, N, K, out_type,
+                       y, 1, stream);
+}
+
+fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                          fp8_recipe recipe, double eps, uint16_t* gx, uint16_t* gw, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (recipe != FP8_RECIPE_TENSORWISE && recipe != FP8_RECIPE_ROWWISE_BF16_WGRAD) return FP8_ERR_INVALID_ARGUMENT;
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0 || K == 0) return FP8_OK;
+  if (!gy || !x || !w || !gx || !gw) return FP8_ERR_INVALID_ARGUMENT;
+  if (N % 16 != 0 || K % 16 != 0) return FP8_ERR_ALIGNMENT;
+  size_t need = 0;
+  bwd_layout(nullptr, M, N, K, recipe, &need);
+  if (!ws || ws_bytes < need) return FP8_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
+  BwdLayout L = bwd_layout((uint8_t*)ws, M, N, K, recipe, &need);
+  const bool tw = recipe == FP8_RECIPE_TENSORWISE;
+  fp8_status st;
+  if (tw) {
+    if ((st = fp8_quant_tensor(gy, M * N, FP8_E5M2_NATIVE, eps, (uint8_t*)L.qg, (float*)L.sg, (float*)L.ig, L.wsg, 256,
+                               stream)) != FP8_OK)
+      return st;
+    // one scale for w, written transposed [K][N]
+    bool e5 = false;
+    fp8_format e4f, e5f;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8_ERR_DEVICE;
+    if ((st = fp8_probe(dev, &e4f, &e5f)) != FP8_OK) return st;
+    QuantArgs a{w, 1, N, K, e5, fp8_format_max(e4f), eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc,
+                (hipStream_t)stream};
+    if ((st = as_status(launch_quant_tensor_transposed(a, L.wscol))) != FP8_OK) return st;
+  } else {
+    if ((st = fp8_quant_row(gy, 1, M, N, FP8_E5M2_NATIVE, eps, (uint8_t*)L.qg, (float*)L.sg, (float*)L.ig, stream)) !=
+        FP8_OK)
+      return st;
+    if ((st = fp8_quant_col(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc, L.wscol,
+                            quant_col_ws_bytes(1, N, K) > 0 ? quant_col_ws_bytes(1, N, K) : 256, stream)) != FP8_OK)
+      return st;
+  }
+  // grad-input: [M][N] x ([K][N])^T -> [M][K]
+  if ((st = fp8_scaled_mm((const uint8_t*)L.qg, FP8_E5M2_NATIVE, (const uint8_t*)L.qwt, FP8_E4M3_NATIVE,
+                          tw ? FP8_SCALE_TENSOR : FP8_SCALE_ROW, (const float*)L.ig, (const float*)L.iwc, M, K, N,
+                          FP8_OUT_BF16, gx, 0, stream)) != FP8_OK)
+    return st;
+  // grad-weight in BF16: [N][K] = gy^T x
+  return fp8_wgrad_bf16(gy, x, M, N, K, gw, stream);
+}
+
+}  // extern "C"

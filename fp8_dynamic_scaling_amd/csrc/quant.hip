@@ -1,0 +1,575 @@
+// quant.hip -- fused dynamic FP8 quantization kernels for gfx950.
+//
+// Each kernel does the whole chain of "FP8 training on AMD GPUs with
+// TorchTitan and TorchAO", section "Triton Kernel Optimization" (absmax per
+// group, derive and apply the scale, clamp and cast) in one pass over HBM,
+// with the group's data held in registers between the reduction and the
+// cast, so nothing intermediate is written (Level 1 of that page). The math is
+// that of "FP8 Training: Quantization, Autograd, Torchao", section 2.
+//
+// Memory design for MI355X: 16-byte loads per lane, 8-byte (or 16-byte)
+// stores, amax reduced with wavefront shuffles and a few words of LDS,
+// fp64 scale derived redundantly per lane (cheaper than a broadcast), and
+// the hardware packed converts (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace fp8dyn {
+
+// ---------------------------------------------------------------------------
+// Row groups. One workgroup of 256 threads per row; the row (up to
+// 2048 * J elements) stays in registers between amax and cast.
+template <int J, bool E5>
+__global__ __launch_bounds__(256) void k_quant_row(const uint16_t* __restrict__ x, int64_t cols,
+                                                   uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                   float* __restrict__ inv, double fmax, double eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * cols;
+  uint8_t* qr = q + row * cols;
+  const int tid = threadIdx.x;
+  uint4 v[J];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(tid + 256 * j) * 8;
+    if (c < cols) {
+      v[j] = ld_nt16(xr + c);
+      m = amax8(v[j], m);
+    }
+  }
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (tid == 0) {
+    scale[row] = s;
+    if (inv) inv[row] = iv;
+  }
+  const float fm = (float)fmax;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(tid + 256 * j) * 8;
+    if (c < cols) {
+      uint2 r = quant8<E5>(v[j], s, fm);
+      st_nt8(qr + c, r);
+    }
+  }
+}
+
+// Any row length / alignment: two passes over the row (the second hits cache).
+template <bool E5>
+__global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __restrict__ x, int64_t cols,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                           float* __restrict__ inv, double fmax, double eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * cols;
+  float m = 0.0f;
+  for (int64_t c = threadIdx.x; c < cols; c += 256)
+    m = fmaxf(m, fabsf(__uint_as_float((uint32_t)xr[c] << 16)));
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (threadIdx.x == 0) {
+    scale[row] = s;
+    if (inv) inv[row] = iv;
+  }
+  const float fm = (float)fmax;
+  for (int64_t c = threadIdx.x; c < cols; c += 256)
+    q[row * cols + c] = cvt1<E5>(clampf(__uint_as_float((uint32_t)xr[c] << 16) * s, fm));
+}
+
+// ---------------------------------------------------------------------------
+// Column groups with transposed output qT[b][c][r]. A workgroup owns a strip
+// of 64 columns and up to 2048 rows (128 row-groups x 16 rows). Lane layout:
+// l8 = tid % 8 picks 8 adjacent columns (one 16-byte load per row), rg =
+// tid / 8 picks 16 consecutive rows. After the column amax, each thread packs
+// its 16 rows of one column into 16 bytes directly with the packed converts
+// (the pair of fp32 inputs of each convert is chosen to be two consecutive
+// rows of the same column), so the transposed tile is formed in registers and
+// each store instruction writes 8 columns x 128 contiguous bytes: the
+// coalesced transposed store of "FP8 training on AMD GPUs with TorchTitan and
+// TorchAO", Level 2, without the LDS round trip.
+//
+// MODE 0: single pass, the workgroup covers all rows and reduces the amax.
+// MODE 1: cast pass of the split form, column amax read from colmax[].
+// MODE 2: amax pass of the split form: relaxed atomic max into colmax[]
+//         ("FP8 training on AMD GPUs with TorchTitan and TorchAO", Level 3).
+constexpr int kColRPT = 16;    // rows per thread
+constexpr int kColRows = 2048; // rows per workgroup (1024 threads)
+
+template <bool E5, int MODE>
+__global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                    int64_t strips, int64_t rchunks,
+                                                    uint8_t* __restrict__ qT, float* __restrict__ scale,
+                                                    float* __restrict__ inv, uint32_t* __restrict__ colmax,
+                                                    int64_t cm_stride, double fmax, double eps) {
+  __shared__ float red[16][64];
+  __shared__ float s_scale[64];
+  const int tid = threadIdx.x;
+  const int nwaves = blockDim.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l8 = tid & 7, rg = tid >> 3;
+  int64_t blk = blockIdx.x;
+  const int64_t rc = blk % rchunks;
+  blk /= rchunks;
+  const int64_t strip = blk % strips;
+  const int64_t b = blk / strips;
+  const int64_t c0 = strip * 64 + l8 * 8;
+  const bool cok = c0 < C;
+  const int64_t r0 = rc * kColRows + (int64_t)rg * kColRPT;
+  const uint16_t* xb = x + b * R * C;
+
+  uint4 v[kColRPT];
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kColRPT; ++j) {
+    const int64_t r = r0 + j;
+    if (cok && r < R) {
+      v[j] = ld_nt16(xb + r * C + c0);
+    } else {
+      v[j] = make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (MODE != 1) {
+      m[0] = fmaxf(m[0], fabsf(bf16_lo(v[j].x)));
+      m[1] = fmaxf(m[1], fabsf(bf16_hi(v[j].x)));
+      m[2] = fmaxf(m[2], fabsf(bf16_lo(v[j].y)));
+      m[3] = fmaxf(m[3], fabsf(bf16_hi(v[j].y)));
+      m[4] = fmaxf(m[4], fabsf(bf16_lo(v[j].z)));
+      m[5] = fmaxf(m[5], fabsf(bf16_hi(v[j].z)));
+      m[6] = fmaxf(m[6], fabsf(bf16_lo(v[j].w)));
+      m[7] = fmaxf(m[7], fabsf(bf16_hi(v[j].w)));
+    }
+  }
+
+  if constexpr (MODE != 1) {
+    // reduce over the 8 row-groups of the wave (lanes with equal l8)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m[i] = fmaxf(m[i], __shfl_xor(m[i], 8, 64));
+      m[i] = fmaxf(m[i], __shfl_xor(m[i], 16, 64));
+      m[i] = fmaxf(m[i], __shfl_xor(m[i], 32, 64));
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float cm = red[0][tid];
+      for (int w = 1; w < nwaves; ++w) cm = fmaxf(cm, red[w][tid]);
+      const int64_t c = strip * 64 + tid;
+      if constexpr (MODE == 2) {
+        if (c < C) atomic_max_relaxed(colmax + b * C + c, cm);
+      } else {
+        float s, iv;
+        scale_from_amax(cm, fmax, eps, s, iv);
+        s_scale[tid] = s;
+        if (c < C) {
+          scale[b * C + c] = s;
+          if (inv) inv[b * C + c] = iv;
+        }
+      }
+    }
+    if constexpr (MODE == 2) return;
+  } else {
+    if (tid < 64) {
+      // cm_stride 1: one amax per column; 0: one amax for the whole tensor
+      const int64_t c = strip * 64 + tid;
+      const int64_t si = (b * C + c) * cm_stride;
+      const float cm = c < C ? __uint_as_float(colmax[si]) : 0.0f;
+      float s, iv;
+      scale_from_amax(cm, fmax, eps, s, iv);
+      s_scale[tid] = s;
+      if (rc == 0 && c < C && (cm_stride != 0 || (b == 0 && c == 0))) {
+        scale[si] = s;
+        if (inv) inv[si] = iv;
+      }
+    }
+  }
+  __syncthreads();
+  if (!cok || r0 >= R) return;
+
+  const float fm = (float)fmax;
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc[i] = s_scale[l8 * 8 + i];
+  uint8_t* qb = qT + (b * C + c0) * R + r0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // column i of this thread: rows r0 .. r0+15 -> 16 bytes
+    float f[kColRPT];
+#pragma unroll
+    for (int j = 0; j < kColRPT; ++j) {
+      const uint32_t w = (i < 2) ? v[j].x : (i < 4) ? v[j].y : (i < 6) ? v[j].z : v[j].w;
+      f[j] = clampf(((i & 1) ? bf16_hi(w) : bf16_lo(w)) * sc[i], fm);
+    }
+    uint4 o;
+    o.x = cvt4<E5>(f[0], f[1], f[2], f[3]);
+    o.y = cvt4<E5>(f[4], f[5], f[6], f[7]);
+    o.z = cvt4<E5>(f[8], f[9], f[10], f[11]);
+    o.w = cvt4<E5>(f[12], f[13], f[14], f[15]);
+    st_nt16(qb + (int64_t)i * R, o);
+  }
+}
+
+// Any shape: one workgroup per column, two passes (correct, slow).
+template <bool E5>
+__global__ __launch_bounds__(256) void k_quant_col_generic(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                           uint8_t* __restrict__ qT, float* __restrict__ scale,
+                                                           float* __restrict__ inv, double fmax, double eps) {
+  __shared__ float red[4];
+  const int64_t bc = blockIdx.x;
+  const int64_t b = bc / C, c = bc % C;
+  const uint16_t* xb = x + b * R * C + c;
+  float m = 0.0f;
+  for (int64_t r = threadIdx.x; r < R; r += 256) m = fmaxf(m, fabsf(__uint_as_float((uint32_t)xb[r * C] << 16)));
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (threadIdx.x == 0) {
+    scale[bc] = s;
+    if (inv) inv[bc] = iv;
+  }
+  const float fm = (float)fmax;
+  for (int64_t r = threadIdx.x; r < R; r += 256)
+    qT[bc * R + r] = cvt1<E5>(clampf(__uint_as_float((uint32_t)xb[r * C] << 16) * s, fm));
+}
+
+// ---------------------------------------------------------------------------
+// Tensorwise: clear, amax with relaxed atomics, cast. The kernel boundary
+// between the amax and the cast launches is the one ordering point.
+__global__ void k_clear_words(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_amax_tensor(const uint16_t* __restrict__ x, int64_t n,
+                                                     uint32_t* __restrict__ amax_word) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  const int64_t nvec = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+    const uint4 v = ld_nt16(x + 8 * i);
+    m = amax8(v, m);
+  }
+  // tail (n % 8 elements)
+  if (blockIdx.x == 0)
+    for (int64_t i = nvec * 8 + threadIdx.x; i < n; i += 256)
+      m = fmaxf(m, fabsf(__uint_as_float((uint32_t)x[i] << 16)));
+  m = block_max<256>(m, red);
+  if (threadIdx.x == 0) atomic_max_relaxed(amax_word, m);
+}
+
+template <bool E5>
+__global__ __launch_bounds__(256) void k_cast_tensor(const uint16_t* __restrict__ x, int64_t n,
+                                                     const uint32_t* __restrict__ amax_word,
+                                                     uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                     float* __restrict__ inv, double fmax, double eps) {
+  const float amax = __uint_as_float(*amax_word);
+  float s, iv;
+  scale_from_amax(amax, fmax, eps, s, iv);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scale[0] = s;
+    if (inv) inv[0] = iv;
+  }
+  const float fm = (float)fmax;
+  const int64_t nvec = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+    const uint4 v = ld_nt16(x + 8 * i);
+    st_nt8(q + 8 * i, quant8<E5>(v, s, fm));
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = nvec * 8 + threadIdx.x; i < n; i += 256)
+      q[i] = cvt1<E5>(clampf(__uint_as_float((uint32_t)x[i] << 16) * s, fm));
+}
+
+// ---------------------------------------------------------------------------
+// 1 x G groups along the row, G in {128, 32}: G/8 lanes per group, one
+// 16-byte chunk each. MX=true: power-of-two scale, E8M0 byte per group.
+template <bool E5, int G, bool MX>
+__global__ __launch_bounds__(256) void k_quant_group1d(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                       float* __restrict__ inv, uint8_t* __restrict__ e8m0,
+                                                       double fmax, double eps, int mx_mode) {
+  constexpr int LPG = G / 8;  // lanes per group
+  constexpr int GPB = 256 / LPG;  // groups per workgroup per iteration
+  const int64_t ngc = (cols + G - 1) / G;
+  const int64_t ngroups = rows * ngc;
+  const int sub = threadIdx.x % LPG;
+  const float fm = (float)fmax;
+  for (int64_t g = (int64_t)blockIdx.x * GPB + threadIdx.x / LPG; g < ngroups; g += (int64_t)gridDim.x * GPB) {
+    const int64_t r = g / ngc, gc = g % ngc;
+    const int64_t c = gc * G + sub * 8;
+    const bool ok = c < cols;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = ld_nt16(x + r * cols + c);
+    float m = amax8(v, 0.0f);
+#pragma unroll
+    for (int o = 1; o < LPG; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float s, iv;
+    if constexpr (MX) {
+      const int k = mx_exponent(m, fmax, eps, mx_mode);
+      s = exp2i(k);
+      if (sub == 0) e8m0[g] = (uint8_t)(127 - k);
+    } else {
+      scale_from_amax(m, fmax, eps, s, iv);
+      if (sub == 0) {
+        scale[g] = s;
+        if (inv) inv[g] = iv;
+      }
+    }
+    if (ok) st_nt8(q + r * cols + c, quant8<E5>(v, s, fm));
+  }
+}
+
+// 128 x 128 blocks: one workgroup of 256 threads per block; thread t owns
+// column chunk t % 16 of rows t / 16 + 16 j.
+template <bool E5>
+__global__ __launch_bounds__(256) void k_quant_block128(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                        int64_t nbr, int64_t nbc, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale, float* __restrict__ inv,
+                                                        double fmax, double eps) {
+  __shared__ float red[4];
+  int64_t blk = blockIdx.x;
+  const int64_t cb = blk % nbc;
+  blk /= nbc;
+  const int64_t rb = blk % nbr;
+  const int64_t b = blk / nbr;
+  const int cc = threadIdx.x & 15, ro = threadIdx.x >> 4;
+  const int64_t c = cb * 128 + cc * 8;
+  const bool cok = c < C;
+  const uint16_t* xb = x + b * R * C;
+  uint4 v[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = rb * 128 + ro + 16 * j;
+    if (cok && r < R) {
+      v[j] = ld_nt16(xb + r * C + c);
+      m = amax8(v[j], m);
+    }
+  }
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (threadIdx.x == 0) {
+    scale[blockIdx.x] = s;
+    if (inv) inv[blockIdx.x] = iv;
+  }
+  const float fm = (float)fmax;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = rb * 128 + ro + 16 * j;
+    if (cok && r < R)
+      st_nt8(q + b * R * C + r * C + c, quant8<E5>(v[j], s, fm));
+  }
+}
+
+// Generic block / MX (any alignment): one workgroup per group, two passes.
+template <bool E5, bool MX>
+__global__ __launch_bounds__(256) void k_quant_block_generic(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                             int64_t br, int64_t bc, int64_t nbr, int64_t nbc,
+                                                             uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                             float* __restrict__ inv, uint8_t* __restrict__ e8m0,
+                                                             double fmax, double eps, int mx_mode) {
+  __shared__ float red[4];
+  int64_t blk = blockIdx.x;
+  const int64_t cbk = blk % nbc;
+  blk /= nbc;
+  const int64_t rbk = blk % nbr;
+  const int64_t b = blk / nbr;
+  const int64_t r0 = rbk * br, c0 = cbk * bc;
+  const int64_t nr = R - r0 < br ? R - r0 : br;
+  const int64_t nc = C - c0 < bc ? C - c0 : bc;
+  const uint16_t* xb = x + b * R * C;
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < nr * nc; i += 256)
+    m = fmaxf(m, fabsf(__uint_as_float((uint32_t)xb[(r0 + i / nc) * C + c0 + i % nc] << 16)));
+  m = block_max<256>(m, red);
+  float s, iv;
+  if constexpr (MX) {
+    const int k = mx_exponent(m, fmax, eps, mx_mode);
+    s = exp2i(k);
+    if (threadIdx.x == 0) e8m0[blockIdx.x] = (uint8_t)(127 - k);
+  } else {
+    scale_from_amax(m, fmax, eps, s, iv);
+    if (threadIdx.x == 0) {
+      scale[blockIdx.x] = s;
+      if (inv) inv[blockIdx.x] = iv;
+    }
+  }
+  const float fm = (float)fmax;
+  for (int64_t i = threadIdx.x; i < nr * nc; i += 256) {
+    const int64_t off = b * R * C + (r0 + i / nc) * C + c0 + i % nc;
+    q[off] = cvt1<E5>(clampf(__uint_as_float((uint32_t)x[off] << 16) * s, fm));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+
+static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+template <bool E5>
+static hipError_t launch_row_t(const QuantArgs& a) {
+  const int64_t R = a.batch * a.rows;
+  if (R == 0 || a.cols == 0) return hipSuccess;
+  const bool vec = a.cols % 8 == 0 && aligned16(a.x) && aligned16(a.q);
+  dim3 grid((unsigned)R), block(256);
+  if (vec && a.cols <= 2048 * 8) {
+    const int64_t J = (a.cols + 2047) / 2048;
+    if (J <= 1)
+      hipLaunchKernelGGL((k_quant_row<1, E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+    else if (J <= 2)
+      hipLaunchKernelGGL((k_quant_row<2, E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+    else if (J <= 4)
+      hipLaunchKernelGGL((k_quant_row<4, E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+    else
+      hipLaunchKernelGGL((k_quant_row<8, E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+  } else {
+    hipLaunchKernelGGL((k_quant_row_generic<E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row(const QuantArgs& a) { return a.e5 ? launch_row_t<true>(a) : launch_row_t<false>(a); }
+
+size_t quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  if (rows <= kColRows) return 0;
+  return (size_t)(batch * cols) * sizeof(uint32_t);
+}
+
+template <bool E5>
+static hipError_t launch_col_t(const QuantArgs& a, uint32_t* colmax) {
+  const int64_t B = a.batch, R = a.rows, C = a.cols;
+  if (B == 0 || R == 0 || C == 0) return hipSuccess;
+  const bool vec = C % 8 == 0 && R % 16 == 0 && aligned16(a.x) && aligned16(a.q);
+  if (!vec) {
+    hipLaunchKernelGGL((k_quant_col_generic<E5>), dim3((unsigned)(B * C)), dim3(256), 0, a.stream, a.x, R, C, a.q,
+                       a.scale, a.inv, a.fmax, a.eps);
+    return hipGetLastError();
+  }
+  const int64_t strips = (C + 63) / 64;
+  if (R <= kColRows) {
+    // threads: 8 per row-group of 16 rows, rounded up to whole waves
+    int64_t threads = ((R + kColRPT - 1) / kColRPT) * 8;
+    threads = (threads + 63) / 64 * 64;
+    hipLaunchKernelGGL((k_quant_col<E5, 0>), dim3((unsigned)(B * strips)), dim3((unsigned)threads), 0, a.stream,
+                       a.x, R, C, strips, (int64_t)1, a.q, a.scale, a.inv, (uint32_t*)nullptr, (int64_t)1, a.fmax,
+                       a.eps);
+    return hipGetLastError();
+  }
+  const int64_t rchunks = (R + kColRows - 1) / kColRows;
+  const int64_t nwords = B * C;
+  hipLaunchKernelGGL(k_clear_words, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, a.stream, colmax, nwords);
+  hipLaunchKernelGGL((k_quant_col<E5, 2>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
+                     strips, rchunks, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
+  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
+                     strips, rchunks, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
+  return hipGetLastError();
+}
+
+// One scale for the whole tensor, written in the transposed layout
+// qT[b][c][r] (the column-major operand of a tensorwise backward GEMM).
+template <bool E5>
+static hipError_t launch_tensor_t_t(const QuantArgs& a, uint32_t* amax_word) {
+  const int64_t B = a.batch, R = a.rows, C = a.cols;
+  const int64_t n = B * R * C;
+  if (n == 0) return hipSuccess;
+  const int64_t nvec = n / 8;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  const int64_t strips = (C + 63) / 64;
+  const int64_t rchunks = (R + kColRows - 1) / kColRows;
+  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
+  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n, amax_word);
+  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
+                     strips, rchunks, a.q, a.scale, a.inv, amax_word, (int64_t)0, a.fmax, a.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws) {
+  if (a.cols % 8 != 0 || a.rows % 16 != 0) return hipErrorInvalidValue;
+  return a.e5 ? launch_tensor_t_t<true>(a, (uint32_t*)ws) : launch_tensor_t_t<false>(a, (uint32_t*)ws);
+}
+
+hipError_t launch_quant_col(const QuantArgs& a, void* ws) {
+  return a.e5 ? launch_col_t<true>(a, (uint32_t*)ws) : launch_col_t<false>(a, (uint32_t*)ws);
+}
+
+template <bool E5>
+static hipError_t launch_tensor_t(const QuantArgs& a, uint32_t* amax_word) {
+  const int64_t n = a.batch * a.rows * a.cols;
+  if (n == 0) return hipSuccess;
+  const int64_t nvec = n / 8;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
+  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n, amax_word);
+  hipLaunchKernelGGL((k_cast_tensor<E5>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n,
+                     (const uint32_t*)amax_word, a.q, a.scale, a.inv, a.fmax, a.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const QuantArgs& a, void* ws) {
+  return a.e5 ? launch_tensor_t<true>(a, (uint32_t*)ws) : launch_tensor_t<false>(a, (uint32_t*)ws);
+}
+
+template <bool E5>
+static hipError_t launch_block_t(const QuantArgs& a, int br, int bc) {
+  const int64_t B = a.batch, R = a.rows, C = a.cols;
+  if (B == 0 || R == 0 || C == 0) return hipSuccess;
+  const bool vec = C % 8 == 0 && aligned16(a.x) && aligned16(a.q);
+  const int64_t nbr = (R + br - 1) / br, nbc = (C + bc - 1) / bc;
+  if (vec && br == 1 && bc == 128) {
+    const int64_t ngroups = B * R * nbc;
+    int64_t blocks = (ngroups + 15) / 16;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((k_quant_group1d<E5, 128, false>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, B * R, C,
+                       a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
+  } else if (vec && br == 128 && bc == 128) {
+    hipLaunchKernelGGL((k_quant_block128<E5>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x, R, C, nbr,
+                       nbc, a.q, a.scale, a.inv, a.fmax, a.eps);
+  } else {
+    hipLaunchKernelGGL((k_quant_block_generic<E5, false>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x,
+                       R, C, (int64_t)br, (int64_t)bc, nbr, nbc, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_block(const QuantArgs& a, int br, int bc) {
+  return a.e5 ? launch_block_t<true>(a, br, bc) : launch_block_t<false>(a, br, bc);
+}
+
+template <bool E5>
+static hipError_t launch_mx_t(const QuantArgs& a, uint8_t* e8m0, int mode) {
+  const int64_t B = a.batch, R = a.rows, C = a.cols;
+  if (B == 0 || R == 0 || C == 0) return hipSuccess;
+  const bool vec = aligned16(a.x) && aligned16(a.q);  // C % 32 == 0 is checked by the API
+  if (vec) {
+    const int64_t ngroups = B * R * (C / 32);
+    int64_t blocks = (ngroups + 63) / 64;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((k_quant_group1d<E5, 32, true>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, B * R, C,
+                       a.q, (float*)nullptr, (float*)nullptr, e8m0, a.fmax, a.eps, mode);
+  } else {
+    const int64_t nbc = C / 32;
+    hipLaunchKernelGGL((k_quant_block_generic<E5, true>), dim3((unsigned)(B * R * nbc)), dim3(256), 0, a.stream, a.x,
+                       B * R, C, (int64_t)1, (int64_t)32, B * R, nbc, a.q, (float*)nullptr, (float*)nullptr, e8m0,
+                       a.fmax, a.eps, mode);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode) {
+  return a.e5 ? launch_mx_t<true>(a, e8m0, mode) : launch_mx_t<false>(a, e8m0, mode);
+}
+
+}  // namespace fp8dyn

@@ -1,0 +1,225 @@
+/*
+ * fp8dyn.h -- C ABI of the MI355X (gfx950) dynamic-FP8 library: fused
+ * absmax -> scale -> clamp -> cast quantization at five granularities, and
+ * the scaled FP8 GEMMs (dense and MoE grouped) that consume those scales.
+ *
+ * The operations are the ones described on these pages:
+ *  [P-AMD]  "FP8 training on AMD GPUs with TorchTitan and TorchAO: upstreaming
+ *           performance" (AMD blog): section "AMD FP8 format in TorchAO"
+ *           (e4m3fnuz table; tensorwise / rowwise / blockwise / MXFP8
+ *           granularities), section "Scaling FP8 to MoE Architectures"
+ *           (Figure 3: per-row activation scales, per-expert-column weight
+ *           scales, an offset tensor routing rows to experts, one launch),
+ *           section "Triton Kernel Optimization" (the chain absmax -> scale ->
+ *           clamp and cast, fused into one pass), Levels 1-3 (no transpose
+ *           copy, coalesced transposed stores, relaxed atomics).
+ *  [P-TAO]  "FP8 Training: Quantization, Autograd, Torchao": section 2 "The
+ *           quantization math" (amax, fp64 scale with an eps clamp, clamp and
+ *           cast, inverse scale), section 3 "Format choice" (e4m3 448 / fnuz
+ *           240 / e5m2 57344; e4m3 for activations and weights, e5m2 for
+ *           gradients), section 4 "_scaled_mm layout requirements" (A
+ *           row-major, B column-major, the GEMM multiplies by the inverse
+ *           scales), section 6 (three GEMMs per linear layer).
+ *
+ * Conventions shared by every call
+ *  - Pointers named x, w, gy, a, b, q, scale, inv_scale, out, y, gx, gw, ws,
+ *    offsets are DEVICE pointers owned by the caller. The library never
+ *    allocates or frees memory in a call and keeps no pointer after it
+ *    returns. Its only state is a per-device cache of fp8_probe's answer.
+ *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *  - stream is a hipStream_t (NULL = the null stream). Every call only
+ *    enqueues work on it and returns; results are valid once the stream has
+ *    been synchronized. No call synchronizes the device or reads device
+ *    data back to the host.
+ *  - Every argument is validated on the host before anything is launched; on
+ *    any error nothing is launched and the status says why. A problem with a
+ *    zero dimension is a successful no-op. Launch failures return
+ *    FP8_ERR_DEVICE; faults inside a kernel surface at the caller's next
+ *    synchronization (fp8_last_device_error keeps the last HIP error seen).
+ *  - eps must be finite and > 0; 1e-12 is the usual value.
+ *  - Quantization writes `scale` (the quantize multiplier fp8_max/amax) and,
+ *    when inv_scale is not NULL, its fp64 reciprocal rounded to fp32. GEMMs
+ *    take only the inverse scales.
+ *  - Device pointers to bf16/fp8 data must be 16-byte aligned, scale arrays
+ *    4-byte aligned.
+ */
+#ifndef FP8DYN_H
+#define FP8DYN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define FP8DYN_API __attribute__((visibility("default")))
+#else
+#define FP8DYN_API
+#endif
+
+/* FP8 encodings [P-TAO section 3 table; P-AMD "AMD FP8 format in TorchAO"].
+ * *_NATIVE resolve, per device, to the variant this GPU's converts and
+ * matrix cores use, as measured by fp8_probe. */
+typedef enum {
+    FP8_E4M3FN = 0,      /* OCP e4m3: max 448, has -0, NaN = 0x7F/0xFF */
+    FP8_E4M3FNUZ = 1,    /* max 240, no -0, 0x80 = NaN */
+    FP8_E5M2 = 2,        /* OCP e5m2: max 57344, has -0, inf/NaN */
+    FP8_E5M2FNUZ = 3,    /* max 57344, no -0, 0x80 = NaN */
+    FP8_E4M3_NATIVE = 4,
+    FP8_E5M2_NATIVE = 5
+} fp8_format;
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, eps <= 0 */
+    FP8_ERR_ALIGNMENT = 2,        /* pointer or size alignment rule broken */
+    FP8_ERR_UNSUPPORTED = 3,      /* format or shape this GPU/library cannot do */
+    FP8_ERR_WORKSPACE = 4,        /* workspace missing or too small */
+    FP8_ERR_DEVICE = 5            /* a HIP call failed */
+} fp8_status;
+
+typedef enum {
+    FP8_SCALE_TENSOR = 0,   /* one inverse scale per operand: a_inv[1], b_inv[1] */
+    FP8_SCALE_ROW = 1,      /* a_inv[M], b_inv[N] (grouped: b_inv[E][N]) */
+    FP8_SCALE_BLOCK128 = 2, /* a_inv[M][K/128], b_inv[E][N/128][K/128] */
+    FP8_SCALE_MX32 = 3      /* E8M0 bytes: a[M][K/32], b[E][N][K/32] */
+} fp8_scaling;
+
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out;
+
+typedef enum {
+    FP8_MX_POW2_FLOOR = 0, /* scale = largest 2^k with amax*2^k <= fp8_max (never clips) */
+    FP8_MX_OCP = 1         /* OCP MX rule: 2^(floor(log2 amax) - emax_elem), saturating */
+} fp8_mx_mode;
+
+typedef enum {
+    FP8_RECIPE_TENSORWISE = 0,        /* one scale per tensor, all GEMMs FP8 */
+    FP8_RECIPE_ROWWISE_BF16_WGRAD = 1 /* rowwise FP8 forward and grad-input; BF16 grad-weight */
+} fp8_recipe;
+
+/* ---- device facts -------------------------------------------------------- */
+
+/* Measures, on `device`, which e4m3 and e5m2 variants the hardware FP8
+ * converts and FP8 matrix-core instructions use (a wrong max silently
+ * corrupts results [P-AMD "AMD FP8 format in TorchAO"]). Runs two tiny
+ * kernels and synchronizes once; the answer is cached per device.
+ * Returns FP8_ERR_UNSUPPORTED if the device is not gfx950 or the converts and
+ * the matrix cores disagree. Output pointers are host pointers, may be NULL. */
+FP8DYN_API fp8_status fp8_probe(int device, fp8_format* e4m3_native, fp8_format* e5m2_native);
+
+FP8DYN_API const char* fp8_status_string(fp8_status s);
+/* The last HIP error code (hipError_t value) the library saw, 0 if none. */
+FP8DYN_API int fp8_last_device_error(void);
+/* Largest finite value of a format (host helper; NATIVE formats need a probed device). */
+FP8DYN_API double fp8_format_max(fp8_format f);
+
+/* ---- quantization [P-TAO section 2; P-AMD "Triton Kernel Optimization"] ----
+ * Per group g: amax = max |x| (fp32); s = fp8_max / max(amax, eps) in fp64;
+ * scale[g] = (float)s; inv_scale[g] = (float)(1/s);
+ * q = RNE-encode(clamp((float)x * scale[g], -fp8_max, fp8_max)).
+ * Formats: the two NATIVE variants (after fp8_probe) are supported on gfx950;
+ * the others return FP8_ERR_UNSUPPORTED. Each call is one pass over x except
+ * where stated. */
+
+/* One scale for all n elements. Needs a device workspace of
+ * fp8_quant_tensor_ws_bytes() bytes (ws, 256-byte aligned); its content on
+ * entry does not matter. Three stream-ordered launches: clear, amax with
+ * relaxed atomics [P-AMD Level 3], cast. x: [n] bf16, q: [n]. */
+FP8DYN_API fp8_status fp8_quant_tensor(const uint16_t* x, int64_t n, fp8_format fmt, double eps,
+                                       uint8_t* q, float* scale, float* inv_scale,
+                                       void* ws, size_t ws_bytes, void* stream);
+FP8DYN_API size_t fp8_quant_tensor_ws_bytes(void);
+
+/* Row groups: x [batch][rows][cols] -> q same layout, scale/inv [batch][rows]. */
+FP8DYN_API fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                    fp8_format fmt, double eps, uint8_t* q, float* scale,
+                                    float* inv_scale, void* stream);
+
+/* Column groups with the transposed output the GEMM's column-major operand
+ * needs [P-TAO section 4; P-AMD Level 1 and Level 2]: x [batch][rows][cols] ->
+ * qT [batch][cols][rows], scale/inv [batch][cols]. Single pass when
+ * rows <= 4096; otherwise a column-amax pass with relaxed atomics and a cast
+ * pass, which need ws of fp8_quant_col_ws_bytes(batch, rows, cols) bytes. */
+FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                    fp8_format fmt, double eps, uint8_t* qT, float* scale,
+                                    float* inv_scale, void* ws, size_t ws_bytes, void* stream);
+FP8DYN_API size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/* Blocks of block_rows x block_cols (1x128 for activations, 128x128 for
+ * weights [P-AMD "AMD FP8 format in TorchAO", blockwise]): x
+ * [batch][rows][cols] -> q same layout, scale/inv
+ * [batch][ceil(rows/block_rows)][ceil(cols/block_cols)]. Partial edge blocks
+ * use their valid elements. block_rows in {1, 128}, block_cols == 128. */
+FP8DYN_API fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                      int block_rows, int block_cols, fp8_format fmt, double eps,
+                                      uint8_t* q, float* scale, float* inv_scale, void* stream);
+
+/* MXFP8: 32 consecutive elements along cols share one E8M0 power-of-two
+ * scale [P-AMD "AMD FP8 format in TorchAO", MXFP8; "Summary and Next Steps"].
+ * e8m0[g] = 127 + log2(dequantize factor); q = encode(clamp(x * 2^k)).
+ * cols % 32 == 0. x [batch][rows][cols] -> q same, e8m0 [batch][rows][cols/32]. */
+FP8DYN_API fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                   fp8_format fmt, fp8_mx_mode mode, double eps, uint8_t* q,
+                                   uint8_t* e8m0, void* stream);
+
+/* ---- GEMMs [P-TAO section 4; P-AMD "Scaling FP8 to MoE Architectures"] ----
+ * out[m][n] = a_inv * b_inv * sum_k dec(a[m][k]) * dec(b[n][k]), fp32
+ * accumulation on the matrix cores, scales applied in fp32, stored as bf16
+ * (round to nearest even) or fp32.
+ * a: [M][K] row-major codes; b: [N][K] row-major codes, i.e. the column-major
+ * K x N operand (a Linear weight as stored). fa in {e4m3, e5m2} native
+ * variants, fb the e4m3 native variant. K % 16 == 0 (K % 128 == 0 for
+ * BLOCK128, K % 32 == 0 for MX32), N % 16 == 0.
+ * use_fast_accum is accepted and has no effect: the matrix cores accumulate
+ * in fp32 either way [P-TAO section 5]. Scaling: TENSOR or ROW. */
+FP8DYN_API fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
+                                    fp8_scaling scaling, const float* a_inv, const float* b_inv,
+                                    int64_t M, int64_t N, int64_t K, fp8_out out_type, void* out,
+                                    int use_fast_accum, void* stream);
+
+/* MoE grouped GEMM in one launch: rows [offsets[e], offsets[e+1]) of a use
+ * expert e's b[e] ([E][N][K]) and scales. offsets: DEVICE int32 [E+1] with
+ * offsets[0] = 0, non-decreasing, offsets[E] = Mtot (not read back; use
+ * fp8_validate_offsets on a host copy to check). Empty experts are skipped.
+ * Scaling: ROW (a_inv [Mtot] float, b_inv [E][N] float), BLOCK128
+ * (a_inv [Mtot][K/128], b_inv [E][N/128][K/128] float; N % 128 == 0) or MX32
+ * (E8M0 bytes a [Mtot][K/32], b [E][N][K/32]). */
+FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
+                                     fp8_scaling scaling, const void* a_scale, const void* b_scale,
+                                     const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N,
+                                     int64_t K, fp8_out out_type, void* out, void* stream);
+
+/* BF16 weight-gradient GEMM [P-AMD Figure 1 caption: the weight-update GEMM
+ * stays in BF16]: gw[n][k] = sum_m gy[m][n] * x[m][k], fp32 accumulation,
+ * bf16 out. gy [M][N], x [M][K], gw [N][K], all bf16 row-major; no
+ * transposed copies are made. N % 16 == 0, K % 16 == 0, M % 16 == 0. */
+FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N,
+                                     int64_t K, uint16_t* gw, void* stream);
+
+/* ---- one Linear layer [P-TAO section 6; P-AMD "AMD FP8 format in TorchAO"] ---
+ * Forward y = x w^T: x [M][K], w [N][K] bf16; quantize both (TENSORWISE: one
+ * scale each; ROWWISE: per row of x and of w, e4m3), then the scaled GEMM;
+ * y [M][N] bf16 or fp32. ws: fp8_linear_ws_bytes(M, N, K, recipe) bytes. */
+FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                     int64_t K, fp8_recipe recipe, double eps, fp8_out out_type,
+                                     void* y, void* ws, size_t ws_bytes, void* stream);
+/* Backward: gy [M][N] bf16 (quantized e5m2: per row for ROWWISE, one scale
+ * for TENSORWISE); w quantized e4m3 per column with the transposed output;
+ * gx [M][K] bf16 = FP8 GEMM. gw [N][K] bf16: the BF16 GEMM for ROWWISE; for
+ * TENSORWISE also BF16 here (the all-FP8 weight gradient is not provided). */
+FP8DYN_API fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w,
+                                     int64_t M, int64_t N, int64_t K, fp8_recipe recipe, double eps,
+                                     uint16_t* gx, uint16_t* gw, void* ws, size_t ws_bytes,
+                                     void* stream);
+FP8DYN_API size_t fp8_linear_ws_bytes(int64_t M, int64_t N, int64_t K, fp8_recipe recipe);
+
+/* Host helper: checks a HOST copy of an offsets array (offsets[0] == 0,
+ * non-decreasing, offsets[E] == Mtot). */
+FP8DYN_API fp8_status fp8_validate_offsets(const int32_t* host_offsets, int32_t E, int64_t Mtot);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

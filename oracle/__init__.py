@@ -73,6 +73,12 @@ def _load():
         "orc_grouped_mm_sample": (None, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, P, P, I64, P]),
         "orc_wgrad_bf16": (None, [P, P, I64, I64, I64, P, I]),
         "orc_wgrad_bf16_sample": (None, [P, P, I64, I64, I64, P, P, I64, P]),
+        "orc_scaled_mm_abs": (None, [P, I, P, I, I, P, P, I64, I64, I64, P, I]),
+        "orc_scaled_mm_abs_sample": (None, [P, I, P, I, I, P, P, I64, I64, I64, P, P, I64, P]),
+        "orc_grouped_mm_abs": (None, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, P, I]),
+        "orc_grouped_mm_abs_sample": (None, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, P, P, I64, P]),
+        "orc_wgrad_bf16_abs": (None, [P, P, I64, I64, I64, P, I]),
+        "orc_wgrad_bf16_abs_sample": (None, [P, P, I64, I64, I64, P, P, I64, P]),
         "orc_threads_used": (I, [I]),
     }
     for name, (res, args) in sig.items():
@@ -208,8 +214,8 @@ def quant_mx(x, fmt, mode=MX_POW2_FLOOR, eps=1e-12, threads=0):
 
 # ---- GEMMs -------------------------------------------------------------------
 
-def scaled_mm(a, fa, b, fb, scaling, a_inv, b_inv, threads=0):
-    """a [M,K] codes, b [N,K] codes -> fp64 [M,N]."""
+def scaled_mm(a, fa, b, fb, scaling, a_inv, b_inv, threads=0, absolute=False):
+    """a [M,K] codes, b [N,K] codes -> fp64 [M,N]. absolute=True: sum of |products| x |scales|."""
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
     M, K = a.shape
@@ -217,11 +223,12 @@ def scaled_mm(a, fa, b, fb, scaling, a_inv, b_inv, threads=0):
     a_inv = np.ascontiguousarray(a_inv, np.float32)
     b_inv = np.ascontiguousarray(b_inv, np.float32)
     out = np.empty((M, N), np.float64)
-    _load().orc_scaled_mm(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(a_inv), _p(b_inv), M, N, K, _p(out), int(threads))
+    fn = _load().orc_scaled_mm_abs if absolute else _load().orc_scaled_mm
+    fn(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(a_inv), _p(b_inv), M, N, K, _p(out), int(threads))
     return out
 
 
-def scaled_mm_sample(a, fa, b, fb, scaling, a_inv, b_inv, rows, cols):
+def scaled_mm_sample(a, fa, b, fb, scaling, a_inv, b_inv, rows, cols, absolute=False):
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
     M, K = a.shape
@@ -231,8 +238,9 @@ def scaled_mm_sample(a, fa, b, fb, scaling, a_inv, b_inv, rows, cols):
     a_inv = np.ascontiguousarray(a_inv, np.float32)
     b_inv = np.ascontiguousarray(b_inv, np.float32)
     out = np.empty(rows.shape, np.float64)
-    _load().orc_scaled_mm_sample(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(a_inv), _p(b_inv),
-                                 M, N, K, _p(rows), _p(cols), rows.size, _p(out))
+    fn = _load().orc_scaled_mm_abs_sample if absolute else _load().orc_scaled_mm_sample
+    fn(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(a_inv), _p(b_inv), M, N, K, _p(rows), _p(cols),
+       rows.size, _p(out))
     return out
 
 
@@ -240,7 +248,7 @@ def _scale_arr(s, scaling):
     return np.ascontiguousarray(s, np.uint8 if scaling == SCALE_MX32 else np.float32)
 
 
-def grouped_mm(a, fa, b, fb, scaling, a_scale, b_scale, offsets, threads=0):
+def grouped_mm(a, fa, b, fb, scaling, a_scale, b_scale, offsets, threads=0, absolute=False):
     """a [Mtot,K], b [E,N,K], offsets int32 [E+1] (host) -> fp64 [Mtot,N]."""
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
@@ -249,12 +257,12 @@ def grouped_mm(a, fa, b, fb, scaling, a_scale, b_scale, offsets, threads=0):
     off = np.ascontiguousarray(offsets, np.int32)
     sa, sb = _scale_arr(a_scale, scaling), _scale_arr(b_scale, scaling)
     out = np.empty((Mtot, N), np.float64)
-    _load().orc_grouped_mm(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(sa), _p(sb), _p(off),
-                           E, Mtot, N, K, _p(out), int(threads))
+    fn = _load().orc_grouped_mm_abs if absolute else _load().orc_grouped_mm
+    fn(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(sa), _p(sb), _p(off), E, Mtot, N, K, _p(out), int(threads))
     return out
 
 
-def grouped_mm_sample(a, fa, b, fb, scaling, a_scale, b_scale, offsets, rows, cols):
+def grouped_mm_sample(a, fa, b, fb, scaling, a_scale, b_scale, offsets, rows, cols, absolute=False):
     a = np.ascontiguousarray(a, np.uint8)
     b = np.ascontiguousarray(b, np.uint8)
     Mtot, K = a.shape
@@ -264,29 +272,32 @@ def grouped_mm_sample(a, fa, b, fb, scaling, a_scale, b_scale, offsets, rows, co
     rows = np.ascontiguousarray(rows, np.int64)
     cols = np.ascontiguousarray(cols, np.int64)
     out = np.empty(rows.shape, np.float64)
-    _load().orc_grouped_mm_sample(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(sa), _p(sb), _p(off),
-                                  E, Mtot, N, K, _p(rows), _p(cols), rows.size, _p(out))
+    fn = _load().orc_grouped_mm_abs_sample if absolute else _load().orc_grouped_mm_sample
+    fn(_p(a), _fmt(fa), _p(b), _fmt(fb), int(scaling), _p(sa), _p(sb), _p(off), E, Mtot, N, K, _p(rows), _p(cols),
+       rows.size, _p(out))
     return out
 
 
-def wgrad_bf16(g, x, threads=0):
+def wgrad_bf16(g, x, threads=0, absolute=False):
     """g [M,N] bf16 bits, x [M,K] bf16 bits -> dW [N,K] fp64."""
     g, x = _u16(g), _u16(x)
     M, N = g.shape
     K = x.shape[1]
     out = np.empty((N, K), np.float64)
-    _load().orc_wgrad_bf16(_p(g), _p(x), M, N, K, _p(out), int(threads))
+    fn = _load().orc_wgrad_bf16_abs if absolute else _load().orc_wgrad_bf16
+    fn(_p(g), _p(x), M, N, K, _p(out), int(threads))
     return out
 
 
-def wgrad_bf16_sample(g, x, ns, ks):
+def wgrad_bf16_sample(g, x, ns, ks, absolute=False):
     g, x = _u16(g), _u16(x)
     M, N = g.shape
     K = x.shape[1]
     ns = np.ascontiguousarray(ns, np.int64)
     ks = np.ascontiguousarray(ks, np.int64)
     out = np.empty(ns.shape, np.float64)
-    _load().orc_wgrad_bf16_sample(_p(g), _p(x), M, N, K, _p(ns), _p(ks), ns.size, _p(out))
+    fn = _load().orc_wgrad_bf16_abs_sample if absolute else _load().orc_wgrad_bf16_sample
+    fn(_p(g), _p(x), M, N, K, _p(ns), _p(ks), ns.size, _p(out))
     return out
 
 

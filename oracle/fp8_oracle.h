@@ -126,6 +126,28 @@ void orc_wgrad_bf16(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, 
 void orc_wgrad_bf16_sample(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
                            const int64_t* ns_idx, const int64_t* ks_idx, int64_t ns, double* out);
 
+/* The same sums with every product taken in absolute value, times |scales|:
+ * S = sum_k |dec(a) dec(b)| |inv_a inv_b| (per scale block). S bounds the
+ * rounding error of any summation order of the product (componentwise error
+ * analysis of dot products), so GEMM checks compare |y - ref| against it. */
+void orc_scaled_mm_abs(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                       const float* a_inv, const float* b_inv,
+                       int64_t M, int64_t N, int64_t K, double* out, int threads);
+void orc_scaled_mm_abs_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                              const float* a_inv, const float* b_inv, int64_t M, int64_t N, int64_t K,
+                              const int64_t* rows, const int64_t* cols, int64_t ns, double* out);
+void orc_grouped_mm_abs(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                        const void* a_scale, const void* b_scale, const int32_t* offsets,
+                        int32_t E, int64_t Mtot, int64_t N, int64_t K, double* out, int threads);
+void orc_grouped_mm_abs_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                               const void* a_scale, const void* b_scale, const int32_t* offsets,
+                               int32_t E, int64_t Mtot, int64_t N, int64_t K,
+                               const int64_t* rows, const int64_t* cols, int64_t ns, double* out);
+void orc_wgrad_bf16_abs(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                        double* dw, int threads);
+void orc_wgrad_bf16_abs_sample(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                               const int64_t* ns_idx, const int64_t* ks_idx, int64_t ns, double* out);
+
 int orc_threads_used(int threads);
 
 #ifdef __cplusplus

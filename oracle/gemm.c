@@ -33,9 +33,15 @@ static void build_table(int fmt, dec_table* t) {
     for (int c = 0; c < 256; ++c) t->v[c] = orc_fp8_decode(fmt, (uint8_t)c);
 }
 
-static double dot(const dec_table* ta, const uint8_t* a, const dec_table* tb, const uint8_t* b, int64_t n) {
+/* sum_k dec(a_k) * dec(b_k); with absolute != 0, sum_k |dec(a_k) * dec(b_k)|. */
+static double dot(const dec_table* ta, const uint8_t* a, const dec_table* tb, const uint8_t* b, int64_t n,
+                  int absolute) {
     double acc = 0.0;
-    for (int64_t k = 0; k < n; ++k) acc += ta->v[a[k]] * tb->v[b[k]];
+    if (absolute) {
+        for (int64_t k = 0; k < n; ++k) acc += fabs(ta->v[a[k]] * tb->v[b[k]]);
+    } else {
+        for (int64_t k = 0; k < n; ++k) acc += ta->v[a[k]] * tb->v[b[k]];
+    }
     return acc;
 }
 
@@ -44,18 +50,20 @@ static double e8m0_value(uint8_t e) { return ldexp(1.0, (int)e - 127); }
 /* One output element of the grouped (or dense, E = 1) product. */
 static double grouped_elem(const dec_table* ta, const dec_table* tb, const uint8_t* a, const uint8_t* b,
                            int scaling, const void* a_scale, const void* b_scale, int64_t e,
-                           int64_t m, int64_t n, int64_t N, int64_t K) {
+                           int64_t m, int64_t n, int64_t N, int64_t K, int ab) {
     const uint8_t* ar = a + m * K;
     const uint8_t* br = b + (e * N + n) * K;
     if (scaling == ORC_SCALE_TENSOR) {
         const float* sa = (const float*)a_scale;
         const float* sb = (const float*)b_scale;
-        return dot(ta, ar, tb, br, K) * (double)sa[0] * (double)sb[0];
+        double sc = (double)sa[0] * (double)sb[0];
+        return dot(ta, ar, tb, br, K, ab) * (ab ? fabs(sc) : sc);
     }
     if (scaling == ORC_SCALE_ROW) {
         const float* sa = (const float*)a_scale;
         const float* sb = (const float*)b_scale;
-        return dot(ta, ar, tb, br, K) * (double)sa[m] * (double)sb[e * N + n];
+        double sc = (double)sa[m] * (double)sb[e * N + n];
+        return dot(ta, ar, tb, br, K, ab) * (ab ? fabs(sc) : sc);
     }
     if (scaling == ORC_SCALE_BLOCK128) {
         const float* sa = (const float*)a_scale;
@@ -63,8 +71,9 @@ static double grouped_elem(const dec_table* ta, const dec_table* tb, const uint8
         int64_t nkb = K / 128, nnb = N / 128;
         double acc = 0.0;
         for (int64_t kb = 0; kb < nkb; ++kb) {
-            double part = dot(ta, ar + kb * 128, tb, br + kb * 128, 128);
-            acc += part * (double)sa[m * nkb + kb] * (double)sb[(e * nnb + n / 128) * nkb + kb];
+            double part = dot(ta, ar + kb * 128, tb, br + kb * 128, 128, ab);
+            double sc = (double)sa[m * nkb + kb] * (double)sb[(e * nnb + n / 128) * nkb + kb];
+            acc += part * (ab ? fabs(sc) : sc);
         }
         return acc;
     }
@@ -74,16 +83,16 @@ static double grouped_elem(const dec_table* ta, const dec_table* tb, const uint8
         int64_t ng = K / 32;
         double acc = 0.0;
         for (int64_t g = 0; g < ng; ++g) {
-            double part = dot(ta, ar + g * 32, tb, br + g * 32, 32);
+            double part = dot(ta, ar + g * 32, tb, br + g * 32, 32, ab);
             acc += part * e8m0_value(sa[m * ng + g]) * e8m0_value(sb[(e * N + n) * ng + g]);
         }
         return acc;
     }
 }
 
-void orc_scaled_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
-                   const float* a_inv, const float* b_inv,
-                   int64_t M, int64_t N, int64_t K, double* out, int threads) {
+static void scaled_mm_impl(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                           const float* a_inv, const float* b_inv,
+                           int64_t M, int64_t N, int64_t K, double* out, int threads, int ab) {
     dec_table ta, tb;
     int nt = orc_threads_used(threads);
     (void)nt;
@@ -92,19 +101,44 @@ void orc_scaled_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scali
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            out[m * N + n] = grouped_elem(&ta, &tb, a, b, scaling, a_inv, b_inv, 0, m, n, N, K);
+            out[m * N + n] = grouped_elem(&ta, &tb, a, b, scaling, a_inv, b_inv, 0, m, n, N, K, ab);
+}
+
+void orc_scaled_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                   const float* a_inv, const float* b_inv,
+                   int64_t M, int64_t N, int64_t K, double* out, int threads) {
+    scaled_mm_impl(a, fa, b, fb, scaling, a_inv, b_inv, M, N, K, out, threads, 0);
+}
+
+void orc_scaled_mm_abs(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                       const float* a_inv, const float* b_inv,
+                       int64_t M, int64_t N, int64_t K, double* out, int threads) {
+    scaled_mm_impl(a, fa, b, fb, scaling, a_inv, b_inv, M, N, K, out, threads, 1);
+}
+
+static void scaled_mm_sample_impl(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                                  const float* a_inv, const float* b_inv, int64_t N, int64_t K,
+                                  const int64_t* rows, const int64_t* cols, int64_t ns, double* out, int ab) {
+    dec_table ta, tb;
+    build_table(fa, &ta);
+    build_table(fb, &tb);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < ns; ++i)
+        out[i] = grouped_elem(&ta, &tb, a, b, scaling, a_inv, b_inv, 0, rows[i], cols[i], N, K, ab);
 }
 
 void orc_scaled_mm_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
                           const float* a_inv, const float* b_inv, int64_t M, int64_t N, int64_t K,
                           const int64_t* rows, const int64_t* cols, int64_t ns, double* out) {
-    dec_table ta, tb;
     (void)M;
-    build_table(fa, &ta);
-    build_table(fb, &tb);
-#pragma omp parallel for schedule(dynamic, 64)
-    for (int64_t i = 0; i < ns; ++i)
-        out[i] = grouped_elem(&ta, &tb, a, b, scaling, a_inv, b_inv, 0, rows[i], cols[i], N, K);
+    scaled_mm_sample_impl(a, fa, b, fb, scaling, a_inv, b_inv, N, K, rows, cols, ns, out, 0);
+}
+
+void orc_scaled_mm_abs_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                              const float* a_inv, const float* b_inv, int64_t M, int64_t N, int64_t K,
+                              const int64_t* rows, const int64_t* cols, int64_t ns, double* out) {
+    (void)M;
+    scaled_mm_sample_impl(a, fa, b, fb, scaling, a_inv, b_inv, N, K, rows, cols, ns, out, 1);
 }
 
 /* Expert owning row m: the e with off[e] <= m < off[e+1]. */
@@ -114,9 +148,9 @@ static int64_t expert_of(const int32_t* off, int32_t E, int64_t m) {
     return -1;
 }
 
-void orc_grouped_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
-                    const void* a_scale, const void* b_scale, const int32_t* offsets,
-                    int32_t E, int64_t Mtot, int64_t N, int64_t K, double* out, int threads) {
+static void grouped_mm_impl(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                            const void* a_scale, const void* b_scale, const int32_t* offsets,
+                            int32_t E, int64_t Mtot, int64_t N, int64_t K, double* out, int threads, int ab) {
     dec_table ta, tb;
     int nt = orc_threads_used(threads);
     (void)nt;
@@ -126,7 +160,34 @@ void orc_grouped_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scal
     for (int64_t m = 0; m < Mtot; ++m) {
         int64_t e = expert_of(offsets, E, m);
         for (int64_t n = 0; n < N; ++n)
-            out[m * N + n] = e < 0 ? 0.0 : grouped_elem(&ta, &tb, a, b, scaling, a_scale, b_scale, e, m, n, N, K);
+            out[m * N + n] = e < 0 ? 0.0 : grouped_elem(&ta, &tb, a, b, scaling, a_scale, b_scale, e, m, n, N, K, ab);
+    }
+}
+
+void orc_grouped_mm(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                    const void* a_scale, const void* b_scale, const int32_t* offsets,
+                    int32_t E, int64_t Mtot, int64_t N, int64_t K, double* out, int threads) {
+    grouped_mm_impl(a, fa, b, fb, scaling, a_scale, b_scale, offsets, E, Mtot, N, K, out, threads, 0);
+}
+
+void orc_grouped_mm_abs(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                        const void* a_scale, const void* b_scale, const int32_t* offsets,
+                        int32_t E, int64_t Mtot, int64_t N, int64_t K, double* out, int threads) {
+    grouped_mm_impl(a, fa, b, fb, scaling, a_scale, b_scale, offsets, E, Mtot, N, K, out, threads, 1);
+}
+
+static void grouped_sample_impl(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                                const void* a_scale, const void* b_scale, const int32_t* offsets,
+                                int32_t E, int64_t N, int64_t K,
+                                const int64_t* rows, const int64_t* cols, int64_t ns, double* out, int ab) {
+    dec_table ta, tb;
+    build_table(fa, &ta);
+    build_table(fb, &tb);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < ns; ++i) {
+        int64_t e = expert_of(offsets, E, rows[i]);
+        out[i] = e < 0 ? 0.0
+                       : grouped_elem(&ta, &tb, a, b, scaling, a_scale, b_scale, e, rows[i], cols[i], N, K, ab);
     }
 }
 
@@ -134,15 +195,26 @@ void orc_grouped_mm_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, i
                            const void* a_scale, const void* b_scale, const int32_t* offsets,
                            int32_t E, int64_t Mtot, int64_t N, int64_t K,
                            const int64_t* rows, const int64_t* cols, int64_t ns, double* out) {
-    dec_table ta, tb;
     (void)Mtot;
-    build_table(fa, &ta);
-    build_table(fb, &tb);
-#pragma omp parallel for schedule(dynamic, 64)
-    for (int64_t i = 0; i < ns; ++i) {
-        int64_t e = expert_of(offsets, E, rows[i]);
-        out[i] = e < 0 ? 0.0 : grouped_elem(&ta, &tb, a, b, scaling, a_scale, b_scale, e, rows[i], cols[i], N, K);
+    grouped_sample_impl(a, fa, b, fb, scaling, a_scale, b_scale, offsets, E, N, K, rows, cols, ns, out, 0);
+}
+
+void orc_grouped_mm_abs_sample(const uint8_t* a, int fa, const uint8_t* b, int fb, int scaling,
+                               const void* a_scale, const void* b_scale, const int32_t* offsets,
+                               int32_t E, int64_t Mtot, int64_t N, int64_t K,
+                               const int64_t* rows, const int64_t* cols, int64_t ns, double* out) {
+    (void)Mtot;
+    grouped_sample_impl(a, fa, b, fb, scaling, a_scale, b_scale, offsets, E, N, K, rows, cols, ns, out, 1);
+}
+
+static double wgrad_elem(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                         int64_t n, int64_t k, int ab) {
+    double acc = 0.0;
+    for (int64_t m = 0; m < M; ++m) {
+        double p = (double)orc_bf16_to_f32(g[m * N + n]) * (double)orc_bf16_to_f32(x[m * K + k]);
+        acc += ab ? fabs(p) : p;
     }
+    return acc;
 }
 
 void orc_wgrad_bf16(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
@@ -151,22 +223,26 @@ void orc_wgrad_bf16(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, 
     (void)nt;
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
     for (int64_t n = 0; n < N; ++n)
-        for (int64_t k = 0; k < K; ++k) {
-            double acc = 0.0;
-            for (int64_t m = 0; m < M; ++m)
-                acc += (double)orc_bf16_to_f32(g[m * N + n]) * (double)orc_bf16_to_f32(x[m * K + k]);
-            dw[n * K + k] = acc;
-        }
+        for (int64_t k = 0; k < K; ++k) dw[n * K + k] = wgrad_elem(g, x, M, N, K, n, k, 0);
+}
+
+void orc_wgrad_bf16_abs(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                        double* dw, int threads) {
+    int nt = orc_threads_used(threads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) dw[n * K + k] = wgrad_elem(g, x, M, N, K, n, k, 1);
 }
 
 void orc_wgrad_bf16_sample(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
                            const int64_t* ns_idx, const int64_t* ks_idx, int64_t ns, double* out) {
 #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t i = 0; i < ns; ++i) {
-        int64_t n = ns_idx[i], k = ks_idx[i];
-        double acc = 0.0;
-        for (int64_t m = 0; m < M; ++m)
-            acc += (double)orc_bf16_to_f32(g[m * N + n]) * (double)orc_bf16_to_f32(x[m * K + k]);
-        out[i] = acc;
-    }
+    for (int64_t i = 0; i < ns; ++i) out[i] = wgrad_elem(g, x, M, N, K, ns_idx[i], ks_idx[i], 0);
+}
+
+void orc_wgrad_bf16_abs_sample(const uint16_t* g, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                               const int64_t* ns_idx, const int64_t* ks_idx, int64_t ns, double* out) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < ns; ++i) out[i] = wgrad_elem(g, x, M, N, K, ns_idx[i], ks_idx[i], 1);
 }

@@ -1,0 +1,236 @@
+"""GPU parity of the FP8 GEMMs (dense, grouped; tensor, row, block, MX scales) and of the
+BF16 weight-gradient GEMM against the oracle's fp64 products of the same quantized
+operands. Acceptance (tests/gpu_util.check_gemm): normwise max relative error at most
+1e-2 for bf16 output and 2e-3 for fp32 output, and every element within the
+componentwise accumulation bound 2^-9 * sum|products| plus the output rounding. The
+operands here are random codes over a format's whole range, the hardest case for the
+matrix cores' internal accumulation."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (check_gemm, gpu, have_gpu, lib, to_dev, to_dev_bf16)
+
+pytestmark = [gpu, pytest.mark.skipif(not have_gpu(), reason="needs an MI355X")]
+
+
+@pytest.fixture(scope="module")
+def f():
+    oracle.build(force=False)
+    synth.build(force=False)
+    return lib()
+
+
+def _names(f):
+    e4, e5 = f.fp8_probe(0)
+    name = {0: "e4m3fn", 1: "e4m3fnuz", 2: "e5m2", 3: "e5m2fnuz"}
+    return name[e4], name[e5]
+
+
+def _codes(name, shape, rng, lo=None):
+    """Random finite codes of a format."""
+    tab = oracle.decode(name, np.arange(256))
+    ok = np.nonzero(np.isfinite(tab))[0]
+    return rng.choice(ok, size=shape).astype(np.uint8)
+
+
+def _out(shape, f32):
+    import torch
+    return torch.empty(shape, dtype=torch.float32 if f32 else torch.bfloat16, device="cuda:0")
+
+
+def _host(out):
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def test_matrix_core_decodes_every_code(f):
+    """A has code c at k = 0 of row c (zeros elsewhere); B row 0 holds the code of 1.0.
+    out[c][0] must be exactly the oracle's value of code c, for all finite codes, both
+    formats on the A side and the e4m3 format on the B side."""
+    import torch
+    e4, e5 = _names(f)
+    one_b = oracle.encode(e4, [1.0])[0]
+    for fa, name in ((f.E4M3_NATIVE, e4), (f.E5M2_NATIVE, e5)):
+        tab = oracle.decode(name, np.arange(256))
+        a = np.zeros((256, 128), np.uint8)
+        a[:, 0] = np.arange(256)
+        fin = np.isfinite(tab)
+        a[~fin, 0] = 0
+        b = np.zeros((16, 128), np.uint8)
+        b[0, 0] = one_b
+        out = _out((256, 16), True)
+        one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+        f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()[:, 0].astype(np.float64)
+        assert np.array_equal(got[fin], tab[fin]), name
+        assert np.all(out.cpu().numpy()[:, 1:] == 0)
+    # and e4m3 codes on the B side
+    tab = oracle.decode(e4, np.arange(256))
+    fin = np.isfinite(tab)
+    b = np.zeros((256, 128), np.uint8)
+    b[:, 0] = np.where(fin, np.arange(256), 0)
+    a = np.zeros((16, 128), np.uint8)
+    a[0, 0] = one_b
+    out = _out((16, 256), True)
+    one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy()[0].astype(np.float64)[fin], tab[fin])
+
+
+def test_small_integer_products_are_exact(f):
+    """Small-integer operands with unit scales: the fp32 result is exact."""
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(1)
+    M, N, K = 96, 80, 512
+    av = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    bv = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    a, b = oracle.encode(e4, av), oracle.encode(e4, bv)
+    out = _out((M, N), True)
+    one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), av.astype(np.float64) @ bv.T.astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 512), (1, 16, 16), (100, 72, 48), (300, 200, 384), (513, 260, 1040)])
+@pytest.mark.parametrize("scaling", ["tensor", "row"])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_scaled_mm(f, M, N, K, scaling, out_f32):
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(M * 7 + N)
+    a, b = _codes(e4, (M, K), rng), _codes(e4, (N, K), rng)
+    if scaling == "tensor":
+        sa, sb, sk = np.float32([0.37]), np.float32([2.5]), f.SCALE_TENSOR
+    else:
+        sa = rng.uniform(0.01, 3, M).astype(np.float32)
+        sb = rng.uniform(0.01, 3, N).astype(np.float32)
+        sk = f.SCALE_ROW
+    out = _out((M, N), out_f32)
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, sk, to_dev(sa), to_dev(sb),
+                    f.OUT_F32 if out_f32 else f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    osk = oracle.SCALE_TENSOR if scaling == "tensor" else oracle.SCALE_ROW
+    ref = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb)
+    S = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb, absolute=True)
+    check_gemm(_host(out), ref, S, not out_f32, f"scaled_mm {M}x{N}x{K} {scaling}")
+
+
+def test_scaled_mm_e5m2_a(f):
+    """Grad-input shape: e5m2 A (a gradient) x e4m3 B."""
+    import torch
+    e4, e5 = _names(f)
+    rng = np.random.default_rng(3)
+    M, N, K = 192, 320, 640
+    a, b = _codes(e5, (M, K), rng), _codes(e4, (N, K), rng)
+    # keep magnitudes moderate so fp32 accumulation stays well inside range
+    a = np.where(np.abs(oracle.decode(e5, a)) > 1024, 0, a).astype(np.uint8)
+    sa = rng.uniform(0.5, 2, M).astype(np.float32)
+    sb = rng.uniform(0.5, 2, N).astype(np.float32)
+    out = _out((M, N), False)
+    f.fp8_scaled_mm(to_dev(a), f.E5M2_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_ROW, to_dev(sa), to_dev(sb),
+                    f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    ref = oracle.scaled_mm(a, e5, b, e4, oracle.SCALE_ROW, sa, sb)
+    S = oracle.scaled_mm(a, e5, b, e4, oracle.SCALE_ROW, sa, sb, absolute=True)
+    check_gemm(_host(out), ref, S, True, "e5m2 x e4m3")
+
+
+def test_scale_direction_negative(f):
+    """Passing the quantize multipliers instead of their inverses is off by (s_a s_b)^2."""
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(4)
+    a, b = _codes(e4, (64, 128), rng), _codes(e4, (32, 128), rng)
+    good, bad = _out((64, 32), True), _out((64, 32), True)
+    inv_a, inv_b = torch.tensor([0.125], device="cuda:0"), torch.tensor([4.0], device="cuda:0")
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, inv_a, inv_b, f.OUT_F32, good)
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, 1 / inv_a, 1 / inv_b,
+                    f.OUT_F32, bad)
+    torch.cuda.synchronize()
+    g, w = good.cpu().numpy(), bad.cpu().numpy()
+    nz = g != 0
+    np.testing.assert_allclose(w[nz] / g[nz], (8.0 * 0.25) ** 2, rtol=1e-6)
+
+
+def _offsets(counts):
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    return off
+
+
+@pytest.mark.parametrize("counts,N,K", [([37, 0, 300, 1, 0, 513], 272, 384), ([0, 0, 64], 128, 128),
+                                         ([256], 256, 256), ([5] * 40, 64, 512)])
+def test_grouped_row(f, counts, N, K):
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(sum(counts) + N)
+    off = _offsets(counts)
+    E, Mt = len(counts), int(off[-1])
+    a, b = _codes(e4, (Mt, K), rng), _codes(e4, (E, N, K), rng)
+    sa = rng.uniform(0.1, 2, Mt).astype(np.float32)
+    sb = rng.uniform(0.1, 2, (E, N)).astype(np.float32)
+    out = torch.full((Mt, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_ROW, to_dev(sa), to_dev(sb),
+                     to_dev(off), f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_ROW, sa, sb, off)
+    S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_ROW, sa, sb, off, absolute=True)
+    got = _host(out)
+    assert not np.any(np.isnan(got)), "rows left unwritten"
+    check_gemm(got, ref, S, True, f"grouped row {counts}")
+
+
+@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256)])
+def test_grouped_block(f, counts, N, K):
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(11)
+    off = _offsets(counts)
+    E, Mt = len(counts), int(off[-1])
+    a, b = _codes(e4, (Mt, K), rng), _codes(e4, (E, N, K), rng)
+    sa = rng.uniform(0.01, 4, (Mt, K // 128)).astype(np.float32)
+    sb = rng.uniform(0.01, 4, (E, N // 128, K // 128)).astype(np.float32)
+    out = _out((Mt, N), False)
+    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_BLOCK128, to_dev(sa), to_dev(sb),
+                     to_dev(off), f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off)
+    S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off, absolute=True)
+    check_gemm(_host(out), ref, S, True, f"grouped block {counts}")
+
+
+@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256), ([33], 48, 96)])
+def test_grouped_mx(f, counts, N, K):
+    import torch
+    e4, _ = _names(f)
+    rng = np.random.default_rng(13)
+    off = _offsets(counts)
+    E, Mt = len(counts), int(off[-1])
+    a, b = _codes(e4, (Mt, K), rng), _codes(e4, (E, N, K), rng)
+    sa = rng.integers(117, 137, (Mt, K // 32)).astype(np.uint8)
+    sb = rng.integers(117, 137, (E, N, K // 32)).astype(np.uint8)
+    out = _out((Mt, N), False)
+    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_MX32, to_dev(sa), to_dev(sb),
+                     to_dev(off), f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_MX32, sa, sb, off)
+    S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_MX32, sa, sb, off, absolute=True)
+    check_gemm(_host(out), ref, S, True, f"grouped mx {counts}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 264, 136), (1000, 512, 256), (7, 16, 8)])
+def test_wgrad_bf16(f, M, N, K):
+    import torch
+    g = synth.normal_bf16((M, N), 700 + M, 1e-3)
+    x = synth.normal_bf16((M, K), 701 + M, 1.0)
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_wgrad_bf16(to_dev_bf16(g), to_dev_bf16(x), gw)
+    torch.cuda.synchronize()
+    ref = oracle.wgrad_bf16(g, x)
+    S = oracle.wgrad_bf16(g, x, absolute=True)
+    check_gemm(_host(gw), ref, S, True, f"wgrad {M}x{N}x{K}")

@@ -1,0 +1,89 @@
+"""GPU parity of one Linear layer (forward and backward) against the oracle's
+composition of the same steps: quantize (tensorwise or rowwise e4m3; e5m2 for the
+gradient; per-column e4m3 for the transposed weight), then the fp64 GEMMs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import check_gemm, gpu, have_gpu, lib, to_dev_bf16
+
+pytestmark = [gpu, pytest.mark.skipif(not have_gpu(), reason="needs an MI355X")]
+EPS = 1e-12
+
+
+@pytest.fixture(scope="module")
+def f():
+    oracle.build(force=False)
+    synth.build(force=False)
+    return lib()
+
+
+def _names(f):
+    e4, e5 = f.fp8_probe(0)
+    name = {0: "e4m3fn", 1: "e4m3fnuz", 2: "e5m2", 3: "e5m2fnuz"}
+    return name[e4], name[e5]
+
+
+def _ws(f, M, N, K, recipe):
+    import torch
+    return torch.empty(f.fp8_linear_ws_bytes(M, N, K, recipe), dtype=torch.uint8, device="cuda:0")
+
+
+def test_linear_tensorwise_forward_fp32(f):
+    """256 x 512 input, 512 x 512 weight, one scale each, fp32 out."""
+    import torch
+    e4, _ = _names(f)
+    w = synth.linear_tensorwise()
+    x, wt = w.tensors["x"], w.tensors["w"]
+    M, K, N = x.shape[0], x.shape[1], wt.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    f.fp8_linear_fwd(to_dev_bf16(x), to_dev_bf16(wt), f.RECIPE_TENSORWISE, EPS, f.OUT_F32, y,
+                     _ws(f, M, N, K, f.RECIPE_TENSORWISE))
+    torch.cuda.synchronize()
+    qx, _, ix = oracle.quant_tensor(x, e4, EPS)
+    qw, _, iw = oracle.quant_tensor(wt, e4, EPS)
+    ref = oracle.scaled_mm(qx, e4, qw, e4, oracle.SCALE_TENSOR, ix, iw)
+    S = oracle.scaled_mm(qx, e4, qw, e4, oracle.SCALE_TENSOR, ix, iw, absolute=True)
+    check_gemm(y.cpu().numpy(), ref, S, False, "tensorwise linear fwd (fp32 out)")
+
+
+@pytest.mark.parametrize("recipe", ["rowwise", "tensorwise"])
+def test_linear_small_fwd_bwd(f, recipe):
+    import torch
+    e4, e5 = _names(f)
+    M, K, N = 200, 384, 272
+    x = synth.normal_bf16((M, K), 801, 1.0)
+    synth.add_outliers(x, 802, 0.01, 50.0)
+    wt = synth.normal_bf16((N, K), 803, 0.02)
+    gy = synth.normal_bf16((M, N), 804, 1e-3)
+    rc = f.RECIPE_ROWWISE_BF16_WGRAD if recipe == "rowwise" else f.RECIPE_TENSORWISE
+    ws = _ws(f, M, N, K, rc)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    xd, wd, gd = to_dev_bf16(x), to_dev_bf16(wt), to_dev_bf16(gy)
+    f.fp8_linear_fwd(xd, wd, rc, EPS, f.OUT_BF16, y, ws)
+    f.fp8_linear_bwd(gd, xd, wd, rc, EPS, gx, gw, ws)
+    torch.cuda.synchronize()
+    if recipe == "rowwise":
+        qx, _, ix = oracle.quant_row(x, e4, EPS)
+        qw, _, iw = oracle.quant_row(wt, e4, EPS)
+        qg, _, ig = oracle.quant_row(gy, e5, EPS)
+        qwt, _, iwc = oracle.quant_col(wt, e4, EPS)
+        sk = oracle.SCALE_ROW
+    else:
+        qx, _, ix = oracle.quant_tensor(x, e4, EPS)
+        qw, _, iw = oracle.quant_tensor(wt, e4, EPS)
+        qg, _, ig = oracle.quant_tensor(gy, e5, EPS)
+        qt, _, iwc = oracle.quant_tensor(wt, e4, EPS)
+        qwt = np.ascontiguousarray(qt.T)
+        sk = oracle.SCALE_TENSOR
+    ref_y = oracle.scaled_mm(qx, e4, qw, e4, sk, ix, iw)
+    S_y = oracle.scaled_mm(qx, e4, qw, e4, sk, ix, iw, absolute=True)
+    ref_gx = oracle.scaled_mm(qg, e5, qwt, e4, sk, ig, iwc)
+    S_gx = oracle.scaled_mm(qg, e5, qwt, e4, sk, ig, iwc, absolute=True)
+    ref_gw = oracle.wgrad_bf16(gy, x)
+    S_gw = oracle.wgrad_bf16(gy, x, absolute=True)
+    for name, got, ref, S in (("y", y, ref_y, S_y), ("gx", gx, ref_gx, S_gx), ("gw", gw, ref_gw, S_gw)):
+        check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}")

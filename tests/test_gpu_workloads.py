@@ -1,0 +1,216 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times: every quantized byte and scale against the oracle (bit-exact), GEMM outputs on
+sampled positions the oracle computes one by one (every expert's first and last row,
+the tile corners, plus seeded random positions)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import check_gemm, gpu, have_gpu, lib, to_dev, to_dev_bf16, u8
+
+pytestmark = [gpu, pytest.mark.skipif(not have_gpu(), reason="needs an MI355X")]
+EPS = 1e-12
+
+
+@pytest.fixture(scope="module")
+def f():
+    oracle.build(force=False)
+    synth.build(force=False)
+    return lib()
+
+
+def _names(f):
+    e4, e5 = f.fp8_probe(0)
+    name = {0: "e4m3fn", 1: "e4m3fnuz", 2: "e5m2", 3: "e5m2fnuz"}
+    return name[e4], name[e5]
+
+
+def _samples(M, N, seed, n=2048, offsets=None):
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, n))
+    cols = list(rng.integers(0, N, n))
+    edge_r = [0, M - 1]
+    if offsets is not None:
+        for e in range(len(offsets) - 1):
+            if offsets[e + 1] > offsets[e]:
+                edge_r += [int(offsets[e]), int(offsets[e + 1]) - 1]
+    for r in edge_r:
+        for c in (0, N - 1, N // 2):
+            rows.append(r)
+            cols.append(c)
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+def _gather(t, rows, cols):
+    import torch
+    r = torch.from_numpy(rows).to(t.device)
+    c = torch.from_numpy(cols).to(t.device)
+    return t[r, c].float().cpu().numpy().astype(np.float64)
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def test_linear_rowwise_llama3_8b_mlp(f):
+    """X [8192,4096] (0.1% outliers x50), W [14336,4096], grad_out [8192,14336]."""
+    import torch
+    e4, e5 = _names(f)
+    wl = synth.linear_rowwise()
+    x, wt, gy = wl.tensors["x"], wl.tensors["w"], wl.tensors["gy"]
+    M, K, N = x.shape[0], x.shape[1], wt.shape[0]
+    _log("linear_rowwise generated", wl.meta["outliers"], "outliers")
+    xd, wd, gd = to_dev_bf16(x), to_dev_bf16(wt), to_dev_bf16(gy)
+    # quantization steps, bit-exact, with the same calls the Linear layer makes
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    ix = torch.empty_like(sx)
+    f.fp8_quant_row(xd, f.E4M3_NATIVE, EPS, qx, sx, ix)
+    qw = torch.empty((N, K), dtype=torch.uint8, device="cuda:0")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    iw = torch.empty_like(sw)
+    f.fp8_quant_row(wd, f.E4M3_NATIVE, EPS, qw, sw, iw)
+    qg = torch.empty((M, N), dtype=torch.uint8, device="cuda:0")
+    sg = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    ig = torch.empty_like(sg)
+    f.fp8_quant_row(gd, f.E5M2_NATIVE, EPS, qg, sg, ig)
+    qwt = torch.empty((K, N), dtype=torch.uint8, device="cuda:0")
+    swc = torch.empty(K, dtype=torch.float32, device="cuda:0")
+    iwc = torch.empty_like(swc)
+    ws = torch.empty(max(f.fp8_quant_col_ws_bytes(1, N, K), 4), dtype=torch.uint8, device="cuda:0")
+    f.fp8_quant_col(wd, f.E4M3_NATIVE, EPS, qwt, swc, iwc, ws)
+    torch.cuda.synchronize()
+    r_qx, r_sx, r_ix = oracle.quant_row(x, e4, EPS)
+    assert np.array_equal(u8(qx), r_qx) and np.array_equal(ix.cpu().numpy(), r_ix)
+    r_qw, r_sw, r_iw = oracle.quant_row(wt, e4, EPS)
+    assert np.array_equal(u8(qw), r_qw) and np.array_equal(iw.cpu().numpy(), r_iw)
+    r_qg, r_sg, r_ig = oracle.quant_row(gy, e5, EPS)
+    assert np.array_equal(u8(qg), r_qg) and np.array_equal(ig.cpu().numpy(), r_ig)
+    r_qwt, r_swc, r_iwc = oracle.quant_col(wt, e4, EPS)
+    assert np.array_equal(u8(qwt), r_qwt) and np.array_equal(iwc.cpu().numpy(), r_iwc)
+    _log("linear_rowwise quantization bit-exact")
+
+    rc = f.RECIPE_ROWWISE_BF16_WGRAD
+    lws = torch.empty(f.fp8_linear_ws_bytes(M, N, K, rc), dtype=torch.uint8, device="cuda:0")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_linear_fwd(xd, wd, rc, EPS, f.OUT_BF16, y, lws)
+    f.fp8_linear_bwd(gd, xd, wd, rc, EPS, gx, gw, lws)
+    torch.cuda.synchronize()
+    r, c = _samples(M, N, 1)
+    ref = oracle.scaled_mm_sample(r_qx, e4, r_qw, e4, oracle.SCALE_ROW, r_ix, r_iw, r, c)
+    S = oracle.scaled_mm_sample(r_qx, e4, r_qw, e4, oracle.SCALE_ROW, r_ix, r_iw, r, c, absolute=True)
+    check_gemm(_gather(y, r, c), ref, S, True, "linear_rowwise forward (sampled)")
+    r, c = _samples(M, K, 2)
+    ref = oracle.scaled_mm_sample(r_qg, e5, r_qwt, e4, oracle.SCALE_ROW, r_ig, r_iwc, r, c)
+    S = oracle.scaled_mm_sample(r_qg, e5, r_qwt, e4, oracle.SCALE_ROW, r_ig, r_iwc, r, c, absolute=True)
+    check_gemm(_gather(gx, r, c), ref, S, True, "linear_rowwise grad-input (sampled)")
+    r, c = _samples(N, K, 3)
+    ref = oracle.wgrad_bf16_sample(gy, x, r, c)
+    S = oracle.wgrad_bf16_sample(gy, x, r, c, absolute=True)
+    check_gemm(_gather(gw, r, c), ref, S, True, "linear_rowwise grad-weight bf16 (sampled)")
+
+
+def test_expert_colwise(f):
+    """32 experts x [2048,7168] with 2 zero columns each -> transposed codes + column scales."""
+    import torch
+    e4, _ = _names(f)
+    wl = synth.expert_colwise()
+    w = wl.tensors["w"]
+    E, R, C = w.shape
+    wd = to_dev_bf16(w)
+    qt = torch.empty((E, C, R), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((E, C), dtype=torch.float32, device="cuda:0")
+    i = torch.empty_like(s)
+    f.fp8_quant_col(wd, f.E4M3_NATIVE, EPS, qt, s, i, None)
+    torch.cuda.synchronize()
+    rq, rs, ri = oracle.quant_col(w, e4, EPS)
+    assert np.array_equal(u8(qt), rq)
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+    # the zero columns took the eps clamp
+    zc = wl.meta["zero_cols"]
+    assert np.all(rs[np.arange(E)[:, None], zc] == np.float32(oracle.fp8_max(e4) / EPS))
+
+
+def test_moe_grouped_forward(f):
+    """16384 tokens x top-8 over 32 experts (Zipf 1.1, 2 empty) -> A [131072,7168] rowwise,
+    W [32][2048][7168] per-expert-column scales, bf16 [131072,2048]."""
+    import torch
+    e4, _ = _names(f)
+    wl = synth.moe_grouped()
+    a, w, off = wl.tensors["a"], wl.tensors["w"], wl.meta["offsets"]
+    Mt, K = a.shape
+    E, N, _ = w.shape
+    _log("moe_grouped generated; counts", list(wl.meta["counts"]))
+    ad, wd = to_dev_bf16(a), to_dev_bf16(w)
+    qa = torch.empty((Mt, K), dtype=torch.uint8, device="cuda:0")
+    sa = torch.empty(Mt, dtype=torch.float32, device="cuda:0")
+    ia = torch.empty_like(sa)
+    f.fp8_quant_row(ad, f.E4M3_NATIVE, EPS, qa, sa, ia)
+    qw = torch.empty((E, N, K), dtype=torch.uint8, device="cuda:0")
+    sw = torch.empty((E, N), dtype=torch.float32, device="cuda:0")
+    iw = torch.empty_like(sw)
+    f.fp8_quant_row(wd, f.E4M3_NATIVE, EPS, qw, sw, iw)
+    out = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ia, iw, to_dev(off), f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    del ad, wd
+    r_qa, _, r_ia = oracle.quant_row(a, e4, EPS)
+    assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
+    del a
+    r_qw, _, r_iw = oracle.quant_row(w, e4, EPS)
+    assert np.array_equal(u8(qw), r_qw) and np.array_equal(iw.cpu().numpy(), r_iw)
+    _log("moe_grouped quantization bit-exact")
+    r, c = _samples(Mt, N, 4, offsets=off)
+    ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c)
+    S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c, absolute=True)
+    check_gemm(_gather(out, r, c), ref, S, True, "moe_grouped gemm (sampled)")
+
+
+def test_moe_block_and_mx(f):
+    """16 experts, K 5120, N 8192, 8192 rows (512 per expert), per-row magnitude spread
+    2^-8..2^8: 1x128 / 128x128 blockwise and 32-element MX quantization and GEMMs."""
+    import torch
+    e4, _ = _names(f)
+    wl = synth.moe_block_mx()
+    a, w, off = wl.tensors["a"], wl.tensors["w"], wl.meta["offsets"]
+    Mt, K = a.shape
+    E, N, _ = w.shape
+    ad, wd, offd = to_dev_bf16(a), to_dev_bf16(w), to_dev(off)
+    # blockwise
+    qa = torch.empty((Mt, K), dtype=torch.uint8, device="cuda:0")
+    sa = torch.empty((Mt, K // 128), dtype=torch.float32, device="cuda:0")
+    ia = torch.empty_like(sa)
+    f.fp8_quant_block(ad, 1, 128, f.E4M3_NATIVE, EPS, qa, sa, ia)
+    qw = torch.empty((E, N, K), dtype=torch.uint8, device="cuda:0")
+    sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda:0")
+    iw = torch.empty_like(sw)
+    f.fp8_quant_block(wd, 128, 128, f.E4M3_NATIVE, EPS, qw, sw, iw)
+    out = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_BLOCK128, ia, iw, offd, f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    r_qa, _, r_ia = oracle.quant_block(a, 1, 128, e4, EPS)
+    assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
+    r_qw, _, r_iw = oracle.quant_block(w, 128, 128, e4, EPS)
+    assert np.array_equal(u8(qw), r_qw) and np.array_equal(iw.cpu().numpy(), r_iw)
+    r, c = _samples(Mt, N, 5, offsets=off)
+    ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_BLOCK128, r_ia, r_iw, off, r, c)
+    S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_BLOCK128, r_ia, r_iw, off, r, c, absolute=True)
+    check_gemm(_gather(out, r, c), ref, S, True, "moe blockwise gemm (sampled)")
+    del r_qw
+    # MX
+    ea = torch.empty((Mt, K // 32), dtype=torch.uint8, device="cuda:0")
+    f.fp8_quant_mx(ad, f.E4M3_NATIVE, f.MX_POW2_FLOOR, EPS, qa, ea)
+    ew = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda:0")
+    f.fp8_quant_mx(wd, f.E4M3_NATIVE, f.MX_POW2_FLOOR, EPS, qw, ew)
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_MX32, ea, ew, offd, f.OUT_BF16, out)
+    torch.cuda.synchronize()
+    r_qa, r_ea = oracle.quant_mx(a, e4, oracle.MX_POW2_FLOOR, EPS)
+    assert np.array_equal(u8(qa), r_qa) and np.array_equal(u8(ea), r_ea)
+    r_qw, r_ew = oracle.quant_mx(w, e4, oracle.MX_POW2_FLOOR, EPS)
+    assert np.array_equal(u8(qw), r_qw) and np.array_equal(u8(ew), r_ew)
+    ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_MX32, r_ea, r_ew, off, r, c)
+    S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_MX32, r_ea, r_ew, off, r, c, absolute=True)
+    check_gemm(_gather(out, r, c), ref, S, True, "moe MX gemm (sampled)")

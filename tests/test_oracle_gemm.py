@@ -162,3 +162,35 @@ def test_wgrad_matches_numpy():
     np.testing.assert_allclose(out, gf.T @ xf, rtol=1e-12, atol=1e-12)
     ns, ks = rng.integers(0, N, 20), rng.integers(0, K, 20)
     assert np.array_equal(oracle.wgrad_bf16_sample(g, x, ns, ks), out[ns, ks])
+
+
+def test_absolute_product_sums():
+    """S = sum |a_k b_k| |scales|: equals numpy's |A| @ |B|^T, bounds |ref|, and equals ref
+    when every product is non-negative."""
+    rng = np.random.default_rng(8)
+    M, N, K = 20, 24, 256
+    a, b = _codes("e4m3fn", (M, K), rng), _codes("e4m3fn", (N, K), rng)
+    sa = rng.uniform(0.5, 2, M).astype(np.float32)
+    sb = rng.uniform(0.5, 2, N).astype(np.float32)
+    ref = oracle.scaled_mm(a, "e4m3fn", b, "e4m3fn", oracle.SCALE_ROW, sa, sb)
+    S = oracle.scaled_mm(a, "e4m3fn", b, "e4m3fn", oracle.SCALE_ROW, sa, sb, absolute=True)
+    np.testing.assert_allclose(S, (np.abs(_dec("e4m3fn", a)) @ np.abs(_dec("e4m3fn", b)).T) * sa[:, None] * sb[None, :],
+                               rtol=1e-13)
+    assert np.all(S >= np.abs(ref) * (1 - 1e-15))
+    pa, pb = a & 0x7F, b & 0x7F  # clear the sign bits: all products >= 0
+    np.testing.assert_allclose(oracle.scaled_mm(pa, "e4m3fn", pb, "e4m3fn", oracle.SCALE_ROW, sa, sb, absolute=True),
+                               oracle.scaled_mm(pa, "e4m3fn", pb, "e4m3fn", oracle.SCALE_ROW, sa, sb), rtol=1e-15)
+    off = _offsets([7, 0, 13])
+    ga = _codes("e4m3fn", (20, K), rng)
+    gb = _codes("e4m3fn", (3, N, K), rng)
+    ia = rng.uniform(0.5, 2, 20).astype(np.float32)
+    ib = rng.uniform(0.5, 2, (3, N)).astype(np.float32)
+    G = oracle.grouped_mm(ga, "e4m3fn", gb, "e4m3fn", oracle.SCALE_ROW, ia, ib, off, absolute=True)
+    rows, cols = rng.integers(0, 20, 30), rng.integers(0, N, 30)
+    assert np.array_equal(oracle.grouped_mm_sample(ga, "e4m3fn", gb, "e4m3fn", oracle.SCALE_ROW, ia, ib, off, rows,
+                                                   cols, absolute=True), G[rows, cols])
+    g = (rng.standard_normal((30, 8)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = (rng.standard_normal((30, 6)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    W = oracle.wgrad_bf16(g, x, absolute=True)
+    np.testing.assert_allclose(W, np.abs(oracle.bf16_to_f32(g).astype(np.float64)).T
+                               @ np.abs(oracle.bf16_to_f32(x).astype(np.float64)), rtol=1e-13)
