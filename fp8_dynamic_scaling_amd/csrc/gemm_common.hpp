@@ -1,0 +1,126 @@
+// gemm_common.hpp -- pieces shared by the FP8 GEMM kernels: parameters, the
+// per-expert tile walk over device offsets, bf16 rounding.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace fp8dyn {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxExperts = 1024;
+constexpr int kGroupM = 4;
+constexpr int kNumXcd = 8;
+
+struct GemmParams {
+  const uint8_t* a;
+  const uint8_t* b;
+  const void* sa;
+  const void* sb;
+  const int32_t* offsets;
+  int32_t E;
+  int64_t M, N, K;
+  void* out;
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Tile bookkeeping shared by the workgroup.
+struct TileInfo {
+  int64_t m0, m_end, n0;
+  int32_t e;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void tile_of(int64_t t, const int32_t* s_off, const int64_t* s_pref, int E, int64_t nt,
+                                        TileInfo& ti) {
+  // expert: largest e with s_pref[e] <= t (s_pref[E] = total)
+  int lo = 0, hi = E;  // invariant: s_pref[lo] <= t < s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int64_t u = t - s_pref[e];
+  const int64_t mrows = (int64_t)s_off[e + 1] - s_off[e];
+  const int64_t mt = (mrows + BM - 1) / BM;
+  const int64_t g = u / (kGroupM * nt);
+  const int64_t rem = u % (kGroupM * nt);
+  const int64_t gm = (mt - g * kGroupM) < kGroupM ? (mt - g * kGroupM) : kGroupM;
+  const int64_t ntile = rem / gm, mtile = g * kGroupM + rem % gm;
+  ti.e = e;
+  ti.m0 = s_off[e] + mtile * BM;
+  ti.m_end = s_off[e + 1];
+  ti.n0 = ntile * BN;
+}
+
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Reads offsets[0..E] into LDS and builds the prefix of tiles per expert.
+// Dense problems pass offsets == nullptr: one expert covering rows [0, M).
+// Returns the total number of tiles.
+template <int BM, int NT>
+__device__ __forceinline__ int64_t build_tile_prefix(const GemmParams& p, int64_t nt, int32_t* s_off,
+                                                     int64_t* s_pref) {
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  if (p.offsets) {
+    for (int i = tid; i <= E; i += NT) s_off[i] = p.offsets[i];
+  } else if (tid == 0) {
+    s_off[0] = 0;
+    s_off[1] = (int32_t)p.M;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+      s_pref[e] = acc;
+      const int64_t mrows = (int64_t)s_off[e + 1] - s_off[e];
+      acc += (mrows > 0 ? (mrows + BM - 1) / BM : 0) * nt;
+    }
+    s_pref[E] = acc;
+  }
+  __syncthreads();
+  return s_pref[E];
+}
+
+// XCD-aware split of the tile list: with the grid a multiple of the 8 XCDs,
+// XCD x (workgroups dealt round robin) owns tiles [x*T/8, (x+1)*T/8) and its
+// workgroups walk them in order, so concurrently running workgroups of one
+// XCD share operands in that XCD's L2.
+__device__ __forceinline__ void xcd_range(int64_t total, int64_t& t_begin, int64_t& t_end, int64_t& t_step) {
+  const int64_t G = gridDim.x;
+  const int64_t per_xcd_blocks = G / kNumXcd;
+  const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  if (per_xcd_blocks > 0 && G % kNumXcd == 0) {
+    t_begin = xcd * total / kNumXcd + slot;
+    t_end = (xcd + 1) * total / kNumXcd;
+    t_step = per_xcd_blocks;
+  } else {
+    t_begin = blockIdx.x;
+    t_end = total;
+    t_step = G;
+  }
+}
+
+inline int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return cus;
+}
+
+}  // namespace fp8dyn

@@ -32,63 +32,9 @@
 //    eighth of the tile list.
 //  - Offsets stay on the device: every workgroup reads them into LDS and
 //    builds the per-expert tile prefix itself; empty experts own no tiles.
-#include "common.hpp"
-#include "internal.hpp"
+#include "gemm_common.hpp"
 
 namespace fp8dyn {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kMaxExperts = 1024;
-constexpr int kGroupM = 4;
-constexpr int kNumXcd = 8;
-
-struct GemmParams {
-  const uint8_t* a;
-  const uint8_t* b;
-  const void* sa;
-  const void* sb;
-  const int32_t* offsets;
-  int32_t E;
-  int64_t M, N, K;
-  void* out;
-};
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Tile bookkeeping shared by the workgroup.
-struct TileInfo {
-  int64_t m0, m_end, n0;
-  int32_t e;
-};
-
-template <int BM, int BN>
-__device__ __forceinline__ void tile_of(int64_t t, const int32_t* s_off, const int64_t* s_pref, int E, int64_t nt,
-                                        TileInfo& ti) {
-  // expert: largest e with s_pref[e] <= t (s_pref[E] = total)
-  int lo = 0, hi = E;  // invariant: s_pref[lo] <= t < s_pref[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pref[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int64_t u = t - s_pref[e];
-  const int64_t mrows = (int64_t)s_off[e + 1] - s_off[e];
-  const int64_t mt = (mrows + BM - 1) / BM;
-  const int64_t g = u / (kGroupM * nt);
-  const int64_t rem = u % (kGroupM * nt);
-  const int64_t gm = (mt - g * kGroupM) < kGroupM ? (mt - g * kGroupM) : kGroupM;
-  const int64_t ntile = rem / gm, mtile = g * kGroupM + rem % gm;
-  ti.e = e;
-  ti.m0 = s_off[e] + mtile * BM;
-  ti.m_end = s_off[e + 1];
-  ti.n0 = ntile * BN;
-}
 
 template <int BM, int BN, int WM, int WN, bool AE5, bool BE5, int SK, bool OF32>
 __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
@@ -363,6 +309,7 @@ static hipError_t launch_fmt(const GemmArgs& g) {
 
 hipError_t launch_gemm_fp8(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (gemm_fp8_fast_eligible(g)) return launch_gemm_fp8_fast(g);
   if (g.a_e5) return g.b_e5 ? launch_fmt<true, true>(g) : launch_fmt<true, false>(g);
   return g.b_e5 ? launch_fmt<false, true>(g) : launch_fmt<false, false>(g);
 }

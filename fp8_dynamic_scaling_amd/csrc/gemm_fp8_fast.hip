@@ -1,0 +1,509 @@
+// gemm_fp8_fast.hip -- the main FP8 GEMM kernel for gfx950 (dense and MoE
+// grouped; tensorwise, rowwise, 128-blockwise and MX scales) for K a multiple
+// of 128 and 16-byte aligned operands; other shapes use the generic kernel in
+// gemm_fp8.hip.
+//
+// What it computes is the scaled GEMM of "FP8 Training: Quantization,
+// Autograd, Torchao", section 4 (A row-major, B column-major, multiply by the
+// inverse scales) over the expert row ranges of "FP8 training on AMD GPUs with
+// TorchTitan and TorchAO", section "Scaling FP8 to MoE Architectures".
+//
+// Design:
+//  - 256 x 256 output tile per workgroup, 128-deep K steps, tiles walked
+//    persistently (one workgroup per CU, XCD-aware order; see gemm_common.hpp).
+//  - Operands go from HBM straight into LDS with global_load_lds_dwordx4:
+//    each wave-wide load fills 1 KB of LDS (8 rows of 128 bytes; lane i lands
+//    at base + 16 i, measured on MI355X), so no VGPRs stage the tiles. Each
+//    lane fetches the 16-byte chunk that belongs at its LDS slot under the
+//    row-XOR swizzle, which keeps the fragment reads conflict-free.
+//  - Two LDS buffers: the loads of step k+1 are in flight while step k is
+//    multiplied; one barrier per step.
+//  - Rows past the end of an expert (or of N) load a valid clamped row; their
+//    outputs are never stored. K % 128 == 0 means no K tail.
+//  - Matrix cores: v_mfma_scale_f32_16x16x128_f8f6f4 with the operand layout
+//    described in gemm_fp8.hip. MX: the E8M0 bytes of the tile ride along in
+//    LDS (one dword per row per step) and feed the instruction's scale
+//    operands. Blockwise: each 128-deep product is scaled by
+//    inv_a[m][kb] * inv_b[nb][kb] and accumulated in fp32 registers, so that
+//    variant uses 8 waves with 128 x 64 wave tiles to keep its accumulators
+//    in VGPRs.
+#include "gemm_common.hpp"
+
+namespace fp8dyn {
+
+#define FP8_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
+#define FP8_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int WM, int WN, bool AE5, bool BE5, int SK, bool OF32>
+__global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8_fast(GemmParams p) {
+  constexpr int BM = 256, BN = 256, BK = 128;
+  constexpr int NT = WM * WN * 64, NW = NT / 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MI = TM / 16, NI = TN / 16;
+  constexpr int ALD = BM / 8 / NW, BLD = BN / 8 / NW;
+  constexpr bool MX = SK == kScaleMX, BLK = SK == kScaleBlock;
+  static_assert(!BLK || TN <= 128, "a wave's columns must sit in one 128-column scale block");
+  static_assert(NW >= 4, "scale staging uses four waves");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t la0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t la1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lb0[BN * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lb1[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint32_t ls0[MX ? 2 * BM : (BLK ? BM : 1)];
+  __shared__ __attribute__((aligned(16))) uint32_t ls1[MX ? 2 * BM : (BLK ? BM : 1)];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int64_t s_pref[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int64_t N = p.N, K = p.K;
+  const int64_t nt = (N + BN - 1) / BN;
+  const int64_t nk = K / BK;
+  const int64_t kb32 = K / 32;
+
+  const int64_t total = build_tile_prefix<BM, NT>(p, nt, s_off, s_pref);
+  int64_t t_begin, t_end, t_step;
+  xcd_range(total, t_begin, t_end, t_step);
+
+  for (int64_t t = t_begin; t < t_end; t += t_step) {
+    TileInfo ti;
+    tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+    // the tile is the same for the whole workgroup: keep its fields in SGPRs
+    ti.m0 = uniform64(ti.m0);
+    ti.m_end = uniform64(ti.m_end);
+    ti.n0 = uniform64(ti.n0);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    const int32_t K32 = (int32_t)K;
+    const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);        // valid rows of this tile (>= 1)
+    const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
+    const uint8_t* A = p.a + ti.m0 * K;                           // tile bases (uniform)
+    const uint8_t* B = p.b + ((int64_t)ti.e * N + ti.n0) * K;
+
+    // ---- direct HBM -> LDS loads of one K step ----
+    auto issue = [&](uint8_t* la, uint8_t* lb, uint32_t* ls, int64_t kt) {
+      const uint8_t* Ak = A + kt * BK;
+      const uint8_t* Bk = B + kt * BK;
+#pragma unroll
+      for (int j = 0; j < ALD; ++j) {
+        const int q = wave * ALD + j;
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int32_t rr = r < a_rows ? r : a_rows - 1;  // clamp: rows past the expert load a valid row
+        __builtin_amdgcn_global_load_lds(FP8_GPTR(Ak + (uint32_t)(rr * K32 + 16 * c)), FP8_LPTR(la + q * 1024), 16,
+                                         0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < BLD; ++j) {
+        const int q = wave * BLD + j;
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int32_t rr = r < b_rows ? r : b_rows - 1;
+        __builtin_amdgcn_global_load_lds(FP8_GPTR(Bk + (uint32_t)(rr * K32 + 16 * c)), FP8_LPTR(lb + q * 1024), 16,
+                                         0, 0);
+      }
+      if constexpr (MX) {
+        // one dword (the four E8M0 bytes of this 128-deep step) per row: A rows
+        // by waves 0-3, B rows by waves 0-3 into the second half
+        if (wave < 4) {
+          const int r = 64 * wave + lane;
+          const int32_t ra = r < a_rows ? r : a_rows - 1;
+          const int32_t rb = r < b_rows ? r : b_rows - 1;
+          const uint8_t* sa = reinterpret_cast<const uint8_t*>(p.sa) + ti.m0 * kb32 + 4 * kt;
+          const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.sb) + ((int64_t)ti.e * N + ti.n0) * kb32 + 4 * kt;
+          __builtin_amdgcn_global_load_lds(FP8_GPTR(sa + (uint32_t)(ra * (int32_t)kb32)), FP8_LPTR(ls + 64 * wave), 4,
+                                           0, 0);
+          __builtin_amdgcn_global_load_lds(FP8_GPTR(sb + (uint32_t)(rb * (int32_t)kb32)),
+                                           FP8_LPTR(ls + BM + 64 * wave), 4, 0, 0);
+        }
+      }
+      if constexpr (BLK) {
+        if (wave < 4) {
+          const int r = 64 * wave + lane;
+          const int32_t ra = r < a_rows ? r : a_rows - 1;
+          const float* sa = reinterpret_cast<const float*>(p.sa) + ti.m0 * nk + kt;
+          __builtin_amdgcn_global_load_lds(FP8_GPTR(sa + ra * (int32_t)nk), FP8_LPTR(ls + 64 * wave), 4, 0, 0);
+        }
+      }
+    };
+
+    v4f acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- one K step: all fragments LDS -> VGPRs, then the next step's loads
+    // are issued, then the matrix-core work runs from registers. Issuing the
+    // LDS-bound loads only after this step's LDS reads keeps the compiler from
+    // making those reads wait for the loads in flight. ----
+    auto step = [&](const uint8_t* la, const uint8_t* lb, const uint32_t* ls, int64_t kt, uint8_t* na, uint8_t* nb,
+                    uint32_t* ns, bool more) {
+      v8i af[MI], bf[NI];
+      int saw[MI], sbw[NI];
+      float s4[MI][4];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int r = wn * TN + 16 * j + lr;
+        const uint8_t* base = lb + r * BK;
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * (lk ^ (r & 7)));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * ((lk + 4) ^ (r & 7)));
+        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sbw[j] = MX ? (int)((ls[BM + r] >> (8 * lk)) & 0xffu) : 127;
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm * TM + 16 * i + lr;
+        const uint8_t* base = la + r * BK;
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * (lk ^ (r & 7)));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * ((lk + 4) ^ (r & 7)));
+        af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        saw[i] = MX ? (int)((ls[r] >> (8 * lk)) & 0xffu) : 127;
+        if constexpr (BLK) {
+          const float4 v = *reinterpret_cast<const float4*>(ls + wm * TM + 16 * i + 4 * lk);
+          s4[i][0] = v.x;
+          s4[i][1] = v.y;
+          s4[i][2] = v.z;
+          s4[i][3] = v.w;
+        }
+      }
+      float sbk = 1.0f;
+      if constexpr (BLK) {
+        const int64_t nbt = N / 128;
+        const int64_t nb = (ti.n0 + wn * TN) / 128;
+        sbk = nb < nbt ? reinterpret_cast<const float*>(p.sb)[((int64_t)ti.e * nbt + nb) * nk + kt] : 0.0f;
+      }
+      if (more) issue(na, nb, ns, kt + 1);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          if constexpr (BLK) {
+            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+            const v4f tmp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], z, AE5 ? 1 : 0,
+                                                                             BE5 ? 1 : 0, 0, 127, 0, 127);
+            keep_live(af[i]);
+            keep_live(bf[j]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] += tmp[r] * (s4[i][r] * sbk);
+          } else {
+            // accumulators live in AGPRs here, so the destination cannot overlap
+            // the VGPR sources (checked on the assembly by the test suite)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], AE5 ? 1 : 0,
+                                                                         BE5 ? 1 : 0, 0, saw[i], 0, sbw[j]);
+          }
+        }
+      }
+    };
+
+    issue(la0, lb0, ls0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const bool odd = kt & 1;
+      step(odd ? la1 : la0, odd ? lb1 : lb0, odd ? ls1 : ls0, kt, odd ? la0 : la1, odd ? lb0 : lb1, odd ? ls0 : ls1,
+           kt + 1 < nk);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+
+    // ---- epilogue: scales and store ----
+    const float* SA = reinterpret_cast<const float*>(p.sa);
+    const float* SB = reinterpret_cast<const float*>(p.sb);
+    float st = 1.0f;
+    if constexpr (SK == kScaleTensor) st = SA[0] * SB[0];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t n = ti.n0 + wn * TN + 16 * j + lr;
+      if (n >= N) continue;
+      float sbn = 1.0f;
+      if constexpr (SK == kScaleRow) sbn = SB[(int64_t)ti.e * N + n];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = ti.m0 + wm * TM + 16 * i + 4 * lk + r;
+          if (m >= ti.m_end) continue;
+          float v = acc[i][j][r];
+          if constexpr (SK == kScaleTensor) v *= st;
+          if constexpr (SK == kScaleRow) v = v * SA[m] * sbn;
+          if constexpr (OF32)
+            reinterpret_cast<float*>(p.out)[m * N + n] = v;
+          else
+            reinterpret_cast<uint16_t*>(p.out)[m * N + n] = f32_to_bf16_rne(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for tensorwise and rowwise scales (the dense Linear GEMMs
+// and the rowwise MoE grouped GEMM).
+//
+//  - 256 x 256 output tile, 4 waves of 128 x 128, v_mfma_scale_f32_32x32x64_f8f6f4
+//    (64-deep K per instruction; measured lane layout: lane l feeds row l % 32,
+//    its low 16 bytes are K [16g, 16g + 16) and its high 16 bytes are
+//    K [32 + 16g, 32 + 16g + 16), g = l / 32; so each lane loads 16-byte chunks
+//    g and g + 2 of a 64-byte row and the instruction's K order is memory order).
+//  - LDS holds a ring of 4 stages of 64-deep K (A and B, 32 KB per stage).
+//    The HBM -> LDS loads of stage s + 3 are issued while stage s is
+//    multiplied, so every load has three stages of matrix-core work to land.
+//    The loads are issued from inline assembly with an explicit vmcnt wait
+//    before each barrier: the compiler cannot tell those LDS writes apart from
+//    this stage's LDS reads and would otherwise wait for all of them before
+//    every read, which serialises the pipeline.
+//  - Within a stage the compiler schedules the fragment reads (16 x 16 bytes
+//    per lane) against the 16 MFMAs; rows of 64 bytes are XOR-swizzled in
+//    16-byte chunks by (row / 4) so a wave's reads hit distinct banks.
+constexpr int kPipeStages = 4;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide 16-byte-per-lane load from global (uniform base + per-lane
+// 32-bit offset) into LDS at lds (uniform; lane i lands at lds + 16 i).
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <bool AE5, bool BE5, int SK, bool OF32>
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
+  constexpr int BM = 256, BN = 256, BK = 64, NS = kPipeStages;
+  constexpr int NW = 4, WN = 2;
+  constexpr int TM = 128, TN = 128, MI = TM / 32, NI = TN / 32;
+  constexpr int SA_BYTES = BM * BK, SB_BYTES = BN * BK, STAGE = SA_BYTES + SB_BYTES;
+  constexpr int D = STAGE / 1024 / NW;  // wave-wide loads per wave per stage
+  static_assert(D == 8, "stage split");
+  typedef float v16f __attribute__((ext_vector_type(16)));
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int64_t s_pref[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int64_t N = p.N, K = p.K;
+  const int64_t nt = (N + BN - 1) / BN;
+  const int64_t nk = K / BK;
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int64_t total = build_tile_prefix<BM, 256>(p, nt, s_off, s_pref);
+  int64_t t_begin, t_end, t_step;
+  xcd_range(total, t_begin, t_end, t_step);
+
+  // this lane's part of each wave-wide load: 16 rows of 64 bytes per load
+  const int ld_row = lane >> 2;    // row within the 16
+  const int ld_pch = lane & 3;     // physical 16-byte chunk in the row
+  // the waves split a stage: waves 0-1 load A (16 loads each), waves 2-3 load B
+  const bool loads_a = wave < 2;
+  const int q0 = (wave & 1) * D;   // first 1 KB piece of the operand this wave loads
+
+  for (int64_t t = t_begin; t < t_end; t += t_step) {
+    TileInfo ti;
+    tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+    ti.m0 = uniform64(ti.m0);
+    ti.m_end = uniform64(ti.m_end);
+    ti.n0 = uniform64(ti.n0);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    const int32_t K32 = (int32_t)K;
+    const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);
+    const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
+    const uint8_t* base = loads_a ? p.a + ti.m0 * K : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    const int32_t rows = loads_a ? a_rows : b_rows;
+    uint32_t off[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int r = 16 * (q0 + d) + ld_row;
+      const int c = ld_pch ^ ((r >> 2) & 3);
+      const int32_t rr = r < rows ? r : rows - 1;  // rows past the expert / N load a valid row
+      off[d] = (uint32_t)(rr * K32 + 16 * c);
+    }
+    const uint32_t opnd_lds = loads_a ? 0u : (uint32_t)SA_BYTES;
+
+    auto issue = [&](int64_t s) {
+      const uint32_t slot = lds0 + (uint32_t)((s % NS) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
+      const uint8_t* bk = base + s * BK;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
+    };
+
+    v16f acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto compute = [&](int64_t s) {
+      const uint8_t* la = lds + (s % NS) * STAGE;
+      const uint8_t* lb = la + SA_BYTES;
+      v8i af[MI], bf[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int r = wn * TN + 32 * j + lrow;
+        const uint8_t* row = lb + r * BK;
+        const int sw = (r >> 2) & 3;
+        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (lg ^ sw));
+        const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((lg + 2) ^ sw));
+        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm * TM + 32 * i + lrow;
+        const uint8_t* row = la + r * BK;
+        const int sw = (r >> 2) & 3;
+        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (lg ^ sw));
+        const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((lg + 2) ^ sw));
+        af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], AE5 ? 1 : 0,
+                                                                      BE5 ? 1 : 0, 0, 127, 0, 127);
+    };
+
+    // prologue: stages 0 .. NS-2 in flight, wait for stage 0
+    const int64_t pre = nk < NS - 1 ? nk : NS - 1;
+    for (int64_t s = 0; s < pre; ++s) issue(s);
+    if (pre >= 3) wait_vm_and_barrier<2 * D>();
+    else if (pre == 2) wait_vm_and_barrier<D>();
+    else wait_vm_and_barrier<0>();
+
+    for (int64_t s = 0; s < nk; ++s) {
+      if (s + NS - 1 < nk) issue(s + NS - 1);
+      compute(s);
+      // stage s + 1 must have landed; the loads issued after it may stay in flight
+      const int64_t after = (nk - 1 < s + NS - 1 ? nk - 1 : s + NS - 1) - (s + 1);
+      if (after >= 2) wait_vm_and_barrier<2 * D>();
+      else if (after == 1) wait_vm_and_barrier<D>();
+      else wait_vm_and_barrier<0>();
+    }
+
+    // ---- epilogue: 32 x 32 tile (i, j), register r of lane l holds
+    // row 32 i + 8 (r / 4) + 4 g + r % 4, column 32 j + l % 32. The scales are
+    // gathered first so their loads overlap, then scaled, rounded, stored. ----
+    const float* SA = reinterpret_cast<const float*>(p.sa);
+    const float* SB = reinterpret_cast<const float*>(p.sb);
+    float rs[MI][16], cs[NI];
+    if constexpr (SK == kScaleTensor) {
+      const float st = SA[0] * SB[0];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rs[i][r] = st;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) cs[j] = 1.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int64_t m = ti.m0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          m = m < ti.m_end ? m : ti.m_end - 1;
+          rs[i][r] = SA[m];
+        }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        int64_t n = ti.n0 + wn * TN + 32 * j + lrow;
+        n = n < N ? n : N - 1;
+        cs[j] = SB[(int64_t)ti.e * N + n];
+      }
+    }
+    // all scale loads have landed before the first store (stores share vmcnt)
+    __builtin_amdgcn_s_waitcnt(0);
+    // stores relative to the tile's corner: 32-bit offsets (256 rows * N < 2^31)
+    int32_t N32 = (int32_t)N;
+    // opaque per tile: keeps the compiler from hoisting every store address
+    // out of the tile loop (256 precomputed addresses would spill)
+    asm volatile("" : "+s"(N32));
+    const int32_t m_lim = (int32_t)(ti.m_end - ti.m0);
+    const int32_t n_lim = (int32_t)(N - ti.n0);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int32_t nl = wn * TN + 32 * j + lrow;
+      if (nl >= n_lim) continue;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t ml = wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (ml >= m_lim) continue;
+          const float v = acc[i][j][r] * rs[i][r] * cs[j];
+          const uint32_t o = (uint32_t)(ml * N32 + nl);
+          if constexpr (OF32)
+            (reinterpret_cast<float*>(p.out) + (ti.m0 * N + ti.n0))[o] = v;
+          else
+            (reinterpret_cast<uint16_t*>(p.out) + (ti.m0 * N + ti.n0))[o] = f32_to_bf16_rne(v);
+        }
+      }
+    }
+  }
+}
+
+template <bool AE5, bool BE5, int SK, bool OF32>
+static hipError_t launch_fast_cfg(const GemmArgs& g) {
+  GemmParams p{g.a, g.b, g.sa, g.sb, g.offsets, g.E, g.M, g.N, g.K, g.out};
+  constexpr int BM = 256, BN = 256;
+  const int64_t nt = (g.N + BN - 1) / BN;
+  const int64_t tiles_ub = g.offsets ? ((g.M + BM - 1) / BM + g.E) * nt : ((g.M + BM - 1) / BM) * nt;
+  int64_t grid = device_cus();
+  if (tiles_ub < grid) grid = tiles_ub;
+  if (grid >= kNumXcd) grid -= grid % kNumXcd;
+  if (grid < 1) grid = 1;
+  if constexpr (SK == kScaleBlock) {
+    hipLaunchKernelGGL((k_gemm_fp8_fast<2, 4, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+  } else if constexpr (SK == kScaleTensor || SK == kScaleRow) {
+    hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
+  } else {
+    hipLaunchKernelGGL((k_gemm_fp8_fast<2, 2, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <bool AE5, bool BE5>
+static hipError_t launch_fast_fmt(const GemmArgs& g) {
+  switch (g.scale_kind) {
+    case kScaleTensor:
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleTensor, true>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleTensor, false>(g);
+    case kScaleRow:
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleRow, true>(g) : launch_fast_cfg<AE5, BE5, kScaleRow, false>(g);
+    case kScaleBlock:
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleBlock, true>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleBlock, false>(g);
+    default:
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleMX, true>(g) : launch_fast_cfg<AE5, BE5, kScaleMX, false>(g);
+  }
+}
+
+bool gemm_fp8_fast_eligible(const GemmArgs& g) {
+  const auto al = [](const void* q, uintptr_t a) { return ((uintptr_t)q % a) == 0; };
+  if (g.N > (1 << 22)) return false;  // 32-bit in-tile output offsets
+  if (g.K % 128 != 0 || g.K == 0) return false;
+  if (g.K > (1 << 23)) return false;  // 32-bit in-tile offsets: 256 rows * K < 2^31
+  if (!al(g.a, 16) || !al(g.b, 16)) return false;
+  if (g.scale_kind == kScaleMX && (!al(g.sa, 4) || !al(g.sb, 4))) return false;
+  return true;
+}
+
+hipError_t launch_gemm_fp8_fast(const GemmArgs& g) {
+  if (g.a_e5) return g.b_e5 ? launch_fast_fmt<true, true>(g) : launch_fast_fmt<true, false>(g);
+  return g.b_e5 ? launch_fast_fmt<false, true>(g) : launch_fast_fmt<false, false>(g);
+}
+
+}  // namespace fp8dyn

@@ -53,6 +53,9 @@ struct GemmArgs {
   hipStream_t stream;
 };
 hipError_t launch_gemm_fp8(const GemmArgs& g);
+// the direct-to-LDS kernel (K % 128 == 0, aligned operands); launch_gemm_fp8 picks it
+bool gemm_fp8_fast_eligible(const GemmArgs& g);
+hipError_t launch_gemm_fp8_fast(const GemmArgs& g);
 
 struct WgradArgs {
   const uint16_t* gy;  // [M][N]

@@ -93,7 +93,7 @@ def test_checker_flags_an_overlap():
     assert not mfma_overlaps("v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]")
 
 
-@pytest.mark.parametrize("src", ["gemm_fp8.hip", "gemm_bf16.hip", "probe.hip"])
+@pytest.mark.parametrize("src", ["gemm_fp8.hip", "gemm_fp8_fast.hip", "gemm_bf16.hip", "probe.hip"])
 def test_no_mfma_destination_overlaps_its_sources(src, tmp_path):
     path = os.path.join(hb.HERE, "csrc", src)
     out = tmp_path / (src + ".s")
