@@ -164,6 +164,55 @@ def build_step(f, torch, dev, wls, dev_of):
     return st
 
 
+# Source files whose kernels each kind of bench row runs: a stored HBM-traffic
+# figure is used only while these files are byte-identical to the ones profiled.
+KERNEL_SOURCES = {
+    "quant": ["quant.hip", "common.hpp"],
+    "gemm8": ["gemm_fp8_fast.hip", "gemm_fp8.hip", "gemm_common.hpp", "common.hpp"],
+    "gemm16": ["gemm_bf16.hip", "gemm_common.hpp", "common.hpp"],
+}
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def sources_digest(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES.get(kind, []):
+        with open(os.path.join(ROOT, "fp8_dynamic_scaling_amd", "csrc", fn), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name, kind):
+    """HBM bytes per launch of bench row `name` from the committed counter table
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy calibration), or None
+    when there is no entry or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    digest = sources_digest(kind)
+    with open(TRAFFIC_TABLE) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 4 and cells[0] == name and cells[1] == digest:
+                try:
+                    return int(cells[-1])
+                except ValueError:
+                    return None
+    return None
+
+
+def calibration_copy(torch, dev, nbytes):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes), run
+    outside the timed region so that counter runs can scale FETCH_SIZE and
+    WRITE_SIZE to bytes."""
+    src = torch.full((nbytes,), 7, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(wls, budget_s=20.0):
     """The oracle as it stands, on a bounded sample of the moe_grouped workload:
     rowwise quantization of the activation rows, then fp64 grouped-GEMM outputs
@@ -220,6 +269,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--only", default="", help="comma-separated workload names (profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -237,6 +288,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     e4, e5 = f.fp8_probe(0)
+    if args.calib_copy_mib > 0:
+        calibration_copy(torch, dev, args.calib_copy_mib << 20)
     t0 = time.perf_counter()
     names = ["linear_tensorwise", "linear_rowwise", "expert_colwise", "moe_grouped", "moe_block_mx"]
     if args.only:
@@ -309,15 +362,18 @@ def main():
         out["gemm_frac_mfma"] = g["frac_mfma"]
     if dom is not None:
         name, kind, avg, work = dom
+        traffic = stored_traffic(name, kind)
         if kind == "quant":
             out["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(work / avg / 1e9, 1),
                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": round(work / avg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+                               "frac": round(work / avg / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic}
         else:
             peak = FP8_PEAK_TFLOPS if kind == "gemm8" else BF16_PEAK_TFLOPS
             out["roofline"] = {"kernel": name, "bound": "mfma", "achieved": round(work / avg / 1e12, 1),
                                "peak": peak, "unit": "TFLOP/s", "frac": round(work / avg / 1e12 / peak, 4),
-                               "traffic": None}
+                               "traffic": traffic}
+        out["roofline"]["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        out["roofline"]["sources"] = sources_digest(kind)
     out["rows"] = rows
     if not args.no_cpu_baseline and "moe_grouped" in wls:
         log("cpu baseline ...")

@@ -275,19 +275,29 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <bool AE5, bool BE5, int SK, bool OF32>
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Fragments of one 64-deep stage for one wave: 4 row blocks of A, 4 of B.
+struct PipeFrags {
+  v8i a[4], b[4];
+};
+
+template <bool AE5, bool BE5, int SK, bool OF32, bool GR>
 __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 64, NS = kPipeStages;
   constexpr int NW = 4, WN = 2;
   constexpr int TM = 128, TN = 128, MI = TM / 32, NI = TN / 32;
   constexpr int SA_BYTES = BM * BK, SB_BYTES = BN * BK, STAGE = SA_BYTES + SB_BYTES;
   constexpr int D = STAGE / 1024 / NW;  // wave-wide loads per wave per stage
-  static_assert(D == 8, "stage split");
+  static_assert(D == 8 && MI == 4 && NI == 4, "stage split");
   typedef float v16f __attribute__((ext_vector_type(16)));
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int64_t s_pref[kMaxExperts + 1];
+  __shared__ int32_t s_off[GR ? kMaxExperts + 1 : 2];
+  __shared__ int64_t s_pref[GR ? kMaxExperts + 1 : 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -299,20 +309,53 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
   const int64_t nk = K / BK;
   const uint32_t lds0 = lds_addr(lds);
 
-  const int64_t total = build_tile_prefix<BM, 256>(p, nt, s_off, s_pref);
+  int64_t total;
+  if constexpr (GR) {
+    total = build_tile_prefix<BM, 256>(p, nt, s_off, s_pref);
+  } else {
+    total = ((p.M + BM - 1) / BM) * nt;
+  }
   int64_t t_begin, t_end, t_step;
   xcd_range(total, t_begin, t_end, t_step);
 
   // this lane's part of each wave-wide load: 16 rows of 64 bytes per load
   const int ld_row = lane >> 2;    // row within the 16
   const int ld_pch = lane & 3;     // physical 16-byte chunk in the row
-  // the waves split a stage: waves 0-1 load A (16 loads each), waves 2-3 load B
+  // the waves split a stage: waves 0-1 load A (8 loads each), waves 2-3 load B
   const bool loads_a = wave < 2;
   const int q0 = (wave & 1) * D;   // first 1 KB piece of the operand this wave loads
 
+  // fragment read offsets within a stage (constant over the whole kernel):
+  // lane l reads row r = 32 i + l % 32 of its wave's block, 16-byte chunks
+  // g and g + 2 (g = l / 32), each XOR-swizzled by (r / 4) % 4
+  uint32_t fa_lo[MI], fa_hi[MI], fb_lo[NI], fb_hi[NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * TM + 32 * i + lrow, sw = (r >> 2) & 3;
+    fa_lo[i] = (uint32_t)(r * BK + 16 * (lg ^ sw));
+    fa_hi[i] = (uint32_t)(r * BK + 16 * ((lg + 2) ^ sw));
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int r = wn * TN + 32 * j + lrow, sw = (r >> 2) & 3;
+    fb_lo[j] = (uint32_t)(SA_BYTES + r * BK + 16 * (lg ^ sw));
+    fb_hi[j] = (uint32_t)(SA_BYTES + r * BK + 16 * ((lg + 2) ^ sw));
+  }
+
   for (int64_t t = t_begin; t < t_end; t += t_step) {
     TileInfo ti;
-    tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+    if constexpr (GR) {
+      tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+    } else {
+      // grouped-M order over the dense tile grid (same walk as one expert)
+      const int64_t mt = (p.M + BM - 1) / BM;
+      const int64_t g = t / (kGroupM * nt), rem = t % (kGroupM * nt);
+      const int64_t gm = (mt - g * kGroupM) < kGroupM ? (mt - g * kGroupM) : kGroupM;
+      ti.e = 0;
+      ti.m0 = (g * kGroupM + rem % gm) * BM;
+      ti.m_end = p.M;
+      ti.n0 = (rem / gm) * BN;
+    }
     ti.m0 = uniform64(ti.m0);
     ti.m_end = uniform64(ti.m_end);
     ti.n0 = uniform64(ti.n0);
@@ -338,6 +381,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
 #pragma unroll
       for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
     };
+    auto read = [&](int64_t s, PipeFrags& f) {
+      const uint8_t* st = lds + (s % NS) * STAGE;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + fa_lo[i]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + fa_hi[i]);
+        f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + fb_lo[j]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + fb_hi[j]);
+        f.b[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    };
 
     v16f acc[MI][NI];
 #pragma unroll
@@ -347,76 +405,79 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto compute = [&](int64_t s) {
-      const uint8_t* la = lds + (s % NS) * STAGE;
-      const uint8_t* lb = la + SA_BYTES;
-      v8i af[MI], bf[NI];
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r = wn * TN + 32 * j + lrow;
-        const uint8_t* row = lb + r * BK;
-        const int sw = (r >> 2) & 3;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (lg ^ sw));
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((lg + 2) ^ sw));
-        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = wm * TM + 32 * i + lrow;
-        const uint8_t* row = la + r * BK;
-        const int sw = (r >> 2) & 3;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * (lg ^ sw));
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((lg + 2) ^ sw));
-        af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    auto mma = [&](const PipeFrags& f) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], AE5 ? 1 : 0,
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AE5 ? 1 : 0,
                                                                       BE5 ? 1 : 0, 0, 127, 0, 127);
     };
 
-    // prologue: stages 0 .. NS-2 in flight, wait for stage 0
-    const int64_t pre = nk < NS - 1 ? nk : NS - 1;
-    for (int64_t s = 0; s < pre; ++s) issue(s);
-    if (pre >= 3) wait_vm_and_barrier<2 * D>();
-    else if (pre == 2) wait_vm_and_barrier<D>();
-    else wait_vm_and_barrier<0>();
+    // One step s: stage s is in registers (cur). Wait until stage s + 1 has
+    // landed (W = stages allowed to stay in flight behind it) and every wave
+    // has finished reading stage s, whose slot is then free; refill that slot
+    // with stage s + 4 (steady state only), read stage s + 1 into nxt while the
+    // matrix cores work on cur. K % 128 == 0 makes nk even, so the steady
+    // state runs in pairs and a tail of 4 (or 2) steps closes the tile.
+    // the 16 fragment reads of the next stage alternate with the 16 MFMAs of
+    // this one, so the reads are in flight while the matrix cores are busy
+    auto read_mma = [&](int64_t s_next, PipeFrags& nxt, const PipeFrags& cur) {
+      read(s_next, nxt);
+      mma(cur);
+#pragma unroll
+      for (int k = 0; k < 2 * (MI + NI); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+    };
+    auto steady = [&](int64_t s, PipeFrags& cur, PipeFrags& nxt) {
+      wait_vm_lgkm_and_barrier<2 * D>();
+      issue(s + NS);
+      read_mma(s + 1, nxt, cur);
+    };
 
-    for (int64_t s = 0; s < nk; ++s) {
-      if (s + NS - 1 < nk) issue(s + NS - 1);
-      compute(s);
-      // stage s + 1 must have landed; the loads issued after it may stay in flight
-      const int64_t after = (nk - 1 < s + NS - 1 ? nk - 1 : s + NS - 1) - (s + 1);
-      if (after >= 2) wait_vm_and_barrier<2 * D>();
-      else if (after == 1) wait_vm_and_barrier<D>();
-      else wait_vm_and_barrier<0>();
+    // prologue: stages 0 .. min(nk, 4) - 1 in flight, stage 0 read into f0
+    PipeFrags f0, f1;
+    if (nk >= NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) issue(s);
+      wait_vm_and_barrier<(NS - 1) * D>();
+    } else {  // nk == 2
+      issue(0);
+      issue(1);
+      wait_vm_and_barrier<D>();
     }
+    read(0, f0);
+
+    for (int64_t s = 0; s + NS < nk; s += 2) {
+      steady(s, f0, f1);
+      steady(s + 1, f1, f0);
+    }
+    if (nk >= NS) {
+      wait_vm_lgkm_and_barrier<2 * D>();
+      read_mma(nk - 3, f1, f0);
+      wait_vm_lgkm_and_barrier<D>();
+      read_mma(nk - 2, f0, f1);
+    }
+    wait_vm_lgkm_and_barrier<0>();
+    read_mma(nk - 1, f1, f0);
+    wait_vm_lgkm_and_barrier<0>();
+    mma(f1);
 
     // ---- epilogue: 32 x 32 tile (i, j), register r of lane l holds
-    // row 32 i + 8 (r / 4) + 4 g + r % 4, column 32 j + l % 32. The scales are
-    // gathered first so their loads overlap, then scaled, rounded, stored. ----
+    // row 32 i + 8 (r / 4) + 4 g + r % 4, column 32 j + l % 32. Per row block
+    // i the 16 row scales are gathered first so their loads overlap, then the
+    // products are scaled, rounded and stored. ----
     const float* SA = reinterpret_cast<const float*>(p.sa);
     const float* SB = reinterpret_cast<const float*>(p.sb);
-    float rs[MI][16], cs[NI];
+    float cs[NI];
+    float st = 1.0f;
     if constexpr (SK == kScaleTensor) {
-      const float st = SA[0] * SB[0];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rs[i][r] = st;
+      st = SA[0] * SB[0];
 #pragma unroll
       for (int j = 0; j < NI; ++j) cs[j] = 1.0f;
     } else {
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int64_t m = ti.m0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          m = m < ti.m_end ? m : ti.m_end - 1;
-          rs[i][r] = SA[m];
-        }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         int64_t n = ti.n0 + wn * TN + 32 * j + lrow;
@@ -424,8 +485,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
         cs[j] = SB[(int64_t)ti.e * N + n];
       }
     }
-    // all scale loads have landed before the first store (stores share vmcnt)
-    __builtin_amdgcn_s_waitcnt(0);
     // stores relative to the tile's corner: 32-bit offsets (256 rows * N < 2^31)
     int32_t N32 = (int32_t)N;
     // opaque per tile: keeps the compiler from hoisting every store address
@@ -433,17 +492,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
     asm volatile("" : "+s"(N32));
     const int32_t m_lim = (int32_t)(ti.m_end - ti.m0);
     const int32_t n_lim = (int32_t)(N - ti.n0);
+    // this lane's first row and column in the tile, also opaque per tile
+    int32_t ml0 = wm * TM + 4 * lg, nl0 = wn * TN + lrow;
+    asm volatile("" : "+v"(ml0), "+v"(nl0));
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int32_t nl = wn * TN + 32 * j + lrow;
-      if (nl >= n_lim) continue;
+    for (int i = 0; i < MI; ++i) {
+      float rs[16];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (SK == kScaleTensor) {
+          rs[r] = st;
+        } else {
+          int64_t m = ti.m0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          m = m < ti.m_end ? m : ti.m_end - 1;
+          rs[r] = SA[m];
+        }
+      }
+      // the scale loads have landed before the first store (stores share vmcnt)
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int32_t nl = nl0 + 32 * j;
+        if (nl >= n_lim) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int32_t ml = wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          const int32_t ml = ml0 + 32 * i + 8 * (r >> 2) + (r & 3);
           if (ml >= m_lim) continue;
-          const float v = acc[i][j][r] * rs[i][r] * cs[j];
+          const float v = acc[i][j][r] * rs[r] * cs[j];
           const uint32_t o = (uint32_t)(ml * N32 + nl);
           if constexpr (OF32)
             (reinterpret_cast<float*>(p.out) + (ti.m0 * N + ti.n0))[o] = v;
@@ -468,7 +543,10 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
   if constexpr (SK == kScaleBlock) {
     hipLaunchKernelGGL((k_gemm_fp8_fast<2, 4, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
   } else if constexpr (SK == kScaleTensor || SK == kScaleRow) {
-    hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
+    if (g.offsets)
+      hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32, true>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
+    else
+      hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32, false>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
   } else {
     hipLaunchKernelGGL((k_gemm_fp8_fast<2, 2, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
   }
