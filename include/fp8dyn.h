@@ -140,7 +140,7 @@ FP8DYN_API fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t ro
 /* Column groups with the transposed output the GEMM's column-major operand
  * needs [P-TAO section 4; P-AMD Level 1 and Level 2]: x [batch][rows][cols] ->
  * qT [batch][cols][rows], scale/inv [batch][cols]. Single pass when
- * rows <= 4096; otherwise a column-amax pass with relaxed atomics and a cast
+ * rows <= 2048; otherwise a column-amax pass with relaxed atomics and a cast
  * pass, which need ws of fp8_quant_col_ws_bytes(batch, rows, cols) bytes. */
 FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                     fp8_format fmt, double eps, uint8_t* qT, float* scale,
