@@ -161,4 +161,14 @@ __device__ __forceinline__ void atomic_max_relaxed(uint32_t* p, float v) {
   __hip_atomic_fetch_max(p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compute units of the current device (host side; 256 on MI355X).
+inline int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return cus;
+}
+
 }  // namespace fp8dyn

@@ -114,13 +114,4 @@ __device__ __forceinline__ void xcd_range(int64_t total, int64_t& t_begin, int64
   }
 }
 
-inline int device_cus() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
-  return cus;
-}
-
 }  // namespace fp8dyn

@@ -80,34 +80,40 @@ __global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Column groups with transposed output qT[b][c][r]. A workgroup owns a strip
-// of 64 columns and up to 2048 rows (128 row-groups x 16 rows). Lane layout:
-// l8 = tid % 8 picks 8 adjacent columns (one 16-byte load per row), rg =
-// tid / 8 picks 16 consecutive rows. After the column amax, each thread packs
-// its 16 rows of one column into 16 bytes directly with the packed converts
-// (the pair of fp32 inputs of each convert is chosen to be two consecutive
-// rows of the same column), so the transposed tile is formed in registers and
-// each store instruction writes 8 columns x 128 contiguous bytes: the
-// coalesced transposed store of "FP8 training on AMD GPUs with TorchTitan and
-// TorchAO", Level 2, without the LDS round trip.
+// Column groups with transposed output qT[b][c][r]. A 256-thread workgroup
+// owns a strip of 64 columns over a range of rows. Lane layout: l8 = tid % 8
+// picks 8 adjacent columns (one 16-byte load per row), rg = tid / 8 picks a
+// row group.
 //
-// MODE 0: single pass, the workgroup covers all rows and reduces the amax.
-// MODE 1: cast pass of the split form, column amax read from colmax[].
-// MODE 2: amax pass of the split form: relaxed atomic max into colmax[]
+// Pass 1 streams the strip (rows rg, rg + 32, ...) and reduces the 64 column
+// maxima (wavefront shuffles, then 4 words per column in LDS). Pass 2 reads
+// the strip again, 16 consecutive rows x 8 columns per thread, and packs the
+// 16 rows of each column into 16 bytes with the packed converts (each
+// convert's pair of inputs is two consecutive rows of one column), so every
+// store instruction writes 8 columns x 128 contiguous bytes of qT: the
+// coalesced transposed store of "FP8 training on AMD GPUs with TorchTitan and
+// TorchAO", Level 2, formed in registers instead of an LDS transpose.
+// Pass 2 walks the strip backwards, so the rows pass 1 read last (still in
+// L2) are read first; HBM sees the strip once per pass at most and in the
+// common case the second read is served by L2 / the Infinity Cache.
+//
+// MODE 0: both passes, the workgroup covers all rows of its strip.
+// MODE 1: pass 2 only; column amax from colmax[] (cm_stride 1: per column,
+//         0: one word for the whole tensor).
+// MODE 2: pass 1 only over a row chunk: relaxed atomic max into colmax[]
 //         ("FP8 training on AMD GPUs with TorchTitan and TorchAO", Level 3).
-constexpr int kColRPT = 16;    // rows per thread
-constexpr int kColRows = 2048; // rows per workgroup (1024 threads)
+constexpr int kColRPT = 16;     // rows per thread in pass 2
+constexpr int kColChunk = 1024; // rows per workgroup in the split form
 
 template <bool E5, int MODE>
-__global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                    int64_t strips, int64_t rchunks,
-                                                    uint8_t* __restrict__ qT, float* __restrict__ scale,
-                                                    float* __restrict__ inv, uint32_t* __restrict__ colmax,
-                                                    int64_t cm_stride, double fmax, double eps) {
-  __shared__ float red[16][64];
+__global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                   int64_t strips, int64_t rchunks, int64_t rows_per_blk,
+                                                   uint8_t* __restrict__ qT, float* __restrict__ scale,
+                                                   float* __restrict__ inv, uint32_t* __restrict__ colmax,
+                                                   int64_t cm_stride, double fmax, double eps) {
+  __shared__ float red[4][64];
   __shared__ float s_scale[64];
   const int tid = threadIdx.x;
-  const int nwaves = blockDim.x >> 6;
   const int lane = tid & 63, wave = tid >> 6;
   const int l8 = tid & 7, rg = tid >> 3;
   int64_t blk = blockIdx.x;
@@ -117,35 +123,37 @@ __global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__
   const int64_t b = blk / strips;
   const int64_t c0 = strip * 64 + l8 * 8;
   const bool cok = c0 < C;
-  const int64_t r0 = rc * kColRows + (int64_t)rg * kColRPT;
-  const uint16_t* xb = x + b * R * C;
-
-  uint4 v[kColRPT];
-  float m[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kColRPT; ++j) {
-    const int64_t r = r0 + j;
-    if (cok && r < R) {
-      v[j] = ld_nt16(xb + r * C + c0);
-    } else {
-      v[j] = make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (MODE != 1) {
-      m[0] = fmaxf(m[0], fabsf(bf16_lo(v[j].x)));
-      m[1] = fmaxf(m[1], fabsf(bf16_hi(v[j].x)));
-      m[2] = fmaxf(m[2], fabsf(bf16_lo(v[j].y)));
-      m[3] = fmaxf(m[3], fabsf(bf16_hi(v[j].y)));
-      m[4] = fmaxf(m[4], fabsf(bf16_lo(v[j].z)));
-      m[5] = fmaxf(m[5], fabsf(bf16_hi(v[j].z)));
-      m[6] = fmaxf(m[6], fabsf(bf16_lo(v[j].w)));
-      m[7] = fmaxf(m[7], fabsf(bf16_hi(v[j].w)));
-    }
-  }
+  const int64_t r_beg = rc * rows_per_blk;
+  const int64_t r_end = r_beg + rows_per_blk < R ? r_beg + rows_per_blk : R;
+  const uint16_t* xb = x + b * R * C + c0;
 
   if constexpr (MODE != 1) {
-    // reduce over the 8 row-groups of the wave (lanes with equal l8)
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = 0.0f;
+    if (cok) {
+      for (int64_t base = r_beg; base < r_end; base += 8 * 32) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t r = base + rg + 32 * u;
+          // plain loads: pass 2 reads these lines again
+          v[u] = r < r_end ? *reinterpret_cast<const uint4*>(xb + r * C) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          m[0] = fmaxf(m[0], fabsf(bf16_lo(v[u].x)));
+          m[1] = fmaxf(m[1], fabsf(bf16_hi(v[u].x)));
+          m[2] = fmaxf(m[2], fabsf(bf16_lo(v[u].y)));
+          m[3] = fmaxf(m[3], fabsf(bf16_hi(v[u].y)));
+          m[4] = fmaxf(m[4], fabsf(bf16_lo(v[u].z)));
+          m[5] = fmaxf(m[5], fabsf(bf16_hi(v[u].z)));
+          m[6] = fmaxf(m[6], fabsf(bf16_lo(v[u].w)));
+          m[7] = fmaxf(m[7], fabsf(bf16_hi(v[u].w)));
+        }
+      }
+    }
+    // reduce over the 8 row groups of the wave (lanes with equal l8)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       m[i] = fmaxf(m[i], __shfl_xor(m[i], 8, 64));
@@ -158,8 +166,7 @@ __global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__
     }
     __syncthreads();
     if (tid < 64) {
-      float cm = red[0][tid];
-      for (int w = 1; w < nwaves; ++w) cm = fmaxf(cm, red[w][tid]);
+      const float cm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
       const int64_t c = strip * 64 + tid;
       if constexpr (MODE == 2) {
         if (c < C) atomic_max_relaxed(colmax + b * C + c, cm);
@@ -176,7 +183,6 @@ __global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__
     if constexpr (MODE == 2) return;
   } else {
     if (tid < 64) {
-      // cm_stride 1: one amax per column; 0: one amax for the whole tensor
       const int64_t c = strip * 64 + tid;
       const int64_t si = (b * C + c) * cm_stride;
       const float cm = c < C ? __uint_as_float(colmax[si]) : 0.0f;
@@ -190,28 +196,151 @@ __global__ __launch_bounds__(1024) void k_quant_col(const uint16_t* __restrict__
     }
   }
   __syncthreads();
-  if (!cok || r0 >= R) return;
+  if (!cok) return;
 
   const float fm = (float)fmax;
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sc[i] = s_scale[l8 * 8 + i];
-  uint8_t* qb = qT + (b * C + c0) * R + r0;
+  // Uniform bases of this strip plus 32-bit per-lane byte offsets (one batch
+  // slice is below 2^31 bytes; the launcher checks).
+  const uint8_t* xs = reinterpret_cast<const uint8_t*>(x + b * R * C + strip * 64);
+  uint8_t* qs = qT + (b * C + strip * 64) * R;
+  const uint32_t row_b = (uint32_t)(C * 2);
+  const uint32_t R32 = (uint32_t)R;
+  // 16-row groups of this thread: g = rg, rg + 32, ... (walked backwards)
+  const int64_t ngroups = (r_end - r_beg) / kColRPT;  // rows are a multiple of 16
+  const int64_t last = rg + ((ngroups - 1 - rg) >= 0 ? ((ngroups - 1 - rg) / 32) * 32 : -32);
+  for (int64_t g = last; g >= rg; g -= 32) {
+    const uint32_t r0 = (uint32_t)(r_beg + g * kColRPT);
+    const uint32_t xo = r0 * row_b + (uint32_t)(l8 * 16);
+    // pk[i][d]: column i, rows r0 + 4d .. r0 + 4d + 3 as four fp8 bytes
+    uint32_t pk[8][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ld_nt16(xs + xo + (uint32_t)(8 * h + j) * row_b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = (i < 2) ? v[j].x : (i < 4) ? v[j].y : (i < 6) ? v[j].z : v[j].w;
+          f[j] = clampf(((i & 1) ? bf16_hi(w) : bf16_lo(w)) * sc[i], fm);
+        }
+        pk[i][2 * h] = cvt4<E5>(f[0], f[1], f[2], f[3]);
+        pk[i][2 * h + 1] = cvt4<E5>(f[4], f[5], f[6], f[7]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st_nt16(qs + (uint32_t)(l8 * 8 + i) * R32 + r0, make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
+  }
+}
+
+// Single pass for up to 2048 rows. A workgroup holds a strip of CW columns x
+// all rows in registers: 16 rows x 8 columns = 64 VGPRs per thread; lanes:
+// lc = tid % (CW / 8) picks 8 adjacent columns, rg = tid / (CW / 8) picks 16
+// consecutive rows. It reduces the CW column maxima, then casts and stores
+// from the same registers with the transposed 16-byte packing described above
+// (each store instruction writes CW / 8 columns x 16 * 64 / (CW / 8)
+// contiguous bytes). Several workgroups share a CU, so some load while others
+// cast and store. Consecutive strips go to the same XCD (strips narrower
+// than 64 columns share 128-byte lines of x).
+#ifndef FP8DYN_COL_CW
+#define FP8DYN_COL_CW 64
+#endif
+constexpr int kColCW = FP8DYN_COL_CW;
+
+template <bool E5, int CW>
+__global__ __launch_bounds__(2048 / 16 * (CW / 8)) void k_quant_col_reg(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t strips, uint8_t* __restrict__ qT,
+    float* __restrict__ scale, float* __restrict__ inv, double fmax, double eps) {
+  constexpr int LPR = CW / 8;                 // lanes per row
+  constexpr int MAXW = 2048 / 16 * LPR / 64;  // waves at 2048 rows
+  __shared__ float red[MAXW][CW];
+  __shared__ float s_scale[CW];
+  const int tid = threadIdx.x;
+  const int nwaves = blockDim.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lc = tid % LPR, rg = tid / LPR;
+  int64_t blk = blockIdx.x;
+  const int64_t G = gridDim.x;
+  if (G % 8 == 0) blk = (blk % 8) * (G / 8) + blk / 8;
+  const int64_t strip = blk % strips;
+  const int64_t b = blk / strips;
+  const int64_t c0 = strip * CW + lc * 8;
+  const bool cok = c0 < C;
+  const int64_t r0 = (int64_t)rg * kColRPT;
+  const bool rok = cok && r0 < R;  // R % 16 == 0: a row group is all in or all out
+  const uint8_t* xs = reinterpret_cast<const uint8_t*>(x + b * R * C + strip * CW);
+  const uint32_t row_b = (uint32_t)(C * 2);
+  const uint32_t xo = (uint32_t)r0 * row_b + (uint32_t)(lc * 16);
+
+  uint4 v[kColRPT];
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
+  if (rok) {
+#pragma unroll
+    for (int j = 0; j < kColRPT; ++j) v[j] = ld_nt16(xs + xo + (uint32_t)j * row_b);
+#pragma unroll
+    for (int j = 0; j < kColRPT; ++j) {
+      m[0] = fmaxf(m[0], fabsf(bf16_lo(v[j].x)));
+      m[1] = fmaxf(m[1], fabsf(bf16_hi(v[j].x)));
+      m[2] = fmaxf(m[2], fabsf(bf16_lo(v[j].y)));
+      m[3] = fmaxf(m[3], fabsf(bf16_hi(v[j].y)));
+      m[4] = fmaxf(m[4], fabsf(bf16_lo(v[j].z)));
+      m[5] = fmaxf(m[5], fabsf(bf16_hi(v[j].z)));
+      m[6] = fmaxf(m[6], fabsf(bf16_lo(v[j].w)));
+      m[7] = fmaxf(m[7], fabsf(bf16_hi(v[j].w)));
+    }
+  }
+  // reduce over the row groups of the wave (lanes with equal lc)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // column i of this thread: rows r0 .. r0+15 -> 16 bytes
+#pragma unroll
+    for (int d = LPR; d < 64; d <<= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], d, 64));
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+  }
+  __syncthreads();
+  if (tid < CW) {
+    float cm = red[0][tid];
+    for (int w = 1; w < nwaves; ++w) cm = fmaxf(cm, red[w][tid]);
+    const int64_t c = strip * CW + tid;
+    float s, iv;
+    scale_from_amax(cm, fmax, eps, s, iv);
+    s_scale[tid] = s;
+    if (c < C) {
+      scale[b * C + c] = s;
+      if (inv) inv[b * C + c] = iv;
+    }
+  }
+  __syncthreads();
+  if (!rok) return;
+
+  const float fm = (float)fmax;
+  uint8_t* qs = qT + (b * C + strip * CW) * R;
+  const uint32_t R32 = (uint32_t)R;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sc = s_scale[lc * 8 + i];
     float f[kColRPT];
 #pragma unroll
     for (int j = 0; j < kColRPT; ++j) {
       const uint32_t w = (i < 2) ? v[j].x : (i < 4) ? v[j].y : (i < 6) ? v[j].z : v[j].w;
-      f[j] = clampf(((i & 1) ? bf16_hi(w) : bf16_lo(w)) * sc[i], fm);
+      f[j] = clampf(((i & 1) ? bf16_hi(w) : bf16_lo(w)) * sc, fm);
     }
     uint4 o;
     o.x = cvt4<E5>(f[0], f[1], f[2], f[3]);
     o.y = cvt4<E5>(f[4], f[5], f[6], f[7]);
     o.z = cvt4<E5>(f[8], f[9], f[10], f[11]);
     o.w = cvt4<E5>(f[12], f[13], f[14], f[15]);
-    st_nt16(qb + (int64_t)i * R, o);
+    st_nt16(qs + (uint32_t)(lc * 8 + i) * R32 + (uint32_t)r0, o);
   }
 }
 
@@ -439,8 +568,16 @@ static hipError_t launch_row_t(const QuantArgs& a) {
 
 hipError_t launch_quant_row(const QuantArgs& a) { return a.e5 ? launch_row_t<true>(a) : launch_row_t<false>(a); }
 
+// The fused form (one workgroup per 64-column strip over all rows) when it
+// gives enough workgroups to fill the chip, else the split form over row
+// chunks of kColChunk rows, which needs one amax word per column.
+static bool col_split(int64_t batch, int64_t rows, int64_t cols) {
+  const int64_t strips = (cols + 63) / 64;
+  return rows > 2048 && batch * strips < 1024;
+}
+
 size_t quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
-  if (rows <= kColRows) return 0;
+  if (!col_split(batch, rows, cols)) return 0;
   return (size_t)(batch * cols) * sizeof(uint32_t);
 }
 
@@ -448,29 +585,35 @@ template <bool E5>
 static hipError_t launch_col_t(const QuantArgs& a, uint32_t* colmax) {
   const int64_t B = a.batch, R = a.rows, C = a.cols;
   if (B == 0 || R == 0 || C == 0) return hipSuccess;
-  const bool vec = C % 8 == 0 && R % 16 == 0 && aligned16(a.x) && aligned16(a.q);
+  // 32-bit in-slice offsets: one batch slice of x (2 B/elem) below 2^31 bytes
+  const bool vec = C % 8 == 0 && R % 16 == 0 && aligned16(a.x) && aligned16(a.q) && R * C < ((int64_t)1 << 30);
   if (!vec) {
     hipLaunchKernelGGL((k_quant_col_generic<E5>), dim3((unsigned)(B * C)), dim3(256), 0, a.stream, a.x, R, C, a.q,
                        a.scale, a.inv, a.fmax, a.eps);
     return hipGetLastError();
   }
-  const int64_t strips = (C + 63) / 64;
-  if (R <= kColRows) {
-    // threads: 8 per row-group of 16 rows, rounded up to whole waves
-    int64_t threads = ((R + kColRPT - 1) / kColRPT) * 8;
+  if (R <= 2048) {
+    const int64_t stripsw = (C + kColCW - 1) / kColCW;
+    // kColCW / 8 threads per 16-row group, whole waves
+    int64_t threads = (R / kColRPT) * (kColCW / 8);
     threads = (threads + 63) / 64 * 64;
-    hipLaunchKernelGGL((k_quant_col<E5, 0>), dim3((unsigned)(B * strips)), dim3((unsigned)threads), 0, a.stream,
-                       a.x, R, C, strips, (int64_t)1, a.q, a.scale, a.inv, (uint32_t*)nullptr, (int64_t)1, a.fmax,
-                       a.eps);
+    hipLaunchKernelGGL((k_quant_col_reg<E5, kColCW>), dim3((unsigned)(B * stripsw)), dim3((unsigned)threads), 0,
+                       a.stream, a.x, R, C, stripsw, a.q, a.scale, a.inv, a.fmax, a.eps);
     return hipGetLastError();
   }
-  const int64_t rchunks = (R + kColRows - 1) / kColRows;
+  const int64_t strips = (C + 63) / 64;
+  if (!col_split(B, R, C)) {
+    hipLaunchKernelGGL((k_quant_col<E5, 0>), dim3((unsigned)(B * strips)), dim3(256), 0, a.stream, a.x, R, C,
+                       strips, (int64_t)1, R, a.q, a.scale, a.inv, (uint32_t*)nullptr, (int64_t)1, a.fmax, a.eps);
+    return hipGetLastError();
+  }
+  const int64_t rchunks = (R + kColChunk - 1) / kColChunk;
   const int64_t nwords = B * C;
   hipLaunchKernelGGL(k_clear_words, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, a.stream, colmax, nwords);
-  hipLaunchKernelGGL((k_quant_col<E5, 2>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
-                     strips, rchunks, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
-  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
-                     strips, rchunks, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
+  hipLaunchKernelGGL((k_quant_col<E5, 2>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
+                     strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
+  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
+                     strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
   return hipGetLastError();
 }
 
@@ -486,16 +629,18 @@ static hipError_t launch_tensor_t_t(const QuantArgs& a, uint32_t* amax_word) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   const int64_t strips = (C + 63) / 64;
-  const int64_t rchunks = (R + kColRows - 1) / kColRows;
+  const int64_t rchunks = (R + kColChunk - 1) / kColChunk;
   hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
   hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n, amax_word);
-  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(1024), 0, a.stream, a.x, R, C,
-                     strips, rchunks, a.q, a.scale, a.inv, amax_word, (int64_t)0, a.fmax, a.eps);
+  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
+                     strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, amax_word, (int64_t)0, a.fmax,
+                     a.eps);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws) {
-  if (a.cols % 8 != 0 || a.rows % 16 != 0) return hipErrorInvalidValue;
+  // the cast pass's 32-bit in-slice offsets
+  if (a.cols % 8 != 0 || a.rows % 16 != 0 || a.rows * a.cols >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
   return a.e5 ? launch_tensor_t_t<true>(a, (uint32_t*)ws) : launch_tensor_t_t<false>(a, (uint32_t*)ws);
 }
 

@@ -139,9 +139,11 @@ FP8DYN_API fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t ro
 
 /* Column groups with the transposed output the GEMM's column-major operand
  * needs [P-TAO section 4; P-AMD Level 1 and Level 2]: x [batch][rows][cols] ->
- * qT [batch][cols][rows], scale/inv [batch][cols]. Single pass when
- * rows <= 2048; otherwise a column-amax pass with relaxed atomics and a cast
- * pass, which need ws of fp8_quant_col_ws_bytes(batch, rows, cols) bytes. */
+ * qT [batch][cols][rows], scale/inv [batch][cols]. One launch when rows <=
+ * 2048 or the tensor has at least 1024 strips of 64 columns (batch *
+ * ceil(cols / 64)); otherwise a column-amax launch over row chunks with
+ * relaxed atomics and a cast launch, which need ws of
+ * fp8_quant_col_ws_bytes(batch, rows, cols) bytes (0 when one launch does). */
 FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                     fp8_format fmt, double eps, uint8_t* qT, float* scale,
                                     float* inv_scale, void* ws, size_t ws_bytes, void* stream);
