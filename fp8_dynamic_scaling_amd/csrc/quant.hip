@@ -56,6 +56,44 @@ __global__ __launch_bounds__(256) void k_quant_row(const uint16_t* __restrict__ 
   }
 }
 
+// Row groups, one wavefront per row (4 rows per 256-thread workgroup): the
+// row (up to 512 * J elements) stays in registers, the amax is reduced with
+// wavefront shuffles only (no LDS, no workgroup barrier), so each wave
+// streams independently and keeps J 16-byte loads in flight.
+template <int J, bool E5>
+__global__ __launch_bounds__(256) void k_quant_row_wave(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                        float* __restrict__ inv, double fmax, double eps) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* xr = x + row * cols;
+  uint8_t* qr = q + row * cols;
+  uint4 v[J];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(lane + 64 * j) * 8;
+    if (c < cols) {
+      v[j] = ld_nt16(xr + c);
+      m = amax8(v[j], m);
+    }
+  }
+  m = wave_max(m);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (lane == 0) {
+    scale[row] = s;
+    if (inv) inv[row] = iv;
+  }
+  const float fm = (float)fmax;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(lane + 64 * j) * 8;
+    if (c < cols) st_nt8(qr + c, quant8<E5>(v[j], s, fm));
+  }
+}
+
 // Any row length / alignment: two passes over the row (the second hits cache).
 template <bool E5>
 __global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __restrict__ x, int64_t cols,
@@ -419,40 +457,61 @@ __global__ __launch_bounds__(256) void k_cast_tensor(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // 1 x G groups along the row, G in {128, 32}: G/8 lanes per group, one
-// 16-byte chunk each. MX=true: power-of-two scale, E8M0 byte per group.
-template <bool E5, int G, bool MX>
+// 16-byte chunk each; each lane set handles U groups per iteration so that
+// U loads are in flight before the reductions (U = 4 for tensors small
+// enough that the grid does not fill the chip several times over, else 1).
+// MX=true: power-of-two scale, E8M0 byte per group.
+template <bool E5, int G, bool MX, int U>
 __global__ __launch_bounds__(256) void k_quant_group1d(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
                                                        float* __restrict__ inv, uint8_t* __restrict__ e8m0,
                                                        double fmax, double eps, int mx_mode) {
-  constexpr int LPG = G / 8;  // lanes per group
-  constexpr int GPB = 256 / LPG;  // groups per workgroup per iteration
+  constexpr int LPG = G / 8;      // lanes per group
+  constexpr int GPB = 256 / LPG;  // groups per workgroup per unrolled slot
   const int64_t ngc = (cols + G - 1) / G;
   const int64_t ngroups = rows * ngc;
+  const bool flat = cols % G == 0;  // groups tile the flattened tensor exactly
   const int sub = threadIdx.x % LPG;
   const float fm = (float)fmax;
-  for (int64_t g = (int64_t)blockIdx.x * GPB + threadIdx.x / LPG; g < ngroups; g += (int64_t)gridDim.x * GPB) {
-    const int64_t r = g / ngc, gc = g % ngc;
-    const int64_t c = gc * G + sub * 8;
-    const bool ok = c < cols;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (ok) v = ld_nt16(x + r * cols + c);
-    float m = amax8(v, 0.0f);
+  const int64_t step = (int64_t)gridDim.x * GPB * U;
+  for (int64_t g0 = (int64_t)blockIdx.x * GPB * U + threadIdx.x / LPG; g0 < ngroups; g0 += step) {
+    uint4 v[U];
+    int64_t off[U];
+    bool ok[U];
 #pragma unroll
-    for (int o = 1; o < LPG; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float s, iv;
-    if constexpr (MX) {
-      const int k = mx_exponent(m, fmax, eps, mx_mode);
-      s = exp2i(k);
-      if (sub == 0) e8m0[g] = (uint8_t)(127 - k);
-    } else {
-      scale_from_amax(m, fmax, eps, s, iv);
-      if (sub == 0) {
-        scale[g] = s;
-        if (inv) inv[g] = iv;
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + (int64_t)u * GPB;
+      if (flat) {
+        off[u] = g * G + sub * 8;
+        ok[u] = g < ngroups;
+      } else {
+        const int64_t r = g / ngc, gc = g % ngc;
+        const int64_t c = gc * G + sub * 8;
+        off[u] = r * cols + c;
+        ok[u] = g < ngroups && c < cols;
       }
+      v[u] = ok[u] ? ld_nt16(x + off[u]) : make_uint4(0, 0, 0, 0);
     }
-    if (ok) st_nt8(q + r * cols + c, quant8<E5>(v, s, fm));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + (int64_t)u * GPB;
+      float m = amax8(v[u], 0.0f);
+#pragma unroll
+      for (int o = 1; o < LPG; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float sc, iv;
+      if constexpr (MX) {
+        const int k = mx_exponent(m, fmax, eps, mx_mode);
+        sc = exp2i(k);
+        if (sub == 0 && g < ngroups) e8m0[g] = (uint8_t)(127 - k);
+      } else {
+        scale_from_amax(m, fmax, eps, sc, iv);
+        if (sub == 0 && g < ngroups) {
+          scale[g] = sc;
+          if (inv) inv[g] = iv;
+        }
+      }
+      if (ok[u]) st_nt8(q + off[u], quant8<E5>(v[u], sc, fm));
+    }
   }
 }
 
@@ -550,7 +609,18 @@ static hipError_t launch_row_t(const QuantArgs& a) {
   if (R == 0 || a.cols == 0) return hipSuccess;
   const bool vec = a.cols % 8 == 0 && aligned16(a.x) && aligned16(a.q);
   dim3 grid((unsigned)R), block(256);
-  if (vec && a.cols <= 2048 * 8) {
+  // rows up to 4096 elements: one wavefront per row; longer rows: one
+  // workgroup per row (measured faster on MI355X for 7168 and 14336)
+  if (vec && a.cols <= 512 * 8) {
+    const int64_t J = (a.cols + 511) / 512;
+    dim3 g4((unsigned)((R + 3) / 4));
+    if (J <= 2)
+      hipLaunchKernelGGL((k_quant_row_wave<2, E5>), g4, block, 0, a.stream, a.x, R, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+    else if (J <= 4)
+      hipLaunchKernelGGL((k_quant_row_wave<4, E5>), g4, block, 0, a.stream, a.x, R, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+    else
+      hipLaunchKernelGGL((k_quant_row_wave<8, E5>), g4, block, 0, a.stream, a.x, R, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
+  } else if (vec && a.cols <= 2048 * 8) {
     const int64_t J = (a.cols + 2047) / 2048;
     if (J <= 1)
       hipLaunchKernelGGL((k_quant_row<1, E5>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv, a.fmax, a.eps);
@@ -675,10 +745,15 @@ static hipError_t launch_block_t(const QuantArgs& a, int br, int bc) {
   const int64_t nbr = (R + br - 1) / br, nbc = (C + bc - 1) / bc;
   if (vec && br == 1 && bc == 128) {
     const int64_t ngroups = B * R * nbc;
-    int64_t blocks = (ngroups + 15) / 16;
+    const bool small = ngroups * 128 < ((int64_t)1 << 28);
+    int64_t blocks = (ngroups + 16 * (small ? 4 : 1) - 1) / (16 * (small ? 4 : 1));
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((k_quant_group1d<E5, 128, false>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, B * R, C,
-                       a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
+    if (small)
+      hipLaunchKernelGGL((k_quant_group1d<E5, 128, false, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
+                         B * R, C, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
+    else
+      hipLaunchKernelGGL((k_quant_group1d<E5, 128, false, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
+                         B * R, C, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
   } else if (vec && br == 128 && bc == 128) {
     hipLaunchKernelGGL((k_quant_block128<E5>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x, R, C, nbr,
                        nbc, a.q, a.scale, a.inv, a.fmax, a.eps);
@@ -700,10 +775,15 @@ static hipError_t launch_mx_t(const QuantArgs& a, uint8_t* e8m0, int mode) {
   const bool vec = aligned16(a.x) && aligned16(a.q);  // C % 32 == 0 is checked by the API
   if (vec) {
     const int64_t ngroups = B * R * (C / 32);
-    int64_t blocks = (ngroups + 63) / 64;
+    const bool small = ngroups * 32 < ((int64_t)1 << 28);
+    int64_t blocks = (ngroups + 64 * (small ? 4 : 1) - 1) / (64 * (small ? 4 : 1));
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((k_quant_group1d<E5, 32, true>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, B * R, C,
-                       a.q, (float*)nullptr, (float*)nullptr, e8m0, a.fmax, a.eps, mode);
+    if (small)
+      hipLaunchKernelGGL((k_quant_group1d<E5, 32, true, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
+                         B * R, C, a.q, (float*)nullptr, (float*)nullptr, e8m0, a.fmax, a.eps, mode);
+    else
+      hipLaunchKernelGGL((k_quant_group1d<E5, 32, true, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
+                         B * R, C, a.q, (float*)nullptr, (float*)nullptr, e8m0, a.fmax, a.eps, mode);
   } else {
     const int64_t nbc = C / 32;
     hipLaunchKernelGGL((k_quant_block_generic<E5, true>), dim3((unsigned)(B * R * nbc)), dim3(256), 0, a.stream, a.x,
