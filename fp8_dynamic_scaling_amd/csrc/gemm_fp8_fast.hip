@@ -9,24 +9,19 @@
 // TorchTitan and TorchAO", section "Scaling FP8 to MoE Architectures".
 //
 // Design:
-//  - 256 x 256 output tile per workgroup, 128-deep K steps, tiles walked
-//    persistently (one workgroup per CU, XCD-aware order; see gemm_common.hpp).
-//  - Operands go from HBM straight into LDS with global_load_lds_dwordx4:
-//    each wave-wide load fills 1 KB of LDS (8 rows of 128 bytes; lane i lands
-//    at base + 16 i, measured on MI355X), so no VGPRs stage the tiles. Each
-//    lane fetches the 16-byte chunk that belongs at its LDS slot under the
-//    row-XOR swizzle, which keeps the fragment reads conflict-free.
-//  - Two LDS buffers: the loads of step k+1 are in flight while step k is
-//    multiplied; one barrier per step.
-//  - Rows past the end of an expert (or of N) load a valid clamped row; their
-//    outputs are never stored. K % 128 == 0 means no K tail.
-//  - Matrix cores: v_mfma_scale_f32_16x16x128_f8f6f4 with the operand layout
-//    described in gemm_fp8.hip. MX: the E8M0 bytes of the tile ride along in
-//    LDS (one dword per row per step) and feed the instruction's scale
-//    operands. Blockwise: each 128-deep product is scaled by
-//    inv_a[m][kb] * inv_b[nb][kb] and accumulated in fp32 registers, so that
-//    variant uses 8 waves with 128 x 64 wave tiles to keep its accumulators
-//    in VGPRs.
+//  - Tensorwise, rowwise and MX scales: the pipelined kernel below (the
+//    header comment there has the details).
+//  - 128-blockwise scales: k_gemm_fp8_fast, a two-buffer kernel with
+//    v_mfma_scale_f32_16x16x128_f8f6f4 and 8 waves of 128 x 64: each 128-deep
+//    product is scaled by inv_a[m][kb] * inv_b[nb][kb] and accumulated in fp32
+//    registers, which needs a second accumulator set.
+//  - Both: 256 x 256 output tiles walked persistently (one workgroup per CU,
+//    XCD-aware order; see gemm_common.hpp); operands go from HBM straight into
+//    LDS with global_load_lds_dwordx4 (lane i lands at base + 16 i, measured on
+//    MI355X), each lane fetching the 16-byte chunk that belongs at its slot
+//    under the row-XOR swizzle; rows past the end of an expert (or of N) load
+//    a valid clamped row and their outputs are never stored; K % 128 == 0
+//    means no K tail.
 #include "gemm_common.hpp"
 
 namespace fp8dyn {
@@ -240,24 +235,29 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8_fast(GemmParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel for tensorwise and rowwise scales (the dense Linear GEMMs
-// and the rowwise MoE grouped GEMM).
+// Pipelined kernel for tensorwise, rowwise and MX scales (the dense Linear
+// GEMMs, the rowwise MoE grouped GEMM and the MX grouped GEMM).
 //
 //  - 256 x 256 output tile, 4 waves of 128 x 128, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (64-deep K per instruction; measured lane layout: lane l feeds row l % 32,
 //    its low 16 bytes are K [16g, 16g + 16) and its high 16 bytes are
 //    K [32 + 16g, 32 + 16g + 16), g = l / 32; so each lane loads 16-byte chunks
-//    g and g + 2 of a 64-byte row and the instruction's K order is memory order).
+//    g and g + 2 of a 64-byte row and the instruction's K order is memory order;
+//    the scale operand of lane l covers row l % 32, K block g).
 //  - LDS holds a ring of 4 stages of 64-deep K (A and B, 32 KB per stage).
-//    The HBM -> LDS loads of stage s + 3 are issued while stage s is
-//    multiplied, so every load has three stages of matrix-core work to land.
-//    The loads are issued from inline assembly with an explicit vmcnt wait
-//    before each barrier: the compiler cannot tell those LDS writes apart from
-//    this stage's LDS reads and would otherwise wait for all of them before
-//    every read, which serialises the pipeline.
-//  - Within a stage the compiler schedules the fragment reads (16 x 16 bytes
-//    per lane) against the 16 MFMAs; rows of 64 bytes are XOR-swizzled in
-//    16-byte chunks by (row / 4) so a wave's reads hit distinct banks.
+//    At step s, after the barrier that proves stage s + 1 has landed and
+//    everyone has finished reading stage s, the HBM -> LDS loads of stage
+//    s + 4 go into stage s's slot, so each load has three steps to land.
+//    The loads are issued from inline assembly with explicit vmcnt waits: the
+//    compiler cannot tell those LDS writes apart from the fragment reads and
+//    would otherwise wait for all of them before every read.
+//  - Fragments are double-buffered in registers: the 16 LDS reads of stage
+//    s + 1 alternate with the 16 MFMAs of stage s. Rows of 64 bytes are
+//    XOR-swizzled in 16-byte chunks by (row / 4) so a wave's reads hit
+//    distinct banks.
+//  - MX: the E8M0 bytes of a stage pair (one dword per row) ride in a small
+//    LDS ring of their own, one wave-wide dword load per stage, and each lane
+//    reads its byte straight into the MFMA's scale operand.
 constexpr int kPipeStages = 4;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -280,9 +280,11 @@ __device__ __forceinline__ void wait_vm_lgkm_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Fragments of one 64-deep stage for one wave: 4 row blocks of A, 4 of B.
+// Fragments of one 64-deep stage for one wave: 4 row blocks of A, 4 of B,
+// and (MX) this lane's E8M0 scale byte for each of them.
 struct PipeFrags {
   v8i a[4], b[4];
+  int sa[4], sb[4];
 };
 
 template <bool AE5, bool BE5, int SK, bool OF32, bool GR>
@@ -298,6 +300,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
   __shared__ int32_t s_off[GR ? kMaxExperts + 1 : 2];
   __shared__ int64_t s_pref[GR ? kMaxExperts + 1 : 2];
+  // MX: E8M0 scales of a stage pair (128-deep K: one dword = 4 K blocks per
+  // row), A rows then B rows, in a ring of 4 pairs
+  constexpr bool MXS = SK == kScaleMX;
+  __shared__ __attribute__((aligned(16))) uint32_t s_scl[MXS ? 4 : 1][MXS ? BM + BN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -375,13 +381,58 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
     }
     const uint32_t opnd_lds = loads_a ? 0u : (uint32_t)SA_BYTES;
 
+    // MX scale loads: one wave-wide dword load per stage, chunk c = 2 wave +
+    // (stage parity) of the pair's 8 chunks of 64 rows (0-3: A, 4-7: B); each
+    // lane fetches its row's 4 E8M0 bytes of the pair (rows past the expert /
+    // N fetch a valid row)
+    const int64_t kb32 = K / 32;
+    // per stage parity: the wave's chunk (uniform base, lane offset, LDS offset)
+    const uint8_t* sc_base0 = nullptr;
+    const uint8_t* sc_base1 = nullptr;
+    uint32_t sc_off0 = 0u, sc_off1 = 0u, sc_lds0 = 0u, sc_lds1 = 0u;
+    if constexpr (MXS) {
+      auto chunk = [&](int par, const uint8_t*& bp, uint32_t& o, uint32_t& l) {
+        const int c = 2 * wave + par;
+        const bool ca = c < 4;
+        const int r = 64 * (c & 3) + lane;
+        const int32_t lim = ca ? a_rows : b_rows;
+        const int32_t rr = r < lim ? r : lim - 1;
+        bp = ca ? reinterpret_cast<const uint8_t*>(p.sa) + ti.m0 * kb32
+                : reinterpret_cast<const uint8_t*>(p.sb) + ((int64_t)ti.e * N + ti.n0) * kb32;
+        o = (uint32_t)(rr * (int32_t)kb32);
+        l = (uint32_t)(4 * ((ca ? 0 : BM) + 64 * (c & 3)));
+      };
+      chunk(0, sc_base0, sc_off0, sc_lds0);
+      chunk(1, sc_base1, sc_off1, sc_lds1);
+    }
+    auto scale_dma = [&](int64_t pair, bool odd) {
+      const int64_t pc = pair < nk / 2 ? pair : nk / 2 - 1;  // past the end: a valid address
+      const uint8_t* bp = odd ? sc_base1 : sc_base0;
+      const uint32_t o = (odd ? sc_off1 : sc_off0) + (uint32_t)(4 * pc);
+      const uint32_t l = lds_addr(&s_scl[pair & 3][0]) + (odd ? sc_lds1 : sc_lds0);
+      asm volatile("global_load_lds_dword %0, %1" ::"v"(o), "s"(bp), "{m0}"(l) : "memory");
+    };
+
+    // unit s: the D loads of stage s, then (MX) one scale load of pair s / 2 + 1
     auto issue = [&](int64_t s) {
       const uint32_t slot = lds0 + (uint32_t)((s % NS) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
       const uint8_t* bk = base + s * BK;
 #pragma unroll
       for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
+      if constexpr (MXS) scale_dma(s / 2 + 1, (s & 1) != 0);
     };
+    constexpr int U = D + (MXS ? 1 : 0);  // loads per unit
+    constexpr int X = U - D;              // loads of a unit after its stage's data
     auto read = [&](int64_t s, PipeFrags& f) {
+      if constexpr (MXS) {
+        // this lane's E8M0 byte: K block 2 s + g of its row (byte (s % 2) * 2 + g
+        // of the row's pair dword), read straight into the scale register
+        const uint8_t* sp = reinterpret_cast<const uint8_t*>(&s_scl[(s / 2) & 3][0]) + 2 * (int)(s & 1) + lg;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) f.sa[i] = sp[4 * (wm * TM + 32 * i + lrow)];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) f.sb[j] = sp[4 * (BM + wn * TN + 32 * j + lrow)];
+      }
       const uint8_t* st = lds + (s % NS) * STAGE;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -409,9 +460,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AE5 ? 1 : 0,
-                                                                      BE5 ? 1 : 0, 0, 127, 0, 127);
+        for (int j = 0; j < NI; ++j) {
+          if constexpr (MXS)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AE5 ? 1 : 0,
+                                                                        BE5 ? 1 : 0, 0, f.sa[i], 0, f.sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], AE5 ? 1 : 0,
+                                                                        BE5 ? 1 : 0, 0, 127, 0, 127);
+        }
     };
 
     // One step s: stage s is in registers (cur). Wait until stage s + 1 has
@@ -425,28 +481,41 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
     auto read_mma = [&](int64_t s_next, PipeFrags& nxt, const PipeFrags& cur) {
       read(s_next, nxt);
       mma(cur);
+      if constexpr (MXS) {
+        // 8 scale reads ride along with the first 8 fragment reads
 #pragma unroll
-      for (int k = 0; k < 2 * (MI + NI); ++k) {
+        for (int k = 0; k < MI + NI; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        }
+      }
+#pragma unroll
+      for (int k = MXS ? MI + NI : 0; k < 2 * (MI + NI); ++k) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
     };
     auto steady = [&](int64_t s, PipeFrags& cur, PipeFrags& nxt) {
-      wait_vm_lgkm_and_barrier<2 * D>();
+      wait_vm_lgkm_and_barrier<2 * U + X>();
       issue(s + NS);
       read_mma(s + 1, nxt, cur);
     };
 
-    // prologue: stages 0 .. min(nk, 4) - 1 in flight, stage 0 read into f0
+    // prologue: (MX) the scales of pair 0, then units 0 .. min(nk, 4) - 1 in
+    // flight; stage 0 (and its scales) read into f0
     PipeFrags f0, f1;
+    if constexpr (MXS) {
+      scale_dma(0, false);
+      scale_dma(0, true);
+    }
     if (nk >= NS) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) issue(s);
-      wait_vm_and_barrier<(NS - 1) * D>();
+      wait_vm_and_barrier<(NS - 1) * U + X>();
     } else {  // nk == 2
       issue(0);
       issue(1);
-      wait_vm_and_barrier<D>();
+      wait_vm_and_barrier<U + X>();
     }
     read(0, f0);
 
@@ -455,12 +524,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
       steady(s + 1, f1, f0);
     }
     if (nk >= NS) {
-      wait_vm_lgkm_and_barrier<2 * D>();
+      wait_vm_lgkm_and_barrier<2 * U + X>();
       read_mma(nk - 3, f1, f0);
-      wait_vm_lgkm_and_barrier<D>();
+      wait_vm_lgkm_and_barrier<U + X>();
       read_mma(nk - 2, f0, f1);
     }
-    wait_vm_lgkm_and_barrier<0>();
+    wait_vm_lgkm_and_barrier<X>();
     read_mma(nk - 1, f1, f0);
     wait_vm_lgkm_and_barrier<0>();
     mma(f1);
@@ -473,8 +542,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
     const float* SB = reinterpret_cast<const float*>(p.sb);
     float cs[NI];
     float st = 1.0f;
-    if constexpr (SK == kScaleTensor) {
-      st = SA[0] * SB[0];
+    if constexpr (SK == kScaleTensor || MXS) {
+      if constexpr (!MXS) st = SA[0] * SB[0];
 #pragma unroll
       for (int j = 0; j < NI; ++j) cs[j] = 1.0f;
     } else {
@@ -500,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
       float rs[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (SK == kScaleTensor) {
+        if constexpr (SK == kScaleTensor || MXS) {
           rs[r] = st;
         } else {
           int64_t m = ti.m0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
@@ -542,13 +611,11 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
   if (grid < 1) grid = 1;
   if constexpr (SK == kScaleBlock) {
     hipLaunchKernelGGL((k_gemm_fp8_fast<2, 4, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
-  } else if constexpr (SK == kScaleTensor || SK == kScaleRow) {
+  } else if constexpr (SK == kScaleTensor || SK == kScaleRow || SK == kScaleMX) {
     if (g.offsets)
       hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32, true>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
     else
       hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32, false>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
-  } else {
-    hipLaunchKernelGGL((k_gemm_fp8_fast<2, 2, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
   }
   return hipGetLastError();
 }

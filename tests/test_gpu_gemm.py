@@ -96,7 +96,8 @@ def test_small_integer_products_are_exact(f):
     assert np.array_equal(out.cpu().numpy().astype(np.float64), av.astype(np.float64) @ bv.T.astype(np.float64))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 512, 512), (1, 16, 16), (100, 72, 48), (300, 200, 384), (513, 260, 1040)])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 512), (1, 16, 16), (100, 72, 48), (300, 200, 384), (513, 260, 1040),
+                                   (300, 520, 1152), (64, 64, 128)])
 @pytest.mark.parametrize("scaling", ["tensor", "row"])
 @pytest.mark.parametrize("out_f32", [True, False])
 def test_scaled_mm(f, M, N, K, scaling, out_f32):
@@ -164,7 +165,8 @@ def _offsets(counts):
 
 
 @pytest.mark.parametrize("counts,N,K", [([37, 0, 300, 1, 0, 513], 272, 384), ([0, 0, 64], 128, 128),
-                                         ([256], 256, 256), ([5] * 40, 64, 512)])
+                                         ([256], 256, 256), ([5] * 40, 64, 512), ([300, 5, 0, 129], 320, 640),
+                                         ([17], 64, 128), ([600, 0, 3], 512, 1152)])
 def test_grouped_row(f, counts, N, K):
     import torch
     e4, _ = _names(f)
@@ -204,7 +206,8 @@ def test_grouped_block(f, counts, N, K):
     check_gemm(_host(out), ref, S, True, f"grouped block {counts}")
 
 
-@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256), ([33], 48, 96)])
+@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256), ([33], 48, 96),
+                                         ([300, 5, 0, 129], 320, 640), ([64], 192, 128), ([600, 0, 3], 512, 1152)])
 def test_grouped_mx(f, counts, N, K):
     import torch
     e4, _ = _names(f)
