@@ -26,214 +26,6 @@
 
 namespace fp8dyn {
 
-#define FP8_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
-#define FP8_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-template <int WM, int WN, bool AE5, bool BE5, int SK, bool OF32>
-__global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8_fast(GemmParams p) {
-  constexpr int BM = 256, BN = 256, BK = 128;
-  constexpr int NT = WM * WN * 64, NW = NT / 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MI = TM / 16, NI = TN / 16;
-  constexpr int ALD = BM / 8 / NW, BLD = BN / 8 / NW;
-  constexpr bool MX = SK == kScaleMX, BLK = SK == kScaleBlock;
-  static_assert(!BLK || TN <= 128, "a wave's columns must sit in one 128-column scale block");
-  static_assert(NW >= 4, "scale staging uses four waves");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t la0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) uint8_t la1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) uint8_t lb0[BN * BK];
-  __shared__ __attribute__((aligned(1024))) uint8_t lb1[BN * BK];
-  __shared__ __attribute__((aligned(16))) uint32_t ls0[MX ? 2 * BM : (BLK ? BM : 1)];
-  __shared__ __attribute__((aligned(16))) uint32_t ls1[MX ? 2 * BM : (BLK ? BM : 1)];
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int64_t s_pref[kMaxExperts + 1];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const int lr = lane & 15, lk = lane >> 4;
-  const int64_t N = p.N, K = p.K;
-  const int64_t nt = (N + BN - 1) / BN;
-  const int64_t nk = K / BK;
-  const int64_t kb32 = K / 32;
-
-  const int64_t total = build_tile_prefix<BM, NT>(p, nt, s_off, s_pref);
-  int64_t t_begin, t_end, t_step;
-  xcd_range(total, t_begin, t_end, t_step);
-
-  for (int64_t t = t_begin; t < t_end; t += t_step) {
-    TileInfo ti;
-    tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
-    // the tile is the same for the whole workgroup: keep its fields in SGPRs
-    ti.m0 = uniform64(ti.m0);
-    ti.m_end = uniform64(ti.m_end);
-    ti.n0 = uniform64(ti.n0);
-    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
-    const int32_t K32 = (int32_t)K;
-    const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);        // valid rows of this tile (>= 1)
-    const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
-    const uint8_t* A = p.a + ti.m0 * K;                           // tile bases (uniform)
-    const uint8_t* B = p.b + ((int64_t)ti.e * N + ti.n0) * K;
-
-    // ---- direct HBM -> LDS loads of one K step ----
-    auto issue = [&](uint8_t* la, uint8_t* lb, uint32_t* ls, int64_t kt) {
-      const uint8_t* Ak = A + kt * BK;
-      const uint8_t* Bk = B + kt * BK;
-#pragma unroll
-      for (int j = 0; j < ALD; ++j) {
-        const int q = wave * ALD + j;
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int32_t rr = r < a_rows ? r : a_rows - 1;  // clamp: rows past the expert load a valid row
-        __builtin_amdgcn_global_load_lds(FP8_GPTR(Ak + (uint32_t)(rr * K32 + 16 * c)), FP8_LPTR(la + q * 1024), 16,
-                                         0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < BLD; ++j) {
-        const int q = wave * BLD + j;
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int32_t rr = r < b_rows ? r : b_rows - 1;
-        __builtin_amdgcn_global_load_lds(FP8_GPTR(Bk + (uint32_t)(rr * K32 + 16 * c)), FP8_LPTR(lb + q * 1024), 16,
-                                         0, 0);
-      }
-      if constexpr (MX) {
-        // one dword (the four E8M0 bytes of this 128-deep step) per row: A rows
-        // by waves 0-3, B rows by waves 0-3 into the second half
-        if (wave < 4) {
-          const int r = 64 * wave + lane;
-          const int32_t ra = r < a_rows ? r : a_rows - 1;
-          const int32_t rb = r < b_rows ? r : b_rows - 1;
-          const uint8_t* sa = reinterpret_cast<const uint8_t*>(p.sa) + ti.m0 * kb32 + 4 * kt;
-          const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.sb) + ((int64_t)ti.e * N + ti.n0) * kb32 + 4 * kt;
-          __builtin_amdgcn_global_load_lds(FP8_GPTR(sa + (uint32_t)(ra * (int32_t)kb32)), FP8_LPTR(ls + 64 * wave), 4,
-                                           0, 0);
-          __builtin_amdgcn_global_load_lds(FP8_GPTR(sb + (uint32_t)(rb * (int32_t)kb32)),
-                                           FP8_LPTR(ls + BM + 64 * wave), 4, 0, 0);
-        }
-      }
-      if constexpr (BLK) {
-        if (wave < 4) {
-          const int r = 64 * wave + lane;
-          const int32_t ra = r < a_rows ? r : a_rows - 1;
-          const float* sa = reinterpret_cast<const float*>(p.sa) + ti.m0 * nk + kt;
-          __builtin_amdgcn_global_load_lds(FP8_GPTR(sa + ra * (int32_t)nk), FP8_LPTR(ls + 64 * wave), 4, 0, 0);
-        }
-      }
-    };
-
-    v4f acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-    // ---- one K step: all fragments LDS -> VGPRs, then the next step's loads
-    // are issued, then the matrix-core work runs from registers. Issuing the
-    // LDS-bound loads only after this step's LDS reads keeps the compiler from
-    // making those reads wait for the loads in flight. ----
-    auto step = [&](const uint8_t* la, const uint8_t* lb, const uint32_t* ls, int64_t kt, uint8_t* na, uint8_t* nb,
-                    uint32_t* ns, bool more) {
-      v8i af[MI], bf[NI];
-      int saw[MI], sbw[NI];
-      float s4[MI][4];
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r = wn * TN + 16 * j + lr;
-        const uint8_t* base = lb + r * BK;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * (lk ^ (r & 7)));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * ((lk + 4) ^ (r & 7)));
-        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sbw[j] = MX ? (int)((ls[BM + r] >> (8 * lk)) & 0xffu) : 127;
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = wm * TM + 16 * i + lr;
-        const uint8_t* base = la + r * BK;
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * (lk ^ (r & 7)));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * ((lk + 4) ^ (r & 7)));
-        af[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        saw[i] = MX ? (int)((ls[r] >> (8 * lk)) & 0xffu) : 127;
-        if constexpr (BLK) {
-          const float4 v = *reinterpret_cast<const float4*>(ls + wm * TM + 16 * i + 4 * lk);
-          s4[i][0] = v.x;
-          s4[i][1] = v.y;
-          s4[i][2] = v.z;
-          s4[i][3] = v.w;
-        }
-      }
-      float sbk = 1.0f;
-      if constexpr (BLK) {
-        const int64_t nbt = N / 128;
-        const int64_t nb = (ti.n0 + wn * TN) / 128;
-        sbk = nb < nbt ? reinterpret_cast<const float*>(p.sb)[((int64_t)ti.e * nbt + nb) * nk + kt] : 0.0f;
-      }
-      if (more) issue(na, nb, ns, kt + 1);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          if constexpr (BLK) {
-            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-            const v4f tmp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], z, AE5 ? 1 : 0,
-                                                                             BE5 ? 1 : 0, 0, 127, 0, 127);
-            keep_live(af[i]);
-            keep_live(bf[j]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] += tmp[r] * (s4[i][r] * sbk);
-          } else {
-            // accumulators live in AGPRs here, so the destination cannot overlap
-            // the VGPR sources (checked on the assembly by the test suite)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], AE5 ? 1 : 0,
-                                                                         BE5 ? 1 : 0, 0, saw[i], 0, sbw[j]);
-          }
-        }
-      }
-    };
-
-    issue(la0, lb0, ls0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const bool odd = kt & 1;
-      step(odd ? la1 : la0, odd ? lb1 : lb0, odd ? ls1 : ls0, kt, odd ? la0 : la1, odd ? lb0 : lb1, odd ? ls0 : ls1,
-           kt + 1 < nk);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-
-    // ---- epilogue: scales and store ----
-    const float* SA = reinterpret_cast<const float*>(p.sa);
-    const float* SB = reinterpret_cast<const float*>(p.sb);
-    float st = 1.0f;
-    if constexpr (SK == kScaleTensor) st = SA[0] * SB[0];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t n = ti.n0 + wn * TN + 16 * j + lr;
-      if (n >= N) continue;
-      float sbn = 1.0f;
-      if constexpr (SK == kScaleRow) sbn = SB[(int64_t)ti.e * N + n];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = ti.m0 + wm * TM + 16 * i + 4 * lk + r;
-          if (m >= ti.m_end) continue;
-          float v = acc[i][j][r];
-          if constexpr (SK == kScaleTensor) v *= st;
-          if constexpr (SK == kScaleRow) v = v * SA[m] * sbn;
-          if constexpr (OF32)
-            reinterpret_cast<float*>(p.out)[m * N + n] = v;
-          else
-            reinterpret_cast<uint16_t*>(p.out)[m * N + n] = f32_to_bf16_rne(v);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Pipelined kernel for tensorwise, rowwise and MX scales (the dense Linear
 // GEMMs, the rowwise MoE grouped GEMM and the MX grouped GEMM).
@@ -599,6 +391,190 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 128-blockwise scales ("FP8 training on AMD GPUs with TorchTitan and
+// TorchAO", section "AMD FP8 format in TorchAO": activations in 1 x 128
+// blocks, weights in 128 x 128 blocks). Every 128-deep partial product carries
+// its own scale inv_a[m][kb] * inv_b[nb][kb], so partial sums cannot stay in
+// the matrix-core accumulator across K blocks.
+//
+//  - 256 x 256 output tile, 8 waves (two per SIMD) of 128 x 64, one
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 x 16 block and K block
+//    (measured lane layout: lane l feeds row l % 16 with K [16g, 16g + 16) and
+//    K [64 + 16g, 64 + 16g + 16), g = l / 16); its result is scaled and added
+//    into fp32 accumulators in VGPRs (4 FMAs per instruction, VALU work that
+//    overlaps the other wave's matrix-core work).
+//  - Stages of 128-deep K (64 KB of A and B plus the 256 A-block scales) in a
+//    two-slot LDS ring, loaded with the same inline-assembly LDS DMA as the
+//    pipelined kernel; the loads of stage k + 1 fly while stage k is
+//    multiplied. Rows of 128 bytes are XOR-swizzled in 16-byte chunks by
+//    (row % 8).
+//  - The B-block scale of the wave's 64 columns (N % 128 == 0, so they share
+//    one 128-column block) is a scalar load issued one stage ahead.
+template <bool AE5, bool BE5, bool OF32>
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
+  constexpr int BM = 256, BN = 256, BK = 128;
+  constexpr int NW = 8, WN = 4;
+  constexpr int TM = 128, TN = 64, MI = TM / 16, NI = TN / 16;
+  constexpr int SA_BYTES = BM * BK, STAGE = (BM + BN) * BK;
+  constexpr int D = STAGE / 1024 / NW;  // wave-wide 1 KB loads per wave per stage
+  static_assert(D == 8, "stage split");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float s_sa[2][BM];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int64_t s_pref[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t N = p.N, K = p.K;
+  const int64_t nt = (N + BN - 1) / BN;
+  const int64_t nk = K / BK;
+  const int64_t nbt = N / 128;
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int64_t total = build_tile_prefix<BM, 512>(p, nt, s_off, s_pref);
+  int64_t t_begin, t_end, t_step;
+  xcd_range(total, t_begin, t_end, t_step);
+
+  // wave w loads 1 KB pieces 8w .. 8w + 7 of a stage: 0-31 are A (8 rows of
+  // 128 bytes each), 32-63 are B; lane -> row lane / 8, chunk lane % 8
+  const bool loads_a = wave < 4;
+  const int q0 = (wave & 3) * D;
+  const int ld_row = lane >> 3, ld_pch = lane & 7;
+
+  // fragment read offsets within a stage (16-row block i of A, j of B)
+  uint32_t fa_lo[MI], fa_hi[MI], fb_lo[NI], fb_hi[NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * TM + 16 * i + lr;
+    fa_lo[i] = (uint32_t)(r * BK + 16 * (lg ^ (r & 7)));
+    fa_hi[i] = (uint32_t)(r * BK + 16 * ((lg + 4) ^ (r & 7)));
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int r = wn * TN + 16 * j + lr;
+    fb_lo[j] = (uint32_t)(SA_BYTES + r * BK + 16 * (lg ^ (r & 7)));
+    fb_hi[j] = (uint32_t)(SA_BYTES + r * BK + 16 * ((lg + 4) ^ (r & 7)));
+  }
+
+  for (int64_t t = t_begin; t < t_end; t += t_step) {
+    TileInfo ti;
+    tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+    ti.m0 = uniform64(ti.m0);
+    ti.m_end = uniform64(ti.m_end);
+    ti.n0 = uniform64(ti.n0);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    const int32_t K32 = (int32_t)K;
+    const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);
+    const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
+    const uint8_t* base = loads_a ? p.a + ti.m0 * K : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    const int32_t rows = loads_a ? a_rows : b_rows;
+    uint32_t off[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int r = 8 * (q0 + d) + ld_row;
+      const int c = ld_pch ^ (r & 7);
+      const int32_t rr = r < rows ? r : rows - 1;  // rows past the expert / N load a valid row
+      off[d] = (uint32_t)(rr * K32 + 16 * c);
+    }
+    const uint32_t opnd_lds = loads_a ? 0u : (uint32_t)SA_BYTES;
+    // A-block scales: wave w (and its twin w + 4, same bytes) loads rows
+    // 64 (w % 4) .. + 63 of inv_a[m][kb]
+    const float* sa_base = reinterpret_cast<const float*>(p.sa) + ti.m0 * nk;
+    int32_t sr = 64 * (wave & 3) + lane;
+    sr = sr < a_rows ? sr : a_rows - 1;
+    const uint32_t sa_off = (uint32_t)(sr * (int32_t)nk) * 4u;
+    // this wave's B-block scales: inv_b[e][nb][kb], nb of its 64 columns
+    const int64_t nb = (ti.n0 + wn * TN) / 128;
+    const float* sb_row = reinterpret_cast<const float*>(p.sb) + ((int64_t)ti.e * nbt + (nb < nbt ? nb : nbt - 1)) * nk;
+
+    auto issue = [&](int64_t k) {
+      const uint32_t slot = lds0 + (uint32_t)((k & 1) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
+      const uint8_t* bk = base + k * BK;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
+      const uint32_t sl = lds_addr(&s_sa[k & 1][64 * (wave & 3)]);
+      asm volatile("global_load_lds_dword %0, %1" ::"v"(sa_off + (uint32_t)(4 * k)),
+                   "s"(reinterpret_cast<const uint8_t*>(sa_base)), "{m0}"(sl)
+                   : "memory");
+    };
+
+    v4f acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    issue(0);
+    float sbk = sb_row[0];
+    for (int64_t k = 0; k < nk; ++k) {
+      // stage k landed everywhere and every wave is done with stage k - 1,
+      // whose slot the loads of stage k + 1 now fill
+      wait_vm_lgkm_and_barrier<0>();
+      if (k + 1 < nk) issue(k + 1);
+      const float sbk_next = sb_row[k + 1 < nk ? k + 1 : k];
+      const uint8_t* st = lds + (k & 1) * STAGE;
+      v8i bf[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + fb_lo[j]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + fb_hi[j]);
+        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + fa_lo[i]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + fa_hi[i]);
+        const v8i af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        // rows 16 i + 4 g + r (r < 4) of this lane's output block
+        const float4 sv = *reinterpret_cast<const float4*>(&s_sa[k & 1][wm * TM + 16 * i + 4 * lg]);
+        const float f0 = sv.x * sbk, f1 = sv.y * sbk, f2 = sv.z * sbk, f3 = sv.w * sbk;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+          const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], z, AE5 ? 1 : 0, BE5 ? 1 : 0,
+                                                                          0, 127, 0, 127);
+          // sources stay live until the result is used, so the compiler cannot
+          // hand their registers to the destination (not allowed for this MFMA)
+          asm volatile("" ::"v"(af), "v"(bf[j]), "v"(pr));
+          acc[i][j][0] += pr[0] * f0;
+          acc[i][j][1] += pr[1] * f1;
+          acc[i][j][2] += pr[2] * f2;
+          acc[i][j][3] += pr[3] * f3;
+        }
+      }
+      sbk = sbk_next;
+    }
+    // every wave is done reading the last stage before the next tile's loads
+    // refill its slot
+    wait_vm_lgkm_and_barrier<0>();
+
+    // ---- epilogue: lane l holds rows 16 i + 4 g + r, column 16 j + l % 16 ----
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t n = ti.n0 + wn * TN + 16 * j + lr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = ti.m0 + wm * TM + 16 * i + 4 * lg + r;
+          if (m >= ti.m_end) continue;
+          if constexpr (OF32)
+            reinterpret_cast<float*>(p.out)[m * N + n] = acc[i][j][r];
+          else
+            reinterpret_cast<uint16_t*>(p.out)[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
 template <bool AE5, bool BE5, int SK, bool OF32>
 static hipError_t launch_fast_cfg(const GemmArgs& g) {
   GemmParams p{g.a, g.b, g.sa, g.sb, g.offsets, g.E, g.M, g.N, g.K, g.out};
@@ -610,7 +586,7 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
   if (grid >= kNumXcd) grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
   if constexpr (SK == kScaleBlock) {
-    hipLaunchKernelGGL((k_gemm_fp8_fast<2, 4, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+    hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
   } else if constexpr (SK == kScaleTensor || SK == kScaleRow || SK == kScaleMX) {
     if (g.offsets)
       hipLaunchKernelGGL((k_gemm_fp8_pipe<AE5, BE5, SK, OF32, true>), dim3((unsigned)grid), dim3(256), 0, g.stream, p);
