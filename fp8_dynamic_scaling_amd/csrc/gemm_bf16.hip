@@ -12,22 +12,11 @@
 // 8 rows of 8 consecutive m values, the layout the bf16 matrix-core
 // instruction (v_mfma_f32_16x16x32_bf16, 8 consecutive contracted values per
 // lane) reads directly.
-#include "common.hpp"
-#include "internal.hpp"
+#include "gemm_common.hpp"
 
 namespace fp8dyn {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-constexpr int kWNumXcd = 8;
-constexpr int kWGroup = 4;
-
-__device__ __forceinline__ uint16_t w_f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 // 8 x 8 transpose of 16-bit values: in[r] holds row r (8 values, 2 per word);
 // out[c] receives column c (8 values, rows 0..7).
@@ -74,19 +63,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_wgrad_bf16(const uint16_t* _
   const int64_t total = tn * tk;
   const int64_t nsteps = (M + MS - 1) / MS;
 
-  const int64_t G = gridDim.x;
-  const int64_t per_xcd = G / kWNumXcd;
-  const int64_t xcd = blockIdx.x % kWNumXcd, slot = blockIdx.x / kWNumXcd;
   int64_t t_begin, t_end, t_step;
-  if (per_xcd > 0 && G % kWNumXcd == 0) {
-    t_begin = xcd * total / kWNumXcd + slot;
-    t_end = (xcd + 1) * total / kWNumXcd;
-    t_step = per_xcd;
-  } else {
-    t_begin = blockIdx.x;
-    t_end = total;
-    t_step = G;
-  }
+  xcd_range(total, t_begin, t_end, t_step);
 
   // loader role of this thread
   const bool is_g = tid < GBLK;
@@ -98,10 +76,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_wgrad_bf16(const uint16_t* _
   const int64_t limc = is_g ? N : K;
 
   for (int64_t t = t_begin; t < t_end; t += t_step) {
-    // grouped order: kWGroup row-tiles, column tiles fastest
-    const int64_t g = t / (kWGroup * tk), rem = t % (kWGroup * tk);
-    const int64_t gm = (tn - g * kWGroup) < kWGroup ? (tn - g * kWGroup) : kWGroup;
-    const int64_t n0 = (g * kWGroup + rem % gm) * BNT, k0 = (rem / gm) * BKT;
+    // grouped order: kGroupM row-tiles, column tiles fastest
+    const int64_t g = t / (kGroupM * tk), rem = t % (kGroupM * tk);
+    const int64_t gm = (tn - g * kGroupM) < kGroupM ? (tn - g * kGroupM) : kGroupM;
+    const int64_t n0 = (g * kGroupM + rem % gm) * BNT, k0 = (rem / gm) * BKT;
     const int64_t c0 = (is_g ? n0 : k0) + blk_c * 8;
 
     v4f acc[MI][NI];
@@ -172,7 +150,207 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_wgrad_bf16(const uint16_t* _
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t n = n0 + wm * TM + 16 * i + 4 * lk + r;
-          if (n < N) gw[n * K + k] = w_f32_to_bf16_rne(acc[i][j][r]);
+          if (n < N) gw[n * K + k] = f32_to_bf16_rne(acc[i][j][r]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined form for M % 64 == 0: no register transpose at all. Tiles of gy
+// and x go from HBM into LDS as stored (rows of m) with the LDS DMA of the
+// FP8 kernels, and the matrix-core fragments, which need consecutive m for a
+// fixed n (or k), are read with gfx950's transposing LDS read
+// ds_read_b64_tr_b16. Measured on MI355X: within each group of 16 lanes,
+// lane r supplies the address of 4 consecutive 16-bit values (row r of a
+// 16 x 4 block) and lane t receives rows 4e + t / 4 (e = 0..3) of column
+// t % 4. With lane r pointing at (m0 + r / 4, n0 + 4 (r % 4)), lane t
+// therefore receives the 4 consecutive m of column n0 + t; two such reads give
+// the 8 consecutive m that v_mfma_f32_32x32x16_bf16 takes per lane (lane l:
+// row l % 32, K [8 (l / 32), 8 (l / 32) + 8)).
+//
+//  - 256 (n) x 256 (k) output tile, 4 waves of 128 x 128 (accumulators in
+//    AGPRs), stages of 32 m (16 KB of gy + 16 KB of x), a ring of 4 stages:
+//    the loads of stage s + 4 are issued after the barrier of step s, the
+//    fragments of stage s + 1 are read while stage s is multiplied (the
+//    schedule of the FP8 pipelined kernel).
+//  - LDS rows are 512 bytes (256 values of one m); their 16-byte chunks are
+//    XOR-swizzled by 4 (m % 8), which spreads the 8 rows x 64 bytes of one
+//    transposing read over all banks.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v4s lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+struct WgFrags {
+  v8bf a[4][2], b[4][2];  // [32-row block][16-deep k step]
+};
+
+__global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restrict__ gy, const uint16_t* __restrict__ x,
+                                                      int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ gw) {
+  constexpr int BN = 256, BK = 256, MS = 32, NS = 4;
+  constexpr int ROWB = 512;                    // bytes per LDS row (256 values)
+  constexpr int SG = MS * ROWB, STAGE = 2 * SG;  // gy part, whole stage
+  constexpr int NW = 4, WN = 2, TM = 128, TN = 128, MI = 4, NI = 4;
+  constexpr int D = STAGE / 1024 / NW;  // wave-wide 1 KB loads per wave per stage
+  static_assert(D == 8, "stage split");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t tn = (N + BN - 1) / BN, tk = (K + BK - 1) / BK;
+  const int64_t total = tn * tk;
+  const int64_t nk = M / MS;  // even (M % 64 == 0)
+  const uint32_t lds0 = lds_addr(lds);
+  int64_t t_begin, t_end, t_step;
+  xcd_range(total, t_begin, t_end, t_step);
+
+  // loads: waves 0-1 take gy (16 pieces of 1 KB = 2 rows), waves 2-3 take x;
+  // lane i of a piece fills row 2 q + i / 32, physical chunk i % 32
+  const bool loads_g = wave < 2;
+  const int q0 = (wave & 1) * D;
+  const uint16_t* src = loads_g ? gy : x;
+  const int64_t ld = loads_g ? N : K;
+  const int64_t nchunk = ld / 8;  // valid 16-byte chunks per row
+
+  // transposing-read address of this lane within a stage region, for row
+  // block base rb (0..224), k step ks, half h: m = 16 ks + 8 (grp / 2) + 4 h +
+  // r / 4, column = rb + 16 (grp % 2) + 4 (r % 4)
+  const int grp = lane >> 4, rr4 = lane & 15;
+  auto tr_off = [&](int rb, int ks, int h) -> uint32_t {
+    const int m = 16 * ks + 8 * (grp >> 1) + 4 * h + (rr4 >> 2);
+    const int c = rb + 16 * (grp & 1) + 4 * (rr4 & 3);
+    const int chunk = (c >> 3) ^ ((m & 7) << 2);
+    return (uint32_t)(m * ROWB + chunk * 16 + (c & 7) * 2);
+  };
+  uint32_t fa[MI][2][2], fb[NI][2][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fa[i][ks][h] = tr_off(wm * TM + 32 * i, ks, h);
+        fb[i][ks][h] = (uint32_t)SG + tr_off(wn * TN + 32 * i, ks, h);
+      }
+
+  for (int64_t t = t_begin; t < t_end; t += t_step) {
+    // grouped order: 4 row tiles (n), column tiles (k) fastest
+    const int64_t g = t / (kGroupM * tk), rem = t % (kGroupM * tk);
+    const int64_t gm = (tn - g * kGroupM) < kGroupM ? (tn - g * kGroupM) : kGroupM;
+    const int64_t n0 = uniform64((g * kGroupM + rem % gm) * BN), k0 = uniform64((rem / gm) * BK);
+    const int64_t col0 = loads_g ? n0 : k0;
+    uint32_t off[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int row = 2 * (q0 + d) + (lane >> 5);
+      const int c = (lane & 31) ^ ((row & 7) << 2);
+      int64_t cc = col0 / 8 + c;
+      cc = cc < nchunk ? cc : nchunk - 1;  // columns past N (or K) load a valid chunk
+      off[d] = (uint32_t)((row * ld + 8 * cc) * 2);
+    }
+    const uint32_t opnd_lds = loads_g ? 0u : (uint32_t)SG;
+
+    auto issue = [&](int64_t s) {
+      const uint32_t slot = lds0 + (uint32_t)((s % NS) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
+      const uint8_t* bs = reinterpret_cast<const uint8_t*>(src + s * MS * ld);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dma16(bs, off[d], slot + (uint32_t)(d * 1024));
+    };
+    auto read = [&](int64_t s, WgFrags& f) {
+      const uint8_t* st = lds + (s % NS) * STAGE;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const v4s lo = lds_read_tr16(st + fa[i][ks][0]), hi = lds_read_tr16(st + fa[i][ks][1]);
+          f.a[i][ks] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const v4s lo = lds_read_tr16(st + fb[j][ks][0]), hi = lds_read_tr16(st + fb[j][ks][1]);
+          f.b[j][ks] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    v16f acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto mma = [&](const WgFrags& f) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i][ks], f.b[j][ks], acc[i][j], 0, 0, 0);
+    };
+    auto read_mma = [&](int64_t s_next, WgFrags& nxt, const WgFrags& cur) {
+      read(s_next, nxt);
+      mma(cur);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+    };
+    auto steady = [&](int64_t s, WgFrags& cur, WgFrags& nxt) {
+      wait_vm_lgkm_and_barrier<2 * D>();
+      issue(s + NS);
+      read_mma(s + 1, nxt, cur);
+    };
+
+    WgFrags f0, f1;
+    if (nk >= NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) issue(s);
+      wait_vm_and_barrier<(NS - 1) * D>();
+    } else {  // nk == 2
+      issue(0);
+      issue(1);
+      wait_vm_and_barrier<D>();
+    }
+    read(0, f0);
+    for (int64_t s = 0; s + NS < nk; s += 2) {
+      steady(s, f0, f1);
+      steady(s + 1, f1, f0);
+    }
+    if (nk >= NS) {
+      wait_vm_lgkm_and_barrier<2 * D>();
+      read_mma(nk - 3, f1, f0);
+      wait_vm_lgkm_and_barrier<D>();
+      read_mma(nk - 2, f0, f1);
+    }
+    wait_vm_lgkm_and_barrier<0>();
+    read_mma(nk - 1, f1, f0);
+    wait_vm_lgkm_and_barrier<0>();
+    mma(f1);
+
+    // ---- epilogue: register r of lane l in block (i, j) holds row (n)
+    // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column (k) 32 j + l % 32 ----
+    const int lg = lane >> 5, lc = lane & 31;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t k = k0 + wn * TN + 32 * j + lc;
+      if (k >= K) continue;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t n = n0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (n < N) gw[n * K + k] = f32_to_bf16_rne(acc[i][j][r]);
         }
     }
   }
@@ -182,13 +360,19 @@ hipError_t launch_wgrad_bf16(const WgradArgs& w) {
   if (w.N == 0 || w.K == 0) return hipSuccess;
   constexpr int BNT = 256, BKT = 256;
   const int64_t total = ((w.N + BNT - 1) / BNT) * ((w.K + BKT - 1) / BKT);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  const int cus = device_cus();
+  // pipelined form: whole 64-row steps of m; a stage (32 rows) of either
+  // operand addressed with 32-bit offsets
+  const int64_t ldmax = w.N > w.K ? w.N : w.K;
+  if (w.M >= 64 && w.M % 64 == 0 && 32 * ldmax * 2 < ((int64_t)1 << 31)) {
+    int64_t grid = cus < total ? cus : total;
+    if (grid >= kNumXcd) grid -= grid % kNumXcd;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_wgrad_pipe, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x, w.M, w.N, w.K, w.gw);
+    return hipGetLastError();
   }
   int64_t grid = cus < total ? cus : total;
-  if (grid >= kWNumXcd) grid -= grid % kWNumXcd;
+  if (grid >= kNumXcd) grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((k_wgrad_bf16<BNT, BKT, 2, 4>), dim3((unsigned)grid), dim3(512), 0, w.stream, w.gy, w.x, w.M, w.N,
                      w.K, w.gw);

@@ -114,4 +114,26 @@ __device__ __forceinline__ void xcd_range(int64_t total, int64_t& t_begin, int64
   }
 }
 
+// ---- LDS DMA pipeline helpers (gfx950) ----
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide 16-byte-per-lane load from global (uniform base + per-lane
+// 32-bit offset) into LDS at lds (uniform; lane i lands at lds + 16 i).
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 }  // namespace fp8dyn

@@ -52,26 +52,6 @@ namespace fp8dyn {
 //    reads its byte straight into the MFMA's scale operand.
 constexpr int kPipeStages = 4;
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One wave-wide 16-byte-per-lane load from global (uniform base + per-lane
-// 32-bit offset) into LDS at lds (uniform; lane i lands at lds + 16 i).
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 // Fragments of one 64-deep stage for one wave: 4 row blocks of A, 4 of B,
 // and (MX) this lane's E8M0 scale byte for each of them.
 struct PipeFrags {

@@ -226,7 +226,8 @@ def test_grouped_mx(f, counts, N, K):
     check_gemm(_host(out), ref, S, True, f"grouped mx {counts}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 264, 136), (1000, 512, 256), (7, 16, 8)])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 264, 136), (1000, 512, 256), (7, 16, 8), (128, 264, 136),
+                                   (640, 520, 264), (1024, 256, 256)])
 def test_wgrad_bf16(f, M, N, K):
     import torch
     g = synth.normal_bf16((M, N), 700 + M, 1e-3)
