@@ -76,6 +76,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
   // row), A rows then B rows, in a ring of 4 pairs
   constexpr bool MXS = SK == kScaleMX;
   __shared__ __attribute__((aligned(16))) uint32_t s_scl[MXS ? 4 : 1][MXS ? BM + BN : 1];
+  // epilogue: each wave's 128 row scales (rowwise)
+  __shared__ __attribute__((aligned(16))) float s_rs[SK == kScaleRow ? NW : 1][SK == kScaleRow ? TM : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -307,9 +309,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
     mma(f1);
 
     // ---- epilogue: 32 x 32 tile (i, j), register r of lane l holds
-    // row 32 i + 8 (r / 4) + 4 g + r % 4, column 32 j + l % 32. Per row block
-    // i the 16 row scales are gathered first so their loads overlap, then the
-    // products are scaled, rounded and stored. ----
+    // row 32 i + 8 (r / 4) + 4 g + r % 4, column 32 j + l % 32. The scales are
+    // gathered first so their loads overlap, then the products are scaled,
+    // rounded and stored. ----
     const float* SA = reinterpret_cast<const float*>(p.sa);
     const float* SB = reinterpret_cast<const float*>(p.sb);
     float cs[NI];
@@ -326,71 +328,60 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_pipe(GemmParams p) {
         cs[j] = SB[(int64_t)ti.e * N + n];
       }
     }
-    // stores relative to the tile's corner: 32-bit offsets (256 rows * N < 2^31)
+    const int32_t m_lim = (int32_t)(ti.m_end - ti.m0);
+    const int32_t n_lim = (int32_t)(N - ti.n0);
+    // the row scales of the wave's 128 rows go through LDS and are all loaded
+    // before the first store: stores and loads share one counter, so a load
+    // issued after stores would make its wait cover the stores too
+    if constexpr (SK == kScaleRow) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t m = ti.m0 + wm * TM + 64 * h + lane;
+        m = m < ti.m_end ? m : ti.m_end - 1;
+        s_rs[wave][64 * h + lane] = SA[m];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    // direct stores relative to the tile's corner (32-bit offsets: 256 rows *
+    // N < 2^31)
     int32_t N32 = (int32_t)N;
     // opaque per tile: keeps the compiler from hoisting every store address
     // out of the tile loop (256 precomputed addresses would spill)
     asm volatile("" : "+s"(N32));
-    const int32_t m_lim = (int32_t)(ti.m_end - ti.m0);
-    const int32_t n_lim = (int32_t)(N - ti.n0);
     // this lane's first row and column in the tile, also opaque per tile
     int32_t ml0 = wm * TM + 4 * lg, nl0 = wn * TN + lrow;
     asm volatile("" : "+v"(ml0), "+v"(nl0));
+    const int64_t corner = ti.m0 * N + ti.n0;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      float rs[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (SK == kScaleTensor || MXS) {
-          rs[r] = st;
-        } else {
-          int64_t m = ti.m0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          m = m < ti.m_end ? m : ti.m_end - 1;
-          rs[r] = SA[m];
-        }
-      }
-      // the scale loads have landed before the first store (stores share vmcnt)
-      __builtin_amdgcn_s_waitcnt(0);
+      for (int q = 0; q < 4; ++q) {
+        // rows 32 i + 8 q + 4 g + t, t < 4: the four row scales in one LDS read
+        float4 rs4 = make_float4(st, st, st, st);
+        if constexpr (SK == kScaleRow)
+          rs4 = *reinterpret_cast<const float4*>(&s_rs[wave][32 * i + 8 * q + 4 * lg]);
+        const float rsv[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int32_t nl = nl0 + 32 * j;
-        if (nl >= n_lim) continue;
+        for (int j = 0; j < NI; ++j) {
+          const int32_t nl = nl0 + 32 * j;
+          if (nl >= n_lim) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t ml = ml0 + 32 * i + 8 * (r >> 2) + (r & 3);
-          if (ml >= m_lim) continue;
-          const float v = acc[i][j][r] * rs[r] * cs[j];
-          const uint32_t o = (uint32_t)(ml * N32 + nl);
-          if constexpr (OF32)
-            (reinterpret_cast<float*>(p.out) + (ti.m0 * N + ti.n0))[o] = v;
-          else
-            (reinterpret_cast<uint16_t*>(p.out) + (ti.m0 * N + ti.n0))[o] = f32_to_bf16_rne(v);
+          for (int t = 0; t < 4; ++t) {
+            const int32_t ml = ml0 + 32 * i + 8 * q + t;
+            if (ml >= m_lim) continue;
+            const uint32_t o = (uint32_t)(ml * N32 + nl);
+            const float v = acc[i][j][4 * q + t] * rsv[t] * cs[j];
+            if constexpr (OF32)
+              (reinterpret_cast<float*>(p.out) + corner)[o] = v;
+            else
+              (reinterpret_cast<uint16_t*>(p.out) + corner)[o] = f32_to_bf16_rne(v);
+          }
         }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// 128-blockwise scales ("FP8 training on AMD GPUs with TorchTitan and
-// TorchAO", section "AMD FP8 format in TorchAO": activations in 1 x 128
-// blocks, weights in 128 x 128 blocks). Every 128-deep partial product carries
-// its own scale inv_a[m][kb] * inv_b[nb][kb], so partial sums cannot stay in
-// the matrix-core accumulator across K blocks.
-//
-//  - 256 x 256 output tile, 8 waves (two per SIMD) of 128 x 64, one
-//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 x 16 block and K block
-//    (measured lane layout: lane l feeds row l % 16 with K [16g, 16g + 16) and
-//    K [64 + 16g, 64 + 16g + 16), g = l / 16); its result is scaled and added
-//    into fp32 accumulators in VGPRs (4 FMAs per instruction, VALU work that
-//    overlaps the other wave's matrix-core work).
-//  - Stages of 128-deep K (64 KB of A and B plus the 256 A-block scales) in a
-//    two-slot LDS ring, loaded with the same inline-assembly LDS DMA as the
-//    pipelined kernel; the loads of stage k + 1 fly while stage k is
-//    multiplied. Rows of 128 bytes are XOR-swizzled in 16-byte chunks by
-//    (row % 8).
-//  - The B-block scale of the wave's 64 columns (N % 128 == 0, so they share
-//    one 128-column block) is a scalar load issued one stage ahead.
 template <bool AE5, bool BE5, bool OF32>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 128;
