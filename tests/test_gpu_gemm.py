@@ -97,7 +97,7 @@ def test_small_integer_products_are_exact(f):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 512, 512), (1, 16, 16), (100, 72, 48), (300, 200, 384), (513, 260, 1040),
-                                   (300, 520, 1152), (64, 64, 128)])
+                                   (300, 520, 1152), (64, 64, 128), (200, 136, 256), (2100, 8200, 128)])
 @pytest.mark.parametrize("scaling", ["tensor", "row"])
 @pytest.mark.parametrize("out_f32", [True, False])
 def test_scaled_mm(f, M, N, K, scaling, out_f32):
