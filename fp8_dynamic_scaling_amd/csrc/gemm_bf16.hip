@@ -172,8 +172,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_wgrad_bf16(const uint16_t* _
 //  - 256 (n) x 256 (k) output tile, 4 waves of 128 x 128 (accumulators in
 //    AGPRs), stages of 32 m (16 KB of gy + 16 KB of x), a ring of 4 stages:
 //    the loads of stage s + 4 are issued after the barrier of step s, the
-//    fragments of stage s + 1 are read while stage s is multiplied (the
-//    schedule of the FP8 pipelined kernel).
+//    fragments of stage s + 1 are read while stage s is multiplied, so each
+//    load has three steps to land.
 //  - LDS rows are 512 bytes (256 values of one m); their 16-byte chunks are
 //    XOR-swizzled by 4 (m % 8), which spreads the 8 rows x 64 bytes of one
 //    transposing read over all banks.
