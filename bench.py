@@ -5,7 +5,10 @@ already resident in HBM:
   linear_tensorwise  fp8_linear_fwd, X [256,512] W [512,512], one scale each, fp32 out
   linear_rowwise     Llama3-8B MLP (tokens 8192, K 4096, N 14336): rowwise quant of X, W
                      (e4m3) and grad_out (e5m2), per-column transposed quant of W, FP8
-                     forward and grad-input GEMMs, BF16 weight-gradient GEMM
+                     forward and grad-input GEMMs, BF16 weight-gradient GEMM; beside it
+                     (reported per row, outside the aggregates) the all-FP8 tensorwise
+                     backward of the same layer: the dual quantization of grad_out and X,
+                     the FP8 weight-gradient GEMM and the whole fp8_linear_bwd call
   expert_colwise     per-expert column scales + transposed cast, 32 x [2048,7168]
   moe_grouped        rowwise quant of A [131072,7168] and of W [32][2048][7168] (per
                      expert column), FP8 grouped GEMM over int32[33] offsets -> bf16
@@ -110,6 +113,23 @@ def build_step(f, torch, dev, wls, dev_of):
            lambda: f.fp8_scaled_mm(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2, use_fast_accum=False))
     st.add("linear_rowwise.wgrad_bf16", "gemm16", 2.0 * M * N * K,
            lambda: f.fp8_wgrad_bf16(g2, x2, gw2))
+
+    # ---- the all-FP8 tensorwise backward of the same layer (beside the
+    # rowwise recipe; not part of the aggregate figures) ----
+    gqb, gqTb, xqTb = torch.empty((M, N), **u8), torch.empty((N, M), **u8), torch.empty((K, M), **u8)
+    dsc = [torch.empty(1, **f32) for _ in range(4)]
+    dws = torch.empty(f.fp8_quant_dual_ws_bytes(), **u8)
+    gwf = torch.empty((N, K), **bf)
+    gxt, gwt = torch.empty((M, K), **bf), torch.empty((N, K), **bf)
+    lws2 = torch.empty(f.fp8_linear_ws_bytes(M, N, K, f.RECIPE_TENSORWISE), **u8)
+    st.add("linear_tensorwise_fp8_bwd.quant_dual_gy_x", "quant_next",
+           2 * (M * N + M * K) + 2 * M * N + M * K + 16,
+           lambda: f.fp8_quant_dual(g2, x2, E5, E4, EPS, gqb, gqTb, dsc[0], dsc[1], xqTb, dsc[2], dsc[3], dws))
+    st.add("linear_tensorwise_fp8_bwd.gemm_wgrad_fp8", "gemm8_next", 2.0 * M * N * K,
+           lambda: f.fp8_scaled_mm(gqTb, E5, xqTb, E4, f.SCALE_TENSOR, dsc[1], dsc[3], f.OUT_BF16, gwf,
+                                   use_fast_accum=False))
+    st.add("linear_tensorwise_fp8_bwd.linear_bwd", "latency", 4.0 * M * N * K,
+           lambda: f.fp8_linear_bwd(g2, x2, wt2, f.RECIPE_TENSORWISE, EPS, gxt, gwt, lws2))
 
     # ---- expert_colwise ----
     w3 = wls["expert_colwise"]
@@ -332,12 +352,15 @@ def main():
                      bytes=int(work))
             q_bytes += work
             q_time += avg
-        elif kind in ("gemm8", "gemm16"):
-            peak = FP8_PEAK_TFLOPS if kind == "gemm8" else BF16_PEAK_TFLOPS
+        elif kind == "quant_next":
+            r.update(gbs=round(work / avg / 1e9, 1), frac_hbm=round(work / avg / 1e9 / HBM_PEAK_GBS, 4),
+                     bytes=int(work))
+        elif kind in ("gemm8", "gemm16", "gemm8_next"):
+            peak = BF16_PEAK_TFLOPS if kind == "gemm16" else FP8_PEAK_TFLOPS
             r.update(tflops=round(work / avg / 1e12, 1), frac_mfma=round(work / avg / 1e12 / peak, 4),
                      flops=work)
         rows[name] = r
-        if kind != "latency" and (dom is None or avg > dom[2]):
+        if kind in ("quant", "gemm8", "gemm16") and (dom is None or avg > dom[2]):
             dom = (name, kind, avg, work)
 
     out = {"metric": METRIC}

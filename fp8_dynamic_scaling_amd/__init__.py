@@ -25,7 +25,8 @@ RECIPE_TENSORWISE, RECIPE_ROWWISE_BF16_WGRAD = range(2)
 EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_col",
-    "fp8_quant_col_ws_bytes", "fp8_quant_block", "fp8_quant_mx", "fp8_scaled_mm",
+    "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_quant_block", "fp8_quant_mx",
+    "fp8_scaled_mm",
     "fp8_grouped_mm", "fp8_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
 ]
@@ -62,6 +63,8 @@ def load(path: str = LIB_PATH):
         "fp8_quant_row": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
+        "fp8_quant_dual": (I, [P, P, I64, I64, I64, I, I, D, P, P, P, P, P, P, P, P, SZ, P]),
+        "fp8_quant_dual_ws_bytes": (SZ, []),
         "fp8_quant_block": (I, [P, I64, I64, I64, I, I, I, D, P, P, P, P]),
         "fp8_quant_mx": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
         "fp8_scaled_mm": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
@@ -154,6 +157,20 @@ def fp8_quant_col(x, fmt, eps, qT, scale, inv_scale=None, ws=None, stream=None):
     b, r, c = _brc(x)
     _check("fp8_quant_col", load().fp8_quant_col(
         _ptr(x), b, r, c, int(fmt), float(eps), _ptr(qT), _ptr(scale), _ptr(inv_scale),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def fp8_quant_dual_ws_bytes() -> int:
+    return load().fp8_quant_dual_ws_bytes()
+
+
+def fp8_quant_dual(gy, x, g_fmt, x_fmt, eps, gq, gqT, g_scale, g_inv, xqT, x_scale, x_inv, ws, stream=None):
+    """gy [M][N] and x [M][K] bf16 -> gq [M][N] (or None), gqT [N][M], xqT [K][M]."""
+    M, N = gy.shape
+    K = x.shape[1]
+    _check("fp8_quant_dual", load().fp8_quant_dual(
+        _ptr(gy), _ptr(x), M, N, K, int(g_fmt), int(x_fmt), float(eps), _ptr(gq), _ptr(gqT),
+        _ptr(g_scale), _ptr(g_inv), _ptr(xqT), _ptr(x_scale), _ptr(x_inv),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 

@@ -202,6 +202,29 @@ fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   return dev_err(launch_quant_col(a, ws));
 }
 
+size_t fp8_quant_dual_ws_bytes(void) { return 256; }
+
+fp8_status fp8_quant_dual(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N, int64_t K, fp8_format g_fmt,
+                          fp8_format x_fmt, double eps, uint8_t* gq, uint8_t* gqT, float* g_scale, float* g_inv,
+                          uint8_t* xqT, float* x_scale, float* x_inv, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || bad_eps(eps)) return FP8_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0 || K == 0) return FP8_OK;
+  if (!gy || !x || !gqT || !g_scale || !xqT || !x_scale) return FP8_ERR_INVALID_ARGUMENT;
+  if (M % 16 != 0 || N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
+  if (M * N >= ((int64_t)1 << 30) || M * K >= ((int64_t)1 << 30)) return FP8_ERR_UNSUPPORTED;
+  if (!aligned(gy, 16) || !aligned(x, 16) || !aligned(gqT, 16) || !aligned(xqT, 16) || (gq && !aligned(gq, 8)) ||
+      !aligned(g_scale, 4) || !aligned(x_scale, 4) || (g_inv && !aligned(g_inv, 4)) || (x_inv && !aligned(x_inv, 4)))
+    return FP8_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < fp8_quant_dual_ws_bytes()) return FP8_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
+  bool ge5, xe5;
+  double gfm, xfm;
+  fp8_status st;
+  if ((st = resolve(g_fmt, &ge5, &gfm)) != FP8_OK || (st = resolve(x_fmt, &xe5, &xfm)) != FP8_OK) return st;
+  const TJobSpec jobs[2] = {{gy, M, N, ge5, gfm, gq, gqT, g_scale, g_inv}, {x, M, K, xe5, xfm, nullptr, xqT, x_scale, x_inv}};
+  return dev_err(launch_quant_tensor_multi_t(jobs, 2, eps, (uint32_t*)ws, (hipStream_t)stream));
+}
+
 fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
                            int block_cols, fp8_format fmt, double eps, uint8_t* q, float* scale, float* inv_scale,
                            void* stream) {

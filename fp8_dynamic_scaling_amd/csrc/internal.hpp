@@ -28,6 +28,25 @@ hipError_t launch_quant_tensor(const QuantArgs& a, void* ws);  // ws >= 256 byte
 // tensorwise scale, transposed output qT[b][c][r]; needs cols % 8 == 0, rows % 16 == 0
 hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws);
 hipError_t launch_quant_block(const QuantArgs& a, int block_rows, int block_cols);
+// Tensorwise quantization of up to kMaxTJobs tensors in three launches (clear
+// the amax words, amax of every tensor, one cast launch): each tensor gets its
+// transposed output qT [cols][rows] and, when q is set, its row-major output
+// q [rows][cols] from the same read. rows % 16 == 0, cols % 8 == 0,
+// rows * cols < 2^30, 16-byte aligned x and qT, 8-byte aligned q.
+// amax_words: kMaxTJobs device words.
+constexpr int kMaxTJobs = 3;
+struct TJobSpec {
+  const uint16_t* x;
+  int64_t rows, cols;
+  bool e5;
+  double fmax;
+  uint8_t* q;   // or nullptr
+  uint8_t* qT;
+  float* scale;
+  float* inv;   // or nullptr
+};
+hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps, uint32_t* amax_words,
+                                       hipStream_t stream);
 hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode);
 
 // Probe kernels: results[0..3] = fp8 codes of 1.0 (e4m3, e5m2) and of the

@@ -6,9 +6,12 @@
 //
 //   forward   y  = (qx * inv_x) (qw * inv_w)^T    qx, qw: e4m3
 //   backward  gx = (qg * inv_g) (qwT * inv_wc)^T  qg: e5m2 of gy, qwT: e4m3 of w
-//                                                 quantized per column of w and
 //                                                 written transposed [K][N]
-//             gw = gy^T x                         bf16 matrix cores
+//                                                 (rowwise: per column of w)
+//             gw = (qgT * inv_g) (qxT * inv_x)^T  tensorwise: all-FP8, qgT and
+//                                                 qxT transposed [N][M], [K][M]
+//                                                 from one cast launch with qg
+//             gw = gy^T x                         rowwise: bf16 matrix cores
 // Every FP8 operand is produced directly in the layout its GEMM reads: no
 // transposed copies ("FP8 training on AMD GPUs with TorchTitan and TorchAO",
 // Level 1).
@@ -49,7 +52,7 @@ FwdLayout fwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r,
 }
 
 struct BwdLayout {
-  void *qg, *sg, *ig, *qwt, *swc, *iwc, *wsg, *wscol;
+  void *qg, *sg, *ig, *qwt, *swc, *iwc, *wsg, *wscol, *qgt, *qxt, *sx, *ix;
 };
 BwdLayout bwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r, size_t* total) {
   Bump b{ws};
@@ -64,6 +67,11 @@ BwdLayout bwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r,
   L.wsg = b.take(256);
   size_t colws = tw ? 256 : quant_col_ws_bytes(1, N, K);
   L.wscol = b.take(colws > 0 ? colws : 256);
+  // tensorwise: transposed gy and x for the FP8 grad-weight GEMM
+  L.qgt = tw ? b.take((size_t)(N * M)) : nullptr;
+  L.qxt = tw ? b.take((size_t)(K * M)) : nullptr;
+  L.sx = tw ? b.take(4) : nullptr;
+  L.ix = tw ? b.take(4) : nullptr;
   *total = b.off;
   return L;
 }
@@ -137,18 +145,22 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
   const bool tw = recipe == FP8_RECIPE_TENSORWISE;
   fp8_status st;
   if (tw) {
-    if ((st = fp8_quant_tensor(gy, M * N, FP8_E5M2_NATIVE, eps, (uint8_t*)L.qg, (float*)L.sg, (float*)L.ig, L.wsg, 256,
-                               stream)) != FP8_OK)
-      return st;
-    // one scale for w, written transposed [K][N]
-    bool e5 = false;
+    // the transposed casts and the grad-weight GEMM contract over m
+    if (M % 16 != 0) return FP8_ERR_ALIGNMENT;
+    const int64_t lim = (int64_t)1 << 30;
+    if (M * N >= lim || M * K >= lim || N * K >= lim) return FP8_ERR_UNSUPPORTED;
     fp8_format e4f, e5f;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FP8_ERR_DEVICE;
     if ((st = fp8_probe(dev, &e4f, &e5f)) != FP8_OK) return st;
-    QuantArgs a{w, 1, N, K, e5, fp8_format_max(e4f), eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc,
-                (hipStream_t)stream};
-    if ((st = as_status(launch_quant_tensor_transposed(a, L.wscol))) != FP8_OK) return st;
+    // one amax launch and one cast launch for all three tensors: gy in both
+    // layouts (e5m2), x transposed [K][M] and w transposed [K][N] (e4m3)
+    const TJobSpec jobs[3] = {
+        {gy, M, N, true, fp8_format_max(e5f), (uint8_t*)L.qg, (uint8_t*)L.qgt, (float*)L.sg, (float*)L.ig},
+        {x, M, K, false, fp8_format_max(e4f), nullptr, (uint8_t*)L.qxt, (float*)L.sx, (float*)L.ix},
+        {w, N, K, false, fp8_format_max(e4f), nullptr, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc}};
+    if ((st = as_status(launch_quant_tensor_multi_t(jobs, 3, eps, (uint32_t*)L.wsg, (hipStream_t)stream))) != FP8_OK)
+      return st;
   } else {
     if ((st = fp8_quant_row(gy, 1, M, N, FP8_E5M2_NATIVE, eps, (uint8_t*)L.qg, (float*)L.sg, (float*)L.ig, stream)) !=
         FP8_OK)
@@ -162,7 +174,10 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
                           tw ? FP8_SCALE_TENSOR : FP8_SCALE_ROW, (const float*)L.ig, (const float*)L.iwc, M, K, N,
                           FP8_OUT_BF16, gx, 0, stream)) != FP8_OK)
     return st;
-  // grad-weight in BF16: [N][K] = gy^T x
+  // grad-weight [N][K]: tensorwise in FP8, ([N][M] x ([K][M])^T), rowwise in BF16 (gy^T x)
+  if (tw)
+    return fp8_scaled_mm((const uint8_t*)L.qgt, FP8_E5M2_NATIVE, (const uint8_t*)L.qxt, FP8_E4M3_NATIVE,
+                         FP8_SCALE_TENSOR, (const float*)L.ig, (const float*)L.ix, N, K, M, FP8_OUT_BF16, gw, 0, stream);
   return fp8_wgrad_bf16(gy, x, M, N, K, gw, stream);
 }
 

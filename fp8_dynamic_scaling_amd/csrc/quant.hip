@@ -413,16 +413,40 @@ __global__ void k_clear_words(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
+// max |x| over the 16-byte vectors [0, nvec) of x, for workgroup `blk` of
+// `nblk` (256 threads each): kAmaxU loads in flight per thread, in chunks of
+// kAmaxU * 256 vectors dealt round robin to the workgroups.
+constexpr int kAmaxU = 8;
+__device__ __forceinline__ float amax_vec_range(const uint16_t* __restrict__ x, int64_t nvec, int64_t blk,
+                                                int64_t nblk) {
+  float m = 0.0f;
+  const int64_t stride = nblk * 256 * kAmaxU;
+  int64_t i = blk * 256 * kAmaxU + threadIdx.x;
+  for (; i + (kAmaxU - 1) * 256 < nvec; i += stride) {
+    uint4 v[kAmaxU];
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) v[u] = ld_nt16(x + 8 * (i + u * 256));
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) m = amax8(v[u], m);
+  }
+  // the partial chunk (later chunks of this thread start past nvec)
+#pragma unroll
+  for (int u = 0; u < kAmaxU; ++u)
+    if (i + u * 256 < nvec) m = amax8(ld_nt16(x + 8 * (i + u * 256)), m);
+  return m;
+}
+
+// workgroups for amax_vec_range over nvec vectors: one chunk each, at most 2048
+static int64_t amax_blocks(int64_t nvec) {
+  int64_t b = (nvec + 256 * kAmaxU - 1) / (256 * kAmaxU);
+  return b < 1 ? 1 : (b > 2048 ? 2048 : b);
+}
+
 __global__ __launch_bounds__(256) void k_amax_tensor(const uint16_t* __restrict__ x, int64_t n,
                                                      uint32_t* __restrict__ amax_word) {
   __shared__ float red[4];
-  float m = 0.0f;
   const int64_t nvec = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
-    const uint4 v = ld_nt16(x + 8 * i);
-    m = amax8(v, m);
-  }
+  float m = amax_vec_range(x, nvec, blockIdx.x, gridDim.x);
   // tail (n % 8 elements)
   if (blockIdx.x == 0)
     for (int64_t i = nvec * 8 + threadIdx.x; i < n; i += 256)
@@ -695,13 +719,10 @@ static hipError_t launch_tensor_t_t(const QuantArgs& a, uint32_t* amax_word) {
   const int64_t n = B * R * C;
   if (n == 0) return hipSuccess;
   const int64_t nvec = n / 8;
-  int64_t blocks = (nvec + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
   const int64_t strips = (C + 63) / 64;
   const int64_t rchunks = (R + kColChunk - 1) / kColChunk;
   hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
-  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n, amax_word);
+  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)amax_blocks(nvec)), dim3(256), 0, a.stream, a.x, n, amax_word);
   hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
                      strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, amax_word, (int64_t)0, a.fmax,
                      a.eps);
@@ -727,9 +748,169 @@ static hipError_t launch_tensor_t(const QuantArgs& a, uint32_t* amax_word) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
-  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n, amax_word);
+  hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)amax_blocks(nvec)), dim3(256), 0, a.stream, a.x, n, amax_word);
   hipLaunchKernelGGL((k_cast_tensor<E5>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n,
                      (const uint32_t*)amax_word, a.q, a.scale, a.inv, a.fmax, a.eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Tensorwise quantization of up to three tensors in two launches, for the
+// all-FP8 backward of one Linear layer ("FP8 Training: Quantization,
+// Autograd, Torchao", section 4: grad_weight = grad_output^T @ input needs
+// grad_output transposed in row-major form and the input column-major; "FP8
+// training on AMD GPUs with TorchTitan and TorchAO", Figure 4 caption: a
+// companion kernel quantizes grad_output and the activation together).
+//  - k_amax_multi: the amax of every tensor (one atomic word each);
+//  - k_cast_multi_t: every tensor's transposed output qT [C][R] and, where
+//    asked, its row-major output q [R][C] from the same registers, so
+//    grad_output is read once for both layouts. Blocks are dealt to tensors by
+//    ranges of blockIdx.x; a block casts 64 columns x up to kColChunk rows with
+//    the 16 x 8 register transpose of the column kernel above.
+struct TJob {
+  const uint16_t* x;  // [R][C], R % 16 == 0, C % 8 == 0, R * C < 2^30
+  int64_t R, C;
+  uint8_t* q;         // [R][C] or nullptr
+  uint8_t* qT;        // [C][R]
+  float* scale;
+  float* inv;         // or nullptr
+  uint32_t* amax;     // one word, cleared before k_amax_multi
+  double fmax;
+  int e5;
+  int64_t amax_blk0, amax_blks;  // this tensor's blocks of k_amax_multi
+  int64_t cast_blk0, rchunks;    // and of k_cast_multi_t (strips x rchunks)
+};
+struct TJobs {
+  TJob j[kMaxTJobs];
+  int n;
+  double eps;
+};
+
+__device__ __forceinline__ int tjob_of(const TJobs& js, int64_t blk, bool cast) {
+  int k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxTJobs; ++i)
+    if (i < js.n && blk >= (cast ? js.j[i].cast_blk0 : js.j[i].amax_blk0)) k = i;
+  return k;
+}
+
+__global__ __launch_bounds__(256) void k_amax_multi(const TJobs js) {
+  __shared__ float red[4];
+  const int k = tjob_of(js, blockIdx.x, false);
+  const TJob& J = js.j[k];
+  float m = amax_vec_range(J.x, J.R * J.C / 8, blockIdx.x - J.amax_blk0, J.amax_blks);
+  m = block_max<256>(m, red);
+  if (threadIdx.x == 0) atomic_max_relaxed(J.amax, m);
+}
+
+template <bool E5>
+__device__ __forceinline__ void cast_strip_t(const TJob& J, int64_t strip, int64_t rc, float s) {
+  const int tid = threadIdx.x;
+  const int l8 = tid & 7, rg = tid >> 3;
+  const int64_t R = J.R, C = J.C;
+  if (strip * 64 + l8 * 8 >= C) return;
+  const float fm = (float)J.fmax;
+  const int64_t r_beg = rc * kColChunk;
+  const int64_t r_end = r_beg + kColChunk < R ? r_beg + kColChunk : R;
+  // uniform bases plus 32-bit per-lane offsets (R * C < 2^30)
+  const uint8_t* xs = reinterpret_cast<const uint8_t*>(J.x + strip * 64);
+  uint8_t* qs = J.qT + strip * 64 * R;
+  uint8_t* qr = J.q ? J.q + strip * 64 + l8 * 8 : nullptr;
+  const uint32_t row_b = (uint32_t)(C * 2);
+  const uint32_t R32 = (uint32_t)R, C32 = (uint32_t)C;
+  const int64_t ngroups = (r_end - r_beg) / kColRPT;
+  for (int64_t g = rg; g < ngroups; g += 32) {
+    const uint32_t r0 = (uint32_t)(r_beg + g * kColRPT);
+    const uint32_t xo = r0 * row_b + (uint32_t)(l8 * 16);
+    // pk[i][d]: column i, rows r0 + 4d .. r0 + 4d + 3 as four fp8 bytes
+    uint32_t pk[8][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ld_nt16(xs + xo + (uint32_t)(8 * h + j) * row_b);
+      float f[8][8];  // [column i][row j]
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = (i < 2) ? v[j].x : (i < 4) ? v[j].y : (i < 6) ? v[j].z : v[j].w;
+          f[i][j] = clampf(((i & 1) ? bf16_hi(w) : bf16_lo(w)) * s, fm);
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pk[i][2 * h] = cvt4<E5>(f[i][0], f[i][1], f[i][2], f[i][3]);
+        pk[i][2 * h + 1] = cvt4<E5>(f[i][4], f[i][5], f[i][6], f[i][7]);
+      }
+      if (qr) {
+        // row-major: 8 columns of each of the 8 rows, the same conversions;
+        // plain stores (a strip writes half of each 128-byte line, the
+        // neighbouring strip the other half: L2 merges them)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint2*>(qr + (r0 + (uint32_t)(8 * h + j)) * C32) =
+              make_uint2(cvt4<E5>(f[0][j], f[1][j], f[2][j], f[3][j]), cvt4<E5>(f[4][j], f[5][j], f[6][j], f[7][j]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st_nt16(qs + (uint32_t)(l8 * 8 + i) * R32 + r0, make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cast_multi_t(const TJobs js) {
+  const int k = tjob_of(js, blockIdx.x, true);
+  const TJob& J = js.j[k];
+  const int64_t lb = blockIdx.x - J.cast_blk0;
+  const int64_t rc = lb % J.rchunks, strip = lb / J.rchunks;
+  float s, iv;
+  scale_from_amax(__uint_as_float(*J.amax), J.fmax, js.eps, s, iv);
+  if (lb == 0 && threadIdx.x == 0) {
+    J.scale[0] = s;
+    if (J.inv) J.inv[0] = iv;
+  }
+  if (J.e5)
+    cast_strip_t<true>(J, strip, rc, s);
+  else
+    cast_strip_t<false>(J, strip, rc, s);
+}
+
+hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps, uint32_t* amax_words,
+                                       hipStream_t stream) {
+  if (n < 1 || n > kMaxTJobs) return hipErrorInvalidValue;
+  TJobs js{};
+  js.n = n;
+  js.eps = eps;
+  int64_t ab = 0, cb = 0;
+  for (int i = 0; i < n; ++i) {
+    const TJobSpec& t = specs[i];
+    if (t.rows % 16 != 0 || t.cols % 8 != 0 || t.rows * t.cols >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
+    TJob& J = js.j[i];
+    J.x = t.x;
+    J.R = t.rows;
+    J.C = t.cols;
+    J.q = t.q;
+    J.qT = t.qT;
+    J.scale = t.scale;
+    J.inv = t.inv;
+    J.amax = amax_words + i;
+    J.fmax = t.fmax;
+    J.e5 = t.e5 ? 1 : 0;
+    const int64_t nvec = t.rows * t.cols / 8;
+    // blocks in proportion to the tensor (about 4 chunks each), so that
+    // tensors of different sizes finish together
+    const int64_t blocks = (nvec + 4 * 256 * kAmaxU - 1) / (4 * 256 * kAmaxU);
+    J.amax_blk0 = ab;
+    J.amax_blks = blocks;
+    ab += blocks;
+    J.rchunks = (t.rows + kColChunk - 1) / kColChunk;
+    if (J.rchunks < 1) J.rchunks = 1;
+    J.cast_blk0 = cb;
+    cb += J.rchunks * ((t.cols + 63) / 64);
+  }
+  hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, stream, amax_words, (int64_t)n);
+  hipLaunchKernelGGL(k_amax_multi, dim3((unsigned)ab), dim3(256), 0, stream, js);
+  hipLaunchKernelGGL(k_cast_multi_t, dim3((unsigned)cb), dim3(256), 0, stream, js);
   return hipGetLastError();
 }
 

@@ -149,6 +149,28 @@ FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t ro
                                     float* inv_scale, void* ws, size_t ws_bytes, void* stream);
 FP8DYN_API size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
 
+/* Dual tensorwise quantization for the all-FP8 Linear backward ["FP8
+ * Training: Quantization, Autograd, Torchao" section 4: grad_weight =
+ * grad_output^T @ input takes grad_output transposed (row-major [N][M]) and
+ * the input column-major; "FP8 training on AMD GPUs with TorchTitan and
+ * TorchAO" Figure 4 caption: a companion kernel quantizes grad_output and the
+ * activation together]. One scale per tensor (amax over the whole tensor,
+ * then the scale rule of fp8_quant_tensor); one amax launch over gy and x,
+ * then ONE cast launch that reads each input once and writes
+ *   gq  [M][N] = ENC(gy * g_scale), row-major (grad-input GEMM's A); may be NULL
+ *   gqT [N][M] = the same bytes transposed (grad-weight GEMM's A)
+ *   xqT [K][M] = ENC(x * x_scale) transposed (grad-weight GEMM's B).
+ * gy [M][N], x [M][K] bf16 row-major; g_scale, x_scale [1] (inv: [1] or
+ * NULL). All pointers device memory owned by the caller. M % 16 == 0,
+ * N % 8 == 0, K % 8 == 0 (else FP8_ERR_ALIGNMENT); M*N and M*K < 2^30 (else
+ * FP8_ERR_UNSUPPORTED); gy, x, gqT, xqT 16-byte aligned, gq 8-byte aligned.
+ * ws: fp8_quant_dual_ws_bytes() bytes, 256-byte aligned (two amax words). */
+FP8DYN_API fp8_status fp8_quant_dual(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                                     fp8_format g_fmt, fp8_format x_fmt, double eps, uint8_t* gq, uint8_t* gqT,
+                                     float* g_scale, float* g_inv, uint8_t* xqT, float* x_scale, float* x_inv,
+                                     void* ws, size_t ws_bytes, void* stream);
+FP8DYN_API size_t fp8_quant_dual_ws_bytes(void);
+
 /* Blocks of block_rows x block_cols (1x128 for activations, 128x128 for
  * weights [P-AMD "AMD FP8 format in TorchAO", blockwise]): x
  * [batch][rows][cols] -> q same layout, scale/inv
@@ -207,10 +229,17 @@ FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int6
 FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                      int64_t K, fp8_recipe recipe, double eps, fp8_out out_type,
                                      void* y, void* ws, size_t ws_bytes, void* stream);
-/* Backward: gy [M][N] bf16 (quantized e5m2: per row for ROWWISE, one scale
- * for TENSORWISE); w quantized e4m3 per column with the transposed output;
- * gx [M][K] bf16 = FP8 GEMM. gw [N][K] bf16: the BF16 GEMM for ROWWISE; for
- * TENSORWISE also BF16 here (the all-FP8 weight gradient is not provided). */
+/* Backward ["FP8 Training: Quantization, Autograd, Torchao" section 4: the
+ * grad-input and grad-weight GEMMs]: gy [M][N], x [M][K], w [N][K] bf16.
+ * gx [M][K] bf16 = FP8 GEMM of gy (e5m2) and w (e4m3, written transposed
+ * [K][N]; per column of w for ROWWISE). gw [N][K] bf16:
+ *  - TENSORWISE: all-FP8, gw = (gy^T in e5m2) x (x in e4m3) over m, with the
+ *    operands gy^T [N][M] and x^T [K][M] written by the same single cast
+ *    launch that writes gy [M][N] and w^T (fp8_quant_dual's kernels, one
+ *    scale per tensor); needs M % 16 == 0 (else FP8_ERR_ALIGNMENT) and
+ *    M*N, M*K, N*K < 2^30 (else FP8_ERR_UNSUPPORTED);
+ *  - ROWWISE_BF16_WGRAD: the BF16 GEMM gy^T x ["FP8 training on AMD GPUs
+ *    with TorchTitan and TorchAO" Figure 1 caption]. */
 FP8DYN_API fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w,
                                      int64_t M, int64_t N, int64_t K, fp8_recipe recipe, double eps,
                                      uint16_t* gx, uint16_t* gw, void* ws, size_t ws_bytes,

@@ -162,6 +162,20 @@ def quant_tensor(x, fmt, eps=1e-12):
     return q, s, i
 
 
+def quant_dual(gy, x, g_fmt, x_fmt, eps=1e-12):
+    """The operands of the all-FP8 Linear backward ("FP8 Training:
+    Quantization, Autograd, Torchao", section 4: grad_output row-major for the
+    grad-input GEMM and transposed for the grad-weight GEMM, the input
+    column-major): quant_tensor of gy and of x, laid out as
+    gq = q(gy) [M][N], gqT = q(gy)^T [N][M] and xqT = q(x)^T [K][M].
+    Quantization is elementwise under one scale per tensor, so a transposed
+    output is exactly the transpose of the row-major one.
+    Returns (gq, gqT, g_scale, g_inv, xqT, x_scale, x_inv)."""
+    gq, gs, gi = quant_tensor(gy, g_fmt, eps)
+    xq, xs, xi = quant_tensor(x, x_fmt, eps)
+    return gq, np.ascontiguousarray(gq.T), gs, gi, np.ascontiguousarray(xq.T), xs, xi
+
+
 def _brc(x):
     if x.ndim == 2:
         return 1, x.shape[0], x.shape[1]

@@ -52,7 +52,8 @@ def test_linear_tensorwise_forward_fp32(f):
 def test_linear_small_fwd_bwd(f, recipe):
     import torch
     e4, e5 = _names(f)
-    M, K, N = 200, 384, 272
+    # rowwise takes any M; the all-FP8 tensorwise backward needs M % 16 == 0
+    M, K, N = (200 if recipe == "rowwise" else 208), 384, 272
     x = synth.normal_bf16((M, K), 801, 1.0)
     synth.add_outliers(x, 802, 0.01, 50.0)
     wt = synth.normal_bf16((N, K), 803, 0.02)
@@ -83,7 +84,28 @@ def test_linear_small_fwd_bwd(f, recipe):
     S_y = oracle.scaled_mm(qx, e4, qw, e4, sk, ix, iw, absolute=True)
     ref_gx = oracle.scaled_mm(qg, e5, qwt, e4, sk, ig, iwc)
     S_gx = oracle.scaled_mm(qg, e5, qwt, e4, sk, ig, iwc, absolute=True)
-    ref_gw = oracle.wgrad_bf16(gy, x)
-    S_gw = oracle.wgrad_bf16(gy, x, absolute=True)
+    if recipe == "rowwise":
+        ref_gw = oracle.wgrad_bf16(gy, x)
+        S_gw = oracle.wgrad_bf16(gy, x, absolute=True)
+    else:
+        # all-FP8 grad-weight: (q(gy)^T * inv_g) (q(x)^T * inv_x)^T over m
+        _, qgT, _, ig2, qxT, _, ix2 = oracle.quant_dual(gy, x, e5, e4, EPS)
+        ref_gw = oracle.scaled_mm(qgT, e5, qxT, e4, sk, ig2, ix2)
+        S_gw = oracle.scaled_mm(qgT, e5, qxT, e4, sk, ig2, ix2, absolute=True)
     for name, got, ref, S in (("y", y, ref_y, S_y), ("gx", gx, ref_gx, S_gx), ("gw", gw, ref_gw, S_gw)):
         check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}")
+
+
+def test_linear_tensorwise_bwd_needs_m_multiple_of_16(f):
+    """The all-FP8 tensorwise backward contracts over m in FP8 (transposed
+    operands of 16-row groups): M % 16 != 0 is refused before any launch."""
+    import torch
+    M, K, N = 200, 128, 64
+    gy = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda:0")
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda:0")
+    w = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda:0")
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(f.Fp8Error) as e:
+        f.fp8_linear_bwd(gy, x, w, f.RECIPE_TENSORWISE, EPS, gx, gw, _ws(f, M, N, K, f.RECIPE_TENSORWISE))
+    assert e.value.status == f.ERR_ALIGNMENT

@@ -167,6 +167,70 @@ def test_quant_tensor(f, n):
         assert np.array_equal(u8(q), rq) and s.item() == rs[0] and i.item() == ri[0]
 
 
+def _run_dual(f, M, N, K, seed, with_row=True, zero_rows=False):
+    """fp8_quant_dual against the oracle's quant_dual, byte for byte, with
+    guard bands after every output."""
+    import torch
+    e4, e5 = f.fp8_probe(0)
+    name = {0: "e4m3fn", 1: "e4m3fnuz", 2: "e5m2", 3: "e5m2fnuz"}
+    gy = _x((M, N), seed, spread=False)
+    x = _x((M, K), seed + 1, spread=True)
+    if zero_rows:
+        gy[:16] = 0x8000
+        x[:, :8] = 0x0000
+    gq, gq_full = empty_u8((M, N), 256) if with_row else (None, None)
+    gqT, gqT_full = empty_u8((N, M), 256)
+    xqT, xqT_full = empty_u8((K, M), 256)
+    sc = [torch.empty(1, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    ws = torch.full((f.fp8_quant_dual_ws_bytes(),), 0x5A, dtype=torch.uint8, device="cuda:0")
+    f.fp8_quant_dual(to_dev_bf16(gy), to_dev_bf16(x), f.E5M2_NATIVE, f.E4M3_NATIVE, EPS, gq, gqT, sc[0], sc[1],
+                     xqT, sc[2], sc[3], ws)
+    torch.cuda.synchronize()
+    for full in (gq_full, gqT_full, xqT_full):
+        if full is not None:
+            check_guard(full, 256)
+    rgq, rgqT, rgs, rgi, rxqT, rxs, rxi = oracle.quant_dual(gy, x, name[e5], name[e4], EPS)
+    if with_row:
+        assert np.array_equal(u8(gq), rgq), "gq"
+    assert np.array_equal(u8(gqT), rgqT), "gqT"
+    assert np.array_equal(u8(xqT), rxqT), "xqT"
+    got = [t.item() for t in sc]
+    assert got == [rgs[0], rgi[0], rxs[0], rxi[0]], (got, rgs, rgi, rxs, rxi)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 8, 8), (48, 264, 136), (1040, 520, 264), (2048, 1032, 64),
+                                   (3088, 72, 4104)])
+def test_quant_dual(f, M, N, K):
+    """Several 1024-row chunks with a ragged last one, strips narrower than 64
+    columns, and both outputs of gy from one read."""
+    print("dual", M, N, K, flush=True)
+    _run_dual(f, M, N, K, 600 + M % 97)
+
+
+def test_quant_dual_without_row_output_and_zeros(f):
+    _run_dual(f, 64, 128, 96, 611, with_row=False, zero_rows=True)
+
+
+def test_quant_dual_rejects_bad_shapes(f):
+    import torch
+    z = lambda *s: torch.zeros(s, dtype=torch.uint8, device="cuda:0")
+    one = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    ws = z(f.fp8_quant_dual_ws_bytes())
+    for M, N, K, st in [(24, 16, 16, f.ERR_ALIGNMENT), (32, 12, 16, f.ERR_ALIGNMENT), (32, 16, 4, f.ERR_ALIGNMENT)]:
+        gy = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda:0")
+        x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda:0")
+        with pytest.raises(f.Fp8Error) as e:
+            f.fp8_quant_dual(gy, x, f.E5M2_NATIVE, f.E4M3_NATIVE, EPS, z(M, N), z(N, M), one, one, z(K, M), one, one,
+                             ws)
+        assert e.value.status == st, (M, N, K, e.value.status)
+    gy = torch.zeros((32, 16), dtype=torch.bfloat16, device="cuda:0")
+    x = torch.zeros((32, 16), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(f.Fp8Error) as e:
+        f.fp8_quant_dual(gy, x, f.E5M2_NATIVE, f.E4M3_NATIVE, EPS, None, z(16, 32), one, None, z(16, 32), one, None,
+                         None)
+    assert e.value.status == f.ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("br,shape", [(1, (3, 300)), (1, (5, 1024)), (1, (2, 7, 640)), (128, (130, 260)),
                                       (128, (2, 256, 384)), (128, (300, 136))])
 def test_quant_block(f, br, shape):

@@ -113,6 +113,47 @@ def test_linear_rowwise_llama3_8b_mlp(f):
     check_gemm(_gather(gw, r, c), ref, S, True, "linear_rowwise grad-weight bf16 (sampled)")
 
 
+def test_linear_tensorwise_all_fp8_backward_llama3_8b_mlp(f):
+    """The all-FP8 tensorwise backward on the Llama3-8B MLP shapes (the same
+    X, W and grad_out as the rowwise workload): the dual quantization's three
+    outputs bit-exact over the whole tensors, then grad-input and the FP8
+    grad-weight GEMM of the whole fp8_linear_bwd call on sampled positions."""
+    import torch
+    e4, e5 = _names(f)
+    wl = synth.linear_rowwise()
+    x, wt, gy = wl.tensors["x"], wl.tensors["w"], wl.tensors["gy"]
+    M, K, N = x.shape[0], x.shape[1], wt.shape[0]
+    xd, wd, gd = to_dev_bf16(x), to_dev_bf16(wt), to_dev_bf16(gy)
+    u8d = dict(dtype=torch.uint8, device="cuda:0")
+    gq, gqT, xqT = torch.empty((M, N), **u8d), torch.empty((N, M), **u8d), torch.empty((K, M), **u8d)
+    sc = [torch.empty(1, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    ws = torch.empty(f.fp8_quant_dual_ws_bytes(), **u8d)
+    f.fp8_quant_dual(gd, xd, f.E5M2_NATIVE, f.E4M3_NATIVE, EPS, gq, gqT, sc[0], sc[1], xqT, sc[2], sc[3], ws)
+    torch.cuda.synchronize()
+    r_gq, r_gqT, r_gs, r_gi, r_xqT, r_xs, r_xi = oracle.quant_dual(gy, x, e5, e4, EPS)
+    assert np.array_equal(u8(gq), r_gq) and np.array_equal(u8(gqT), r_gqT) and np.array_equal(u8(xqT), r_xqT)
+    assert [t.item() for t in sc] == [r_gs[0], r_gi[0], r_xs[0], r_xi[0]]
+    del gq, gqT, xqT
+    _log("dual quantization bit-exact")
+
+    rc = f.RECIPE_TENSORWISE
+    lws = torch.empty(f.fp8_linear_ws_bytes(M, N, K, rc), **u8d)
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_linear_bwd(gd, xd, wd, rc, EPS, gx, gw, lws)
+    torch.cuda.synchronize()
+    r_qw, _, r_iw = oracle.quant_tensor(wt, e4, EPS)
+    r_qwt = np.ascontiguousarray(r_qw.T)
+    r, c = _samples(M, K, 4)
+    ref = oracle.scaled_mm_sample(r_gq, e5, r_qwt, e4, oracle.SCALE_TENSOR, r_gi, r_iw, r, c)
+    S = oracle.scaled_mm_sample(r_gq, e5, r_qwt, e4, oracle.SCALE_TENSOR, r_gi, r_iw, r, c, absolute=True)
+    check_gemm(_gather(gx, r, c), ref, S, True, "tensorwise grad-input (sampled)")
+    r, c = _samples(N, K, 5)
+    ref = oracle.scaled_mm_sample(r_gqT, e5, r_xqT, e4, oracle.SCALE_TENSOR, r_gi, r_xi, r, c)
+    S = oracle.scaled_mm_sample(r_gqT, e5, r_xqT, e4, oracle.SCALE_TENSOR, r_gi, r_xi, r, c, absolute=True)
+    check_gemm(_gather(gw, r, c), ref, S, True, "tensorwise FP8 grad-weight (sampled)")
+
+
 def test_expert_colwise(f):
     """32 experts x [2048,7168] with 2 zero columns each -> transposed codes + column scales."""
     import torch

@@ -60,6 +60,25 @@ def test_col_block_tensor_mx_bruteforce(fmt):
     assert np.array_equal(q, rq) and s[0] == rs and i[0] == ri
 
 
+@pytest.mark.parametrize("gfmt,xfmt", [("e5m2", "e4m3fn"), ("e5m2fnuz", "e4m3fnuz")])
+def test_dual_bruteforce(gfmt, xfmt):
+    """The all-FP8 backward's operands against the brute-force chain, one
+    tensor scale each: gqT[n][m] is the chain's code of gy[m][n] and xqT[k][m]
+    that of x[m][k] (a transposed orientation or a swapped scale fails)."""
+    gy = _rand_bits((5, 7), 43, spread=True)
+    x = _rand_bits((5, 3), 44, spread=True)
+    gq, gqT, gs, gi, xqT, xs, xi = oracle.quant_dual(gy, x, gfmt, xfmt, EPS)
+    rg, rgs, rgi = pins.quant_chain_reference(gfmt, gy, EPS, oracle.fp8_max(gfmt))
+    rx, rxs, rxi = pins.quant_chain_reference(xfmt, x, EPS, oracle.fp8_max(xfmt))
+    assert gq.shape == (5, 7) and gqT.shape == (7, 5) and xqT.shape == (3, 5)
+    for m in range(5):
+        for n in range(7):
+            assert gq[m, n] == rg[m, n] and gqT[n, m] == rg[m, n]
+        for k in range(3):
+            assert xqT[k, m] == rx[m, k]
+    assert (gs[0], gi[0], xs[0], xi[0]) == (rgs, rgi, rxs, rxi)
+
+
 @pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
 def test_mx_bruteforce(fmt):
     # MX mode 0: power-of-two scale = largest 2^k with amax * 2^k <= fmax
