@@ -11,7 +11,11 @@ already resident in HBM:
                      the FP8 weight-gradient GEMM and the whole fp8_linear_bwd call
   expert_colwise     per-expert column scales + transposed cast, 32 x [2048,7168]
   moe_grouped        rowwise quant of A [131072,7168] and of W [32][2048][7168] (per
-                     expert column), FP8 grouped GEMM over int32[33] offsets -> bf16
+                     expert column), FP8 grouped GEMM over int32[33] offsets -> bf16; beside
+                     it (per row, outside the aggregates) the layer's backward: grad_out
+                     [131072,2048] per-row e5m2, the grouped grad-input GEMM against
+                     expert_colwise's transposed per-column weights, the grouped BF16
+                     grad-weight GEMM over the same offsets
   moe_block_mx       1x128 / 128x128 blockwise and MX quant, 16 experts, K 5120, N 8192,
                      and the blockwise and MX grouped GEMMs
 Every launch is bracketed by HIP events on the stream it runs on. The JSON line
@@ -155,6 +159,23 @@ def build_step(f, torch, dev, wls, dev_of):
            lambda: f.fp8_quant_row(we4, E4, EPS, qw4, sw4, iw4))
     st.add("moe_grouped.grouped_gemm", "gemm8", 2.0 * Mt * N4 * K4,
            lambda: f.fp8_grouped_mm(qa4, E4, qw4, E4, f.SCALE_ROW, ia4, iw4, off4, f.OUT_BF16, out4))
+
+    # ---- the MoE layer's backward on the same routing (outside the
+    # aggregates): grad_out quantized per row (e5m2); grouped grad-input
+    # against the per-expert-column transposed weights expert_colwise wrote
+    # (its W has the layer's [32][2048][7168] shape); grouped BF16
+    # grad-weight over the offsets ----
+    import synth as _synth
+    go4 = dev_of(_synth.normal_bf16((Mt, N4), 4003, 1e-3))
+    qgo4, sgo4, igo4 = torch.empty((Mt, N4), **u8), torch.empty(Mt, **f32), torch.empty(Mt, **f32)
+    gx4 = torch.empty((Mt, K4), **bf)
+    gw4 = torch.empty((E4n, N4, K4), **bf)
+    st.add("moe_backward.quant_row_go_e5m2", "quant_next", 3 * Mt * N4 + 8 * Mt,
+           lambda: f.fp8_quant_row(go4, E5, EPS, qgo4, sgo4, igo4))
+    st.add("moe_backward.grouped_dgrad", "gemm8_next", 2.0 * Mt * N4 * K4,
+           lambda: f.fp8_grouped_mm(qgo4, E5, qt3, E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16, gx4))
+    st.add("moe_backward.grouped_wgrad_bf16", "gemm16_next", 2.0 * Mt * N4 * K4,
+           lambda: f.fp8_grouped_wgrad_bf16(go4, a4, off4, gw4))
 
     # ---- moe_block_mx ----
     w5 = wls["moe_block_mx"]
@@ -355,8 +376,8 @@ def main():
         elif kind == "quant_next":
             r.update(gbs=round(work / avg / 1e9, 1), frac_hbm=round(work / avg / 1e9 / HBM_PEAK_GBS, 4),
                      bytes=int(work))
-        elif kind in ("gemm8", "gemm16", "gemm8_next"):
-            peak = BF16_PEAK_TFLOPS if kind == "gemm16" else FP8_PEAK_TFLOPS
+        elif kind in ("gemm8", "gemm16", "gemm8_next", "gemm16_next"):
+            peak = BF16_PEAK_TFLOPS if kind.startswith("gemm16") else FP8_PEAK_TFLOPS
             r.update(tflops=round(work / avg / 1e12, 1), frac_mfma=round(work / avg / 1e12 / peak, 4),
                      flops=work)
         rows[name] = r

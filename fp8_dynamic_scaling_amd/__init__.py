@@ -27,7 +27,7 @@ EXPORTS = [
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_col",
     "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_quant_block", "fp8_quant_mx",
     "fp8_scaled_mm",
-    "fp8_grouped_mm", "fp8_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
+    "fp8_grouped_mm", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
 ]
 
@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH):
         "fp8_scaled_mm": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
         "fp8_grouped_mm": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, P]),
         "fp8_wgrad_bf16": (I, [P, P, I64, I64, I64, P, P]),
+        "fp8_grouped_wgrad_bf16": (I, [P, P, P, I32, I64, I64, I64, P, P]),
         "fp8_linear_fwd": (I, [P, P, I64, I64, I64, I, D, I, P, P, SZ, P]),
         "fp8_linear_bwd": (I, [P, P, P, I64, I64, I64, I, D, P, P, P, SZ, P]),
         "fp8_linear_ws_bytes": (SZ, [I64, I64, I64, I]),
@@ -212,6 +213,15 @@ def fp8_wgrad_bf16(gy, x, gw, stream=None):
 
 
 # ---- Linear layer -----------------------------------------------------------------
+
+def fp8_grouped_wgrad_bf16(gy, x, offsets, gw, stream=None):
+    """gy [Mtot][N], x [Mtot][K] bf16, offsets device int32 [E+1] -> gw [E][N][K] bf16."""
+    Mtot, N = gy.shape
+    K = x.shape[1]
+    E = offsets.numel() - 1
+    _check("fp8_grouped_wgrad_bf16", load().fp8_grouped_wgrad_bf16(
+        _ptr(gy), _ptr(x), _ptr(offsets), E, Mtot, N, K, _ptr(gw), _stream(stream)))
+
 
 def fp8_linear_ws_bytes(M, N, K, recipe) -> int:
     return load().fp8_linear_ws_bytes(int(M), int(N), int(K), int(recipe))

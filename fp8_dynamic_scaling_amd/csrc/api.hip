@@ -312,6 +312,20 @@ fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int6
   return dev_err(launch_wgrad_bf16(w));
 }
 
+fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t* x, const int32_t* offsets, int32_t E,
+                                  int64_t Mtot, int64_t N, int64_t K, uint16_t* gw, void* stream) {
+  if (E < 0 || Mtot < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
+  if (E == 0 || N == 0 || K == 0) return FP8_OK;
+  if (!gw || !offsets || (Mtot > 0 && (!gy || !x))) return FP8_ERR_INVALID_ARGUMENT;
+  if (N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
+  if ((gy && !aligned(gy, 16)) || (x && !aligned(x, 16)) || !aligned(gw, 4) || !aligned(offsets, 4))
+    return FP8_ERR_ALIGNMENT;
+  // a 32-row stage of either operand addressed with 32-bit offsets
+  if (32 * (N > K ? N : K) * 2 >= ((int64_t)1 << 31)) return FP8_ERR_UNSUPPORTED;
+  GroupedWgradArgs w{gy, x, offsets, E, Mtot, N, K, gw, (hipStream_t)stream};
+  return dev_err(launch_grouped_wgrad_bf16(w));
+}
+
 fp8_status fp8_validate_offsets(const int32_t* host_offsets, int32_t E, int64_t Mtot) {
   if (!host_offsets || E < 1 || Mtot < 0) return FP8_ERR_INVALID_ARGUMENT;
   if (host_offsets[0] != 0 || host_offsets[E] != Mtot) return FP8_ERR_INVALID_ARGUMENT;

@@ -188,8 +188,16 @@ struct WgFrags {
   v8bf a[4][2], b[4][2];  // [32-row block][16-deep k step]
 };
 
+// Grouped form (GR): expert e contracts over its own rows [off[e], off[e+1]):
+// gw[e] = gy[rows]^T x[rows]. Its stages are padded to an even count; loads of
+// rows past the expert's end fetch its last row (a valid address) and the wave
+// that loaded them zeroes those LDS rows after its own loads landed and before
+// the barrier that lets anyone read the stage. An empty expert gets a zero
+// gradient.
+template <bool GR>
 __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restrict__ gy, const uint16_t* __restrict__ x,
-                                                      int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ gw) {
+                                                      const int32_t* __restrict__ offsets, int32_t E, int64_t M,
+                                                      int64_t N, int64_t K, uint16_t* __restrict__ gw) {
   constexpr int BN = 256, BK = 256, MS = 32, NS = 4;
   constexpr int ROWB = 512;                    // bytes per LDS row (256 values)
   constexpr int SG = MS * ROWB, STAGE = 2 * SG;  // gy part, whole stage
@@ -204,8 +212,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tn = (N + BN - 1) / BN, tk = (K + BK - 1) / BK;
-  const int64_t total = tn * tk;
-  const int64_t nk = M / MS;  // even (M % 64 == 0)
+  const int64_t total = tn * tk * (GR ? E : 1);
   const uint32_t lds0 = lds_addr(lds);
   int64_t t_begin, t_end, t_step;
   xcd_range(total, t_begin, t_end, t_step);
@@ -239,8 +246,20 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
         fb[i][ks][h] = (uint32_t)SG + tr_off(wn * TN + 32 * i, ks, h);
       }
 
-  for (int64_t t = t_begin; t < t_end; t += t_step) {
-    // grouped order: 4 row tiles (n), column tiles (k) fastest
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += t_step) {
+    // expert (grouped form), then grouped order over its tiles: 4 row tiles
+    // (n), column tiles (k) fastest
+    int64_t t = t0, m_beg = 0, m_end = M;
+    int32_t e = 0;
+    if constexpr (GR) {
+      e = __builtin_amdgcn_readfirstlane((int32_t)(t0 / (tn * tk)));
+      t = t0 - (int64_t)e * tn * tk;
+      m_beg = offsets[e];
+      m_end = offsets[e + 1];
+    }
+    const int64_t me = m_end - m_beg;
+    // stages of 32 rows (even count: whole steady pairs); dense: M % 64 == 0
+    const int64_t nk = GR ? ((me + 2 * MS - 1) / (2 * MS)) * 2 : M / MS;
     const int64_t g = t / (kGroupM * tk), rem = t % (kGroupM * tk);
     const int64_t gm = (tn - g * kGroupM) < kGroupM ? (tn - g * kGroupM) : kGroupM;
     const int64_t n0 = uniform64((g * kGroupM + rem % gm) * BN), k0 = uniform64((rem / gm) * BK);
@@ -258,9 +277,35 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
 
     auto issue = [&](int64_t s) {
       const uint32_t slot = lds0 + (uint32_t)((s % NS) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
-      const uint8_t* bs = reinterpret_cast<const uint8_t*>(src + s * MS * ld);
+      if (!GR || MS * (s + 1) <= me) {
+        const uint8_t* bs = reinterpret_cast<const uint8_t*>(src + (m_beg + s * MS) * ld);
 #pragma unroll
-      for (int d = 0; d < D; ++d) dma16(bs, off[d], slot + (uint32_t)(d * 1024));
+        for (int d = 0; d < D; ++d) dma16(bs, off[d], slot + (uint32_t)(d * 1024));
+      } else {
+        // the expert ends inside (or before) this stage: rows past its end
+        // load its last row, zeroed later by zero_tail
+        const int64_t r0 = m_beg + s * MS < m_end - 1 ? m_beg + s * MS : m_end - 1;
+        const int32_t rmax = (int32_t)(m_end - 1 - r0);
+        const uint8_t* bs = reinterpret_cast<const uint8_t*>(src + r0 * ld);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int32_t row = 2 * (q0 + d) + (lane >> 5);
+          const int32_t rc = row < rmax ? row : rmax;
+          dma16(bs, off[d] - (uint32_t)((row - rc) * ld * 2), slot + (uint32_t)(d * 1024));
+        }
+      }
+    };
+    // zero this wave's LDS rows of stage s that lie past the expert's end
+    // (after its own loads of the stage landed)
+    auto zero_tail = [&](int64_t s) {
+      if (!GR || MS * (s + 1) <= me) return;
+      uint8_t* slot = lds + (s % NS) * STAGE + opnd_lds + q0 * 1024;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int row = 2 * (q0 + d) + (lane >> 5);
+        if (m_beg + s * MS + row >= m_end)
+          *reinterpret_cast<uint4*>(slot + d * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
     };
     auto read = [&](int64_t s, WgFrags& f) {
       const uint8_t* st = lds + (s % NS) * STAGE;
@@ -312,31 +357,41 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
       read_mma(s + 1, nxt, cur);
     };
 
+    // only the last two stages can hold rows past the expert's end: their
+    // waits are split so each wave zeroes its own such rows in between
     WgFrags f0, f1;
-    if (nk >= NS) {
+    if (!GR || nk > 0) {
+      if (nk >= NS) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) issue(s);
-      wait_vm_and_barrier<(NS - 1) * D>();
-    } else {  // nk == 2
-      issue(0);
-      issue(1);
-      wait_vm_and_barrier<D>();
+        for (int s = 0; s < NS; ++s) issue(s);
+        wait_vm_and_barrier<(NS - 1) * D>();
+      } else {  // nk == 2
+        issue(0);
+        issue(1);
+        wait_vm<D>();
+        zero_tail(0);
+        wait_lgkm_and_barrier();
+      }
+      read(0, f0);
+      for (int64_t s = 0; s + NS < nk; s += 2) {
+        steady(s, f0, f1);
+        steady(s + 1, f1, f0);
+      }
+      if (nk >= NS) {
+        wait_vm_lgkm_and_barrier<2 * D>();
+        read_mma(nk - 3, f1, f0);
+        wait_vm<D>();
+        zero_tail(nk - 2);
+        wait_lgkm_and_barrier();
+        read_mma(nk - 2, f0, f1);
+      }
+      wait_vm<0>();
+      zero_tail(nk - 1);
+      wait_lgkm_and_barrier();
+      read_mma(nk - 1, f1, f0);
+      wait_vm_lgkm_and_barrier<0>();
+      mma(f1);
     }
-    read(0, f0);
-    for (int64_t s = 0; s + NS < nk; s += 2) {
-      steady(s, f0, f1);
-      steady(s + 1, f1, f0);
-    }
-    if (nk >= NS) {
-      wait_vm_lgkm_and_barrier<2 * D>();
-      read_mma(nk - 3, f1, f0);
-      wait_vm_lgkm_and_barrier<D>();
-      read_mma(nk - 2, f0, f1);
-    }
-    wait_vm_lgkm_and_barrier<0>();
-    read_mma(nk - 1, f1, f0);
-    wait_vm_lgkm_and_barrier<0>();
-    mma(f1);
 
     // ---- epilogue: register r of lane l in block (i, j) holds row (n)
     // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column (k) 32 j + l % 32 ----
@@ -350,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t n = n0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (n < N) gw[n * K + k] = f32_to_bf16_rne(acc[i][j][r]);
+          if (n < N) gw[((int64_t)e * N + n) * K + k] = f32_to_bf16_rne(acc[i][j][r]);
         }
     }
   }
@@ -368,7 +423,8 @@ hipError_t launch_wgrad_bf16(const WgradArgs& w) {
     int64_t grid = cus < total ? cus : total;
     if (grid >= kNumXcd) grid -= grid % kNumXcd;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(k_wgrad_pipe, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x, w.M, w.N, w.K, w.gw);
+    hipLaunchKernelGGL(k_wgrad_pipe<false>, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x,
+                       (const int32_t*)nullptr, 1, w.M, w.N, w.K, w.gw);
     return hipGetLastError();
   }
   int64_t grid = cus < total ? cus : total;
@@ -376,6 +432,19 @@ hipError_t launch_wgrad_bf16(const WgradArgs& w) {
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((k_wgrad_bf16<BNT, BKT, 2, 4>), dim3((unsigned)grid), dim3(512), 0, w.stream, w.gy, w.x, w.M, w.N,
                      w.K, w.gw);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_wgrad_bf16(const GroupedWgradArgs& w) {
+  if (w.E == 0 || w.N == 0 || w.K == 0) return hipSuccess;
+  constexpr int BNT = 256, BKT = 256;
+  const int64_t total = (int64_t)w.E * ((w.N + BNT - 1) / BNT) * ((w.K + BKT - 1) / BKT);
+  const int cus = device_cus();
+  int64_t grid = cus < total ? cus : total;
+  if (grid >= kNumXcd) grid -= grid % kNumXcd;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_wgrad_pipe<true>, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x, w.offsets, w.E,
+                     w.Mtot, w.N, w.K, w.gw);
   return hipGetLastError();
 }
 

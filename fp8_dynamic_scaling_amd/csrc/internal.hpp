@@ -85,4 +85,15 @@ struct WgradArgs {
 };
 hipError_t launch_wgrad_bf16(const WgradArgs& w);
 
+struct GroupedWgradArgs {
+  const uint16_t* gy;       // [Mtot][N]
+  const uint16_t* x;        // [Mtot][K]
+  const int32_t* offsets;   // device [E+1]
+  int32_t E;
+  int64_t Mtot, N, K;       // N % 8 == 0, K % 8 == 0, 32 * max(N, K) * 2 < 2^31
+  uint16_t* gw;             // [E][N][K]
+  hipStream_t stream;
+};
+hipError_t launch_grouped_wgrad_bf16(const GroupedWgradArgs& w);
+
 }  // namespace fp8dyn

@@ -222,6 +222,23 @@ FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint
 FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N,
                                      int64_t K, uint16_t* gw, void* stream);
 
+/* Grouped BF16 weight gradient of an MoE layer over device offsets [SURVEY
+ * next step "MoE backward"; "FP8 training on AMD GPUs with TorchTitan and
+ * TorchAO" Figure 1 caption: the weight-update GEMM stays in BF16; section
+ * "Scaling FP8 to MoE Architectures": expert e owns rows [off[e], off[e+1])]:
+ *   gw[e][n][k] = sum over m in [off[e], off[e+1]) of gy[m][n] * x[m][k],
+ * fp32 accumulation, bf16 out (RNE); an expert with no rows gets zeros.
+ * gy [Mtot][N], x [Mtot][K] bf16 row-major (the grouped forward's output
+ * gradient and input, as stored: no transposed copies), gw [E][N][K] bf16.
+ * offsets: device int32[E+1] with offsets[0] == 0, non-decreasing,
+ * offsets[E] == Mtot (check a host copy with fp8_validate_offsets; the
+ * kernel trusts them and never reads them back to the host). N % 8 == 0,
+ * K % 8 == 0, gy and x 16-byte aligned (else FP8_ERR_ALIGNMENT);
+ * 64 * max(N, K) < 2^31 (else FP8_ERR_UNSUPPORTED). */
+FP8DYN_API fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t* x, const int32_t* offsets,
+                                             int32_t E, int64_t Mtot, int64_t N, int64_t K, uint16_t* gw,
+                                             void* stream);
+
 /* ---- one Linear layer [P-TAO section 6; P-AMD "AMD FP8 format in TorchAO"] ---
  * Forward y = x w^T: x [M][K], w [N][K] bf16; quantize both (TENSORWISE: one
  * scale each; ROWWISE: per row of x and of w, e4m3), then the scaled GEMM;

@@ -315,5 +315,23 @@ def wgrad_bf16_sample(g, x, ns, ks, absolute=False):
     return out
 
 
+def grouped_wgrad_bf16(g, x, offsets, threads=0, absolute=False):
+    """The MoE weight gradient over expert row ranges ("FP8 training on AMD
+    GPUs with TorchTitan and TorchAO", section "Scaling FP8 to MoE
+    Architectures": expert e owns rows [off[e], off[e+1]); Figure 1 caption:
+    the weight-update GEMM stays in BF16): gw[e] = wgrad_bf16 of the expert's
+    rows of g and x, zeros for an expert with no rows. Returns [E][N][K] in
+    fp64, before the final bf16 rounding (absolute=True: sums of |products|)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    N, K = g.shape[1], x.shape[1]
+    out = np.zeros((E, N, K), dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            out[e] = wgrad_bf16(np.ascontiguousarray(g[a:b]), np.ascontiguousarray(x[a:b]), threads, absolute)
+    return out
+
+
 def threads_used(threads=0) -> int:
     return int(_load().orc_threads_used(int(threads)))

@@ -238,3 +238,29 @@ def test_wgrad_bf16(f, M, N, K):
     ref = oracle.wgrad_bf16(g, x)
     S = oracle.wgrad_bf16(g, x, absolute=True)
     check_gemm(_host(gw), ref, S, True, f"wgrad {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("counts,N,K", [([37, 0, 300, 1, 0, 513], 264, 136), ([64], 256, 256), ([0, 0], 64, 64),
+                                         ([5] * 40, 64, 512), ([600, 0, 3], 520, 264),
+                                         ([32, 31, 33, 95, 96, 97, 128], 128, 136)])
+def test_grouped_wgrad_bf16(f, counts, N, K):
+    """Expert row ranges shorter than one 32-row stage, on stage boundaries and
+    ragged; empty experts must come out exactly zero."""
+    import torch
+    off = _offsets(counts)
+    E, Mt = len(counts), int(off[-1])
+    g = synth.normal_bf16((max(Mt, 1), N), 900 + E, 1e-3)[:Mt]
+    x = synth.normal_bf16((max(Mt, 1), K), 901 + E, 1.0)[:Mt]
+    gw = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    gd = to_dev_bf16(np.ascontiguousarray(g)) if Mt else torch.empty((0, N), dtype=torch.bfloat16, device="cuda:0")
+    xd = to_dev_bf16(np.ascontiguousarray(x)) if Mt else torch.empty((0, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_wgrad_bf16(gd, xd, to_dev(off), gw)
+    torch.cuda.synchronize()
+    got = gw.float().cpu().numpy()
+    ref = oracle.grouped_wgrad_bf16(g, x, off)
+    S = oracle.grouped_wgrad_bf16(g, x, off, absolute=True)
+    for e, c in enumerate(counts):
+        if c == 0:
+            assert np.all(got[e] == 0.0), f"expert {e} (empty) not zero"
+        else:
+            check_gemm(got[e], ref[e], S[e], True, f"grouped wgrad expert {e} ({c} rows)")

@@ -210,6 +210,59 @@ def test_moe_grouped_forward(f):
     check_gemm(_gather(out, r, c), ref, S, True, "moe_grouped gemm (sampled)")
 
 
+def test_moe_backward(f):
+    """The MoE layer's backward on the same routing and weights: grad_out
+    [131072,2048] ~N(0,1e-3) quantized per row (e5m2); grouped grad-input
+    against the per-expert-column transposed weights (the column kernel on W
+    [32][2048][7168] -> [32][7168][2048]); grouped BF16 grad-weight over the
+    offsets -> [32][2048][7168] (the two empty experts exactly zero)."""
+    import torch
+    e4, e5 = _names(f)
+    wl = synth.moe_grouped()
+    a, w, off = wl.tensors["a"], wl.tensors["w"], wl.meta["offsets"]
+    Mt, K = a.shape
+    E, N, _ = w.shape
+    go = synth.normal_bf16((Mt, N), 4003, 1e-3)
+    ad, wd, gd = to_dev_bf16(a), to_dev_bf16(w), to_dev_bf16(go)
+    offd = to_dev(off)
+    qg = torch.empty((Mt, N), dtype=torch.uint8, device="cuda:0")
+    sg = torch.empty(Mt, dtype=torch.float32, device="cuda:0")
+    ig = torch.empty_like(sg)
+    f.fp8_quant_row(gd, f.E5M2_NATIVE, EPS, qg, sg, ig)
+    qT = torch.empty((E, K, N), dtype=torch.uint8, device="cuda:0")
+    sT = torch.empty((E, K), dtype=torch.float32, device="cuda:0")
+    iT = torch.empty_like(sT)
+    f.fp8_quant_col(wd, f.E4M3_NATIVE, EPS, qT, sT, iT, None)
+    gx = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(qg, f.E5M2_NATIVE, qT, f.E4M3_NATIVE, f.SCALE_ROW, ig, iT, offd, f.OUT_BF16, gx)
+    gw = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_wgrad_bf16(gd, ad, offd, gw)
+    torch.cuda.synchronize()
+    del ad, wd, gd
+    r_qg, _, r_ig = oracle.quant_row(go, e5, EPS)
+    assert np.array_equal(u8(qg), r_qg) and np.array_equal(ig.cpu().numpy(), r_ig)
+    r_qT, _, r_iT = oracle.quant_col(w, e4, EPS)
+    assert np.array_equal(u8(qT), r_qT) and np.array_equal(iT.cpu().numpy(), r_iT)
+    _log("moe backward quantization bit-exact")
+    r, c = _samples(Mt, K, 6, offsets=off)
+    ref = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c)
+    S = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c, absolute=True)
+    check_gemm(_gather(gx, r, c), ref, S, True, "moe grouped grad-input (sampled)")
+    rng = np.random.default_rng(7)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            assert torch.count_nonzero(gw[e]).item() == 0, f"empty expert {e}"
+            continue
+        ns = np.concatenate([rng.integers(0, N, 96), [0, N - 1]])
+        ks = np.concatenate([rng.integers(0, K, 96), [K - 1, 0]])
+        gs, xs = np.ascontiguousarray(go[lo:hi]), np.ascontiguousarray(a[lo:hi])
+        ref = oracle.wgrad_bf16_sample(gs, xs, ns, ks)
+        S = oracle.wgrad_bf16_sample(gs, xs, ns, ks, absolute=True)
+        got = gw[e][torch.from_numpy(ns).cuda(), torch.from_numpy(ks).cuda()].float().cpu().numpy()
+        check_gemm(got.astype(np.float64), ref, S, True, f"moe grouped grad-weight expert {e} (sampled)")
+
+
 def test_moe_block_and_mx(f):
     """16 experts, K 5120, N 8192, 8192 rows (512 per expert), per-row magnitude spread
     2^-8..2^8: 1x128 / 128x128 blockwise and 32-element MX quantization and GEMMs."""

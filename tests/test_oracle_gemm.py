@@ -164,6 +164,27 @@ def test_wgrad_matches_numpy():
     assert np.array_equal(oracle.wgrad_bf16_sample(g, x, ns, ks), out[ns, ks])
 
 
+def test_grouped_wgrad_matches_numpy_per_expert():
+    """Each expert's slice of rows against numpy's fp64 g^T x over exactly those
+    rows (a shifted boundary or a dropped expert fails); an empty expert is 0."""
+    rng = np.random.default_rng(7)
+    counts = [5, 0, 33, 1, 0, 9]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    Mt, N, K = int(off[-1]), 16, 24
+    g = (rng.standard_normal((Mt, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = (rng.standard_normal((Mt, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out = oracle.grouped_wgrad_bf16(g, x, off)
+    gf = oracle.bf16_to_f32(g).astype(np.float64)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    assert out.shape == (len(counts), N, K)
+    for e in range(len(counts)):
+        ref = gf[off[e]:off[e + 1]].T @ xf[off[e]:off[e + 1]]
+        np.testing.assert_allclose(out[e], ref, rtol=1e-12, atol=1e-12)
+    assert not out[1].any() and not out[4].any()
+    S = oracle.grouped_wgrad_bf16(g, x, off, absolute=True)
+    np.testing.assert_allclose(S[2], np.abs(gf[5:38]).T @ np.abs(xf[5:38]), rtol=1e-12)
+
+
 def test_absolute_product_sums():
     """S = sum |a_k b_k| |scales|: equals numpy's |A| @ |B|^T, bounds |ref|, and equals ref
     when every product is non-negative."""
