@@ -317,6 +317,7 @@ fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t* x, const i
   if (E < 0 || Mtot < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
   if (E == 0 || N == 0 || K == 0) return FP8_OK;
   if (!gw || !offsets || (Mtot > 0 && (!gy || !x))) return FP8_ERR_INVALID_ARGUMENT;
+  if (E > 1024) return FP8_ERR_UNSUPPORTED;  // the kernel keeps offsets and costs in LDS
   if (N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
   if ((gy && !aligned(gy, 16)) || (x && !aligned(x, 16)) || !aligned(gw, 4) || !aligned(offsets, 4))
     return FP8_ERR_ALIGNMENT;

@@ -188,6 +188,9 @@ struct WgFrags {
   v8bf a[4][2], b[4][2];  // [32-row block][16-deep k step]
 };
 
+// per-tile cost beyond its stages (prologue, epilogue), in stages
+constexpr int64_t kTileCost = 4;
+
 // Grouped form (GR): expert e contracts over its own rows [off[e], off[e+1]):
 // gw[e] = gy[rows]^T x[rows]. Its stages are padded to an even count; loads of
 // rows past the expert's end fetch its last row (a valid address) and the wave
@@ -206,16 +209,65 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
   static_assert(D == 8, "stage split");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+  // grouped form: offsets and the cumulative cost of the experts' tiles
+  __shared__ int32_t s_off[GR ? kMaxExperts + 1 : 1];
+  __shared__ int64_t s_cum[GR ? kMaxExperts + 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tn = (N + BN - 1) / BN, tk = (K + BK - 1) / BK;
-  const int64_t total = tn * tk * (GR ? E : 1);
   const uint32_t lds0 = lds_addr(lds);
+  // The XCD-aware split of the tile list (xcd_range). Grouped: the tiles of
+  // an expert differ in length (its rows), so the XCDs get contiguous ranges
+  // of equal total cost (stages + kTileCost per tile) rather than of equal
+  // tile counts; within an XCD the workgroups still take neighbouring tiles
+  // together, which share operand rows in that XCD's L2.
+  const int64_t tpe = tn * tk;  // tiles per expert
   int64_t t_begin, t_end, t_step;
-  xcd_range(total, t_begin, t_end, t_step);
+  auto stages_of = [&](int32_t e) -> int64_t {
+    const int64_t me = (int64_t)s_off[e + 1] - s_off[e];
+    return ((me + 2 * MS - 1) / (2 * MS)) * 2;
+  };
+  if constexpr (GR) {
+    for (int i = tid; i <= E; i += 256) s_off[i] = offsets[i];
+    __syncthreads();
+    if (tid == 0) {
+      int64_t acc = 0;
+      for (int32_t e = 0; e < E; ++e) {
+        s_cum[e] = acc;
+        acc += tpe * (stages_of(e) + kTileCost);
+      }
+      s_cum[E] = acc;
+    }
+    __syncthreads();
+    // first tile whose start cost is >= w
+    auto tile_at = [&](int64_t w) -> int64_t {
+      if (w >= s_cum[E]) return (int64_t)E * tpe;
+      int32_t lo = 0, hi = E;  // s_cum[lo] <= w < s_cum[hi]
+      while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) / 2;
+        if (s_cum[mid] <= w) lo = mid; else hi = mid;
+      }
+      const int64_t cost = stages_of(lo) + kTileCost;
+      const int64_t j = (w - s_cum[lo] + cost - 1) / cost;
+      return (int64_t)lo * tpe + j;  // j == tpe is the next expert's first tile
+    };
+    const int64_t G = gridDim.x, W = s_cum[E];
+    if (G % kNumXcd == 0) {
+      const int64_t xcd = blockIdx.x % kNumXcd;
+      t_begin = uniform64(tile_at(W * xcd / kNumXcd) + blockIdx.x / kNumXcd);
+      t_end = uniform64(tile_at(W * (xcd + 1) / kNumXcd));
+      t_step = G / kNumXcd;
+    } else {
+      t_begin = blockIdx.x;
+      t_end = (int64_t)E * tpe;
+      t_step = G;
+    }
+  } else {
+    xcd_range(tpe, t_begin, t_end, t_step);
+  }
 
   // loads: waves 0-1 take gy (16 pieces of 1 KB = 2 rows), waves 2-3 take x;
   // lane i of a piece fills row 2 q + i / 32, physical chunk i % 32
@@ -252,10 +304,10 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
     int64_t t = t0, m_beg = 0, m_end = M;
     int32_t e = 0;
     if constexpr (GR) {
-      e = __builtin_amdgcn_readfirstlane((int32_t)(t0 / (tn * tk)));
-      t = t0 - (int64_t)e * tn * tk;
-      m_beg = offsets[e];
-      m_end = offsets[e + 1];
+      e = __builtin_amdgcn_readfirstlane((int32_t)(t0 / tpe));
+      t = t0 - (int64_t)e * tpe;
+      m_beg = __builtin_amdgcn_readfirstlane(s_off[e]);
+      m_end = __builtin_amdgcn_readfirstlane(s_off[e + 1]);
     }
     const int64_t me = m_end - m_beg;
     // stages of 32 rows (even count: whole steady pairs); dense: M % 64 == 0

@@ -234,7 +234,7 @@ FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int6
  * offsets[E] == Mtot (check a host copy with fp8_validate_offsets; the
  * kernel trusts them and never reads them back to the host). N % 8 == 0,
  * K % 8 == 0, gy and x 16-byte aligned (else FP8_ERR_ALIGNMENT);
- * 64 * max(N, K) < 2^31 (else FP8_ERR_UNSUPPORTED). */
+ * 64 * max(N, K) < 2^31 and E <= 1024 (else FP8_ERR_UNSUPPORTED). */
 FP8DYN_API fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t* x, const int32_t* offsets,
                                              int32_t E, int64_t Mtot, int64_t N, int64_t K, uint16_t* gw,
                                              void* stream);
