@@ -104,6 +104,24 @@ fp8_status resolve(fp8_format f, bool* is_e5, double* fmax) {
   return FP8_OK;
 }
 
+// Quantization outputs that are not consumed by this GPU's matrix cores: the
+// fnuz variants on an OCP device, written by the software encoder (MI300
+// interop). Anything else resolves as above.
+fp8_status resolve_out(fp8_format f, bool* is_e5, double* fmax, bool* fnuz) {
+  *fnuz = false;
+  fp8_status st = resolve(f, is_e5, fmax);
+  if (st != FP8_ERR_UNSUPPORTED || (f != FP8_E4M3FNUZ && f != FP8_E5M2FNUZ)) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8_ERR_DEVICE;
+  fp8_format e4, e5;
+  if ((st = probe_device(dev, &e4, &e5)) != FP8_OK) return st;
+  if (e4 != FP8_E4M3FN || e5 != FP8_E5M2) return FP8_ERR_UNSUPPORTED;
+  *is_e5 = f == FP8_E5M2FNUZ;
+  *fmax = f == FP8_E4M3FNUZ ? 240.0 : 57344.0;
+  *fnuz = true;
+  return FP8_OK;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool bad_eps(double eps) { return !(std::isfinite(eps) && eps > 0.0); }
 
@@ -167,10 +185,10 @@ fp8_status fp8_quant_tensor(const uint16_t* x, int64_t n, fp8_format fmt, double
   if (n == 0) return FP8_OK;
   if (!ws || ws_bytes < fp8_quant_tensor_ws_bytes()) return FP8_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
-  bool e5;
+  bool e5, nz;
   double fm;
-  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
-  QuantArgs a{x, 1, 1, n, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  if ((st = resolve_out(fmt, &e5, &fm, &nz)) != FP8_OK) return st;
+  QuantArgs a{x, 1, 1, n, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream, nz};
   return dev_err(launch_quant_tensor(a, ws));
 }
 
@@ -178,10 +196,10 @@ fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t
                          uint8_t* q, float* scale, float* inv_scale, void* stream) {
   fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
   if (st != FP8_OK || batch * rows * cols == 0) return st;
-  bool e5;
+  bool e5, nz;
   double fm;
-  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
-  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  if ((st = resolve_out(fmt, &e5, &fm, &nz)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream, nz};
   return dev_err(launch_quant_row(a));
 }
 

@@ -110,14 +110,64 @@ __device__ __forceinline__ uint8_t cvt1(float a) {
   return (uint8_t)(w & 0xff);
 }
 
-// Eight bf16 (one 16-byte load) -> eight fp8 bytes.
+// Software encoder for the fnuz variants ("FP8 training on AMD GPUs with
+// TorchTitan and TorchAO", section "AMD FP8 format in TorchAO": finite, no
+// negative zero; e4m3fnuz: exponent bias 8, 3 mantissa bits, max 240; e5m2fnuz:
+// bias 16, 2 mantissa bits, max 57344). gfx950's converts write the OCP
+// encodings, so MI300-readable bytes are produced here from the bits of the
+// clamped fp32 value: round to nearest, ties to even mantissa, including the
+// subnormal band (quantum 2^(1 - bias - mbits)); a value that rounds to zero
+// is 0x00 whatever its sign; 0x80 (NaN) is never written. |y| <= max.
 template <bool E5>
+__device__ __forceinline__ uint32_t enc_fnuz(float y) {
+  constexpr int MB = E5 ? 2 : 3, BIAS = E5 ? 16 : 8;
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t ab = bits & 0x7fffffffu;
+  const int e = (int)(ab >> 23) - 127;  // exponent of |y| (fp32 denormals: far below the fnuz range)
+  uint32_t code;
+  if (e < 1 - BIAS) {
+    // below the smallest normal: q = |y| / 2^(1 - BIAS - MB), rounded to even
+    // (scaling by a power of two is exact; rintf rounds to nearest even)
+    const float q = rintf(__uint_as_float(ab) * __uint_as_float((uint32_t)(127 + BIAS + MB - 1) << 23));
+    code = (uint32_t)q;  // 2^MB here is the smallest normal: the same bits
+  } else {
+    // normal: keep MB of the 23 mantissa bits, round to nearest even
+    constexpr int SH = 23 - MB;
+    const uint32_t mant = ab & 0x7fffffu;
+    uint32_t qm = mant >> SH;
+    const uint32_t rem = mant & ((1u << SH) - 1), half = 1u << (SH - 1);
+    qm += (rem > half || (rem == half && (qm & 1u))) ? 1u : 0u;
+    code = ((uint32_t)(e + BIAS) << MB) + qm;  // a mantissa carry bumps the exponent
+  }
+  return code == 0 ? 0u : (sign | code);
+}
+
+// Four values -> four packed bytes (a in the low byte); NZ: the fnuz bytes.
+template <bool E5, bool NZ>
+__device__ __forceinline__ uint32_t cvt4x(float a, float b, float c, float d) {
+  if constexpr (NZ)
+    return enc_fnuz<E5>(a) | (enc_fnuz<E5>(b) << 8) | (enc_fnuz<E5>(c) << 16) | (enc_fnuz<E5>(d) << 24);
+  else
+    return cvt4<E5>(a, b, c, d);
+}
+
+template <bool E5, bool NZ>
+__device__ __forceinline__ uint8_t cvt1x(float a) {
+  if constexpr (NZ)
+    return (uint8_t)enc_fnuz<E5>(a);
+  else
+    return cvt1<E5>(a);
+}
+
+// Eight bf16 (one 16-byte load) -> eight fp8 bytes.
+template <bool E5, bool NZ = false>
 __device__ __forceinline__ uint2 quant8(const uint4& v, float s, float fm) {
   uint2 r;
-  r.x = cvt4<E5>(clampf(bf16_lo(v.x) * s, fm), clampf(bf16_hi(v.x) * s, fm),
-                 clampf(bf16_lo(v.y) * s, fm), clampf(bf16_hi(v.y) * s, fm));
-  r.y = cvt4<E5>(clampf(bf16_lo(v.z) * s, fm), clampf(bf16_hi(v.z) * s, fm),
-                 clampf(bf16_lo(v.w) * s, fm), clampf(bf16_hi(v.w) * s, fm));
+  r.x = cvt4x<E5, NZ>(clampf(bf16_lo(v.x) * s, fm), clampf(bf16_hi(v.x) * s, fm),
+                      clampf(bf16_lo(v.y) * s, fm), clampf(bf16_hi(v.y) * s, fm));
+  r.y = cvt4x<E5, NZ>(clampf(bf16_lo(v.z) * s, fm), clampf(bf16_hi(v.z) * s, fm),
+                      clampf(bf16_lo(v.w) * s, fm), clampf(bf16_hi(v.w) * s, fm));
   return r;
 }
 

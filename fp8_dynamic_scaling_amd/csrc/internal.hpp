@@ -19,6 +19,7 @@ struct QuantArgs {
   float* scale;
   float* inv;
   hipStream_t stream;
+  bool fnuz = false;  // write the fnuz variant by software encoding (rowwise, tensorwise)
 };
 
 hipError_t launch_quant_row(const QuantArgs& a);

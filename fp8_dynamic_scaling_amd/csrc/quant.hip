@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void k_quant_row_wave(const uint16_t* __restri
 }
 
 // Any row length / alignment: two passes over the row (the second hits cache).
-template <bool E5>
+// NZ: fnuz output bytes (interop with MI300-generation GPUs).
+template <bool E5, bool NZ = false>
 __global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __restrict__ x, int64_t cols,
                                                            uint8_t* __restrict__ q, float* __restrict__ scale,
                                                            float* __restrict__ inv, double fmax, double eps) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __res
   }
   const float fm = (float)fmax;
   for (int64_t c = threadIdx.x; c < cols; c += 256)
-    q[row * cols + c] = cvt1<E5>(clampf(__uint_as_float((uint32_t)xr[c] << 16) * s, fm));
+    q[row * cols + c] = cvt1x<E5, NZ>(clampf(__uint_as_float((uint32_t)xr[c] << 16) * s, fm));
 }
 
 // ---------------------------------------------------------------------------
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const uint16_t* __restrict_
   if (threadIdx.x == 0) atomic_max_relaxed(amax_word, m);
 }
 
-template <bool E5>
+template <bool E5, bool NZ = false>
 __global__ __launch_bounds__(256) void k_cast_tensor(const uint16_t* __restrict__ x, int64_t n,
                                                      const uint32_t* __restrict__ amax_word,
                                                      uint8_t* __restrict__ q, float* __restrict__ scale,
@@ -472,11 +473,11 @@ __global__ __launch_bounds__(256) void k_cast_tensor(const uint16_t* __restrict_
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
     const uint4 v = ld_nt16(x + 8 * i);
-    st_nt8(q + 8 * i, quant8<E5>(v, s, fm));
+    st_nt8(q + 8 * i, quant8<E5, NZ>(v, s, fm));
   }
   if (blockIdx.x == 0)
     for (int64_t i = nvec * 8 + threadIdx.x; i < n; i += 256)
-      q[i] = cvt1<E5>(clampf(__uint_as_float((uint32_t)x[i] << 16) * s, fm));
+      q[i] = cvt1x<E5, NZ>(clampf(__uint_as_float((uint32_t)x[i] << 16) * s, fm));
 }
 
 // ---------------------------------------------------------------------------
@@ -633,6 +634,11 @@ static hipError_t launch_row_t(const QuantArgs& a) {
   if (R == 0 || a.cols == 0) return hipSuccess;
   const bool vec = a.cols % 8 == 0 && aligned16(a.x) && aligned16(a.q);
   dim3 grid((unsigned)R), block(256);
+  if (a.fnuz) {
+    hipLaunchKernelGGL((k_quant_row_generic<E5, true>), grid, block, 0, a.stream, a.x, a.cols, a.q, a.scale, a.inv,
+                       a.fmax, a.eps);
+    return hipGetLastError();
+  }
   // rows up to 4096 elements: one wavefront per row; longer rows: one
   // workgroup per row (measured faster on MI355X for 7168 and 14336)
   if (vec && a.cols <= 512 * 8) {
@@ -749,6 +755,10 @@ static hipError_t launch_tensor_t(const QuantArgs& a, uint32_t* amax_word) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_clear_words, dim3(1), dim3(64), 0, a.stream, amax_word, (int64_t)1);
   hipLaunchKernelGGL(k_amax_tensor, dim3((unsigned)amax_blocks(nvec)), dim3(256), 0, a.stream, a.x, n, amax_word);
+  if (a.fnuz)
+    hipLaunchKernelGGL((k_cast_tensor<E5, true>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n,
+                       (const uint32_t*)amax_word, a.q, a.scale, a.inv, a.fmax, a.eps);
+  else
   hipLaunchKernelGGL((k_cast_tensor<E5>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, n,
                      (const uint32_t*)amax_word, a.q, a.scale, a.inv, a.fmax, a.eps);
   return hipGetLastError();

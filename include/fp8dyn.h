@@ -119,9 +119,14 @@ FP8DYN_API double fp8_format_max(fp8_format f);
  * Per group g: amax = max |x| (fp32); s = fp8_max / max(amax, eps) in fp64;
  * scale[g] = (float)s; inv_scale[g] = (float)(1/s);
  * q = RNE-encode(clamp((float)x * scale[g], -fp8_max, fp8_max)).
- * Formats: the two NATIVE variants (after fp8_probe) are supported on gfx950;
- * the others return FP8_ERR_UNSUPPORTED. Each call is one pass over x except
- * where stated. */
+ * Formats: the two NATIVE variants (after fp8_probe) are supported by every
+ * call. fp8_quant_tensor and fp8_quant_row also write FP8_E4M3FNUZ and
+ * FP8_E5M2FNUZ on an OCP device (gfx950) for MI300-generation interop [P-AMD
+ * "AMD FP8 format in TorchAO": the fnuz variants, max 240 / 57344, no
+ * negative zero]: a software encoder, not the hardware converts, so slower;
+ * those bytes are for storage or export, no GEMM here reads them. Other
+ * non-native requests return FP8_ERR_UNSUPPORTED. Each call is one pass over
+ * x except where stated. */
 
 /* One scale for all n elements. Needs a device workspace of
  * fp8_quant_tensor_ws_bytes() bytes (ws, 256-byte aligned); its content on

@@ -167,6 +167,94 @@ def test_quant_tensor(f, n):
         assert np.array_equal(u8(q), rq) and s.item() == rs[0] and i.item() == ri[0]
 
 
+@pytest.mark.parametrize("shape", [(5, 300), (3, 4096), (2, 3, 136)])
+def test_quant_row_fnuz_interop(f, shape):
+    """fnuz bytes written by the software encoder on an OCP device, against the
+    oracle's fnuz encoder (rows with outliers, zeros and negative zeros)."""
+    import torch
+    e4, e5 = f.fp8_probe(0)
+    if (e4, e5) != (f.E4M3FN, f.E5M2):
+        pytest.skip("fnuz is this device's native encoding")
+    x = _x(shape, 700 + shape[-1])
+    flat = x.reshape(-1, shape[-1])
+    flat[0, :5] = 0x8000
+    flat[-1, :] = 0x0000
+    for fmt, name in [(f.E4M3FNUZ, "e4m3fnuz"), (f.E5M2FNUZ, "e5m2fnuz")]:
+        q, full = empty_u8(x.shape, 256)
+        s = torch.empty(x.shape[:-1], dtype=torch.float32, device="cuda:0")
+        i = torch.empty(x.shape[:-1], dtype=torch.float32, device="cuda:0")
+        f.fp8_quant_row(to_dev_bf16(x), fmt, EPS, q, s, i)
+        torch.cuda.synchronize()
+        check_guard(full, 256)
+        rq, rs, ri = oracle.quant_row(x, name, EPS)
+        got = u8(q)
+        bad = np.nonzero(got != rq)
+        assert bad[0].size == 0, (name, [b[:5] for b in bad], got[bad][:8], rq[bad][:8])
+        assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+        assert not np.any(got == 0x80), "fnuz NaN code written"
+
+
+@pytest.mark.parametrize("n", [7, 262144, 3_000_017])
+def test_quant_tensor_fnuz_interop(f, n):
+    import torch
+    e4, e5 = f.fp8_probe(0)
+    if (e4, e5) != (f.E4M3FN, f.E5M2):
+        pytest.skip("fnuz is this device's native encoding")
+    x = _x((n,), 710 + n % 97, spread=False)
+    for fmt, name in [(f.E4M3FNUZ, "e4m3fnuz"), (f.E5M2FNUZ, "e5m2fnuz")]:
+        q, full = empty_u8((n,), 256)
+        s = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        i = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        ws = torch.empty((f.fp8_quant_tensor_ws_bytes(),), dtype=torch.uint8, device="cuda:0")
+        f.fp8_quant_tensor(to_dev_bf16(x), fmt, EPS, q, s, i, ws)
+        torch.cuda.synchronize()
+        check_guard(full, 256)
+        rq, rs, ri = oracle.quant_tensor(x, name, EPS)
+        assert np.array_equal(u8(q), rq) and s.item() == rs[0] and i.item() == ri[0], name
+
+
+def test_fnuz_every_representable_value(f):
+    """Every bf16 pattern whose magnitude is within the fnuz range, through the
+    row kernel with a unit scale (amax pinned to fnuz max): the software encoder
+    against the oracle's, over the whole subnormal band, all binades and ties."""
+    import torch
+    e4, e5 = f.fp8_probe(0)
+    if (e4, e5) != (f.E4M3FN, f.E5M2):
+        pytest.skip("fnuz is this device's native encoding")
+    for fmt, name in [(f.E4M3FNUZ, "e4m3fnuz"), (f.E5M2FNUZ, "e5m2fnuz")]:
+        fm = oracle.fp8_max(name)
+        bits = np.arange(65536, dtype=np.uint32)
+        v = (bits << 16).view(np.float32)
+        v = v[np.isfinite(v) & (np.abs(v) <= fm)]
+        n = (v.size + 1022) // 1023 * 1023
+        body = np.concatenate([v, np.zeros(n - v.size, np.float32)]).reshape(-1, 1023)
+        rows = np.concatenate([body, np.full((body.shape[0], 1), fm, np.float32)], axis=1)
+        xb = (rows.view(np.uint32) >> 16).astype(np.uint16)
+        q = torch.empty(xb.shape, dtype=torch.uint8, device="cuda:0")
+        s = torch.empty(xb.shape[0], dtype=torch.float32, device="cuda:0")
+        f.fp8_quant_row(to_dev_bf16(xb), fmt, EPS, q, s)
+        torch.cuda.synchronize()
+        assert np.all(s.cpu().numpy() == 1.0)
+        ref = oracle.encode(name, rows)
+        got = u8(q)
+        bad = np.nonzero(got != ref)
+        assert bad[0].size == 0, (name, rows[bad][:8], got[bad][:8], ref[bad][:8])
+
+
+def test_fnuz_rejected_where_no_encoder(f):
+    """Only the rowwise and tensorwise calls write fnuz on an OCP device."""
+    import torch
+    e4, e5 = f.fp8_probe(0)
+    if (e4, e5) != (f.E4M3FN, f.E5M2):
+        pytest.skip("fnuz is this device's native encoding")
+    x = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda:0")
+    q = torch.empty((64, 16), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty(64, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(f.Fp8Error) as e:
+        f.fp8_quant_col(x, f.E4M3FNUZ, EPS, q, s, None, None)
+    assert e.value.status == f.ERR_UNSUPPORTED
+
+
 def _run_dual(f, M, N, K, seed, with_row=True, zero_rows=False):
     """fp8_quant_dual against the oracle's quant_dual, byte for byte, with
     guard bands after every output."""
