@@ -118,6 +118,25 @@ def build_step(f, torch, dev, wls, dev_of):
     st.add("linear_rowwise.wgrad_bf16", "gemm16", 2.0 * M * N * K,
            lambda: f.fp8_wgrad_bf16(g2, x2, gw2))
 
+    # ---- the norm that produces X, fused with its rowwise quantization,
+    # against the unfused pair (outside the aggregates) ----
+    import numpy as np
+    import synth as _synth
+    # RMSNorm weights 1 + N(0, 0.1), truncated to bf16
+    gn = _synth.normal_bf16((1, K), 2004, 0.1).reshape(K)
+    gn32 = (gn.astype(np.uint32) << 16).view(np.float32) + np.float32(1.0)
+    gnd = dev_of((gn32.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    yn = torch.empty((M, K), **bf)
+    qn, sn, in_ = torch.empty((M, K), **u8), torch.empty(M, **f32), torch.empty(M, **f32)
+    st.add("norm_quant.unfused_rmsnorm", "quant_next", 4 * M * K,
+           lambda: f.fp8_norm_quant_row(x2, gnd, None, f.NORM_RMS, 1e-5, E4, EPS, yn, None, None))
+    st.add("norm_quant.unfused_quant_row", "quant_next", 3 * M * K + 8 * M,
+           lambda: f.fp8_quant_row(yn, E4, EPS, qn, sn, in_))
+    st.add("norm_quant.fused_y_and_q", "quant_next", 5 * M * K + 8 * M,
+           lambda: f.fp8_norm_quant_row(x2, gnd, None, f.NORM_RMS, 1e-5, E4, EPS, yn, qn, sn, in_))
+    st.add("norm_quant.fused_q_only", "quant_next", 3 * M * K + 8 * M,
+           lambda: f.fp8_norm_quant_row(x2, gnd, None, f.NORM_RMS, 1e-5, E4, EPS, None, qn, sn, in_))
+
     # ---- the all-FP8 tensorwise backward of the same layer (beside the
     # rowwise recipe; not part of the aggregate figures) ----
     gqb, gqTb, xqTb = torch.empty((M, N), **u8), torch.empty((N, M), **u8), torch.empty((K, M), **u8)

@@ -25,7 +25,8 @@ RECIPE_TENSORWISE, RECIPE_ROWWISE_BF16_WGRAD = range(2)
 EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_col",
-    "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_quant_block", "fp8_quant_mx",
+    "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
+    "fp8_quant_block", "fp8_quant_mx",
     "fp8_scaled_mm",
     "fp8_grouped_mm", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
@@ -64,6 +65,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
         "fp8_quant_dual": (I, [P, P, I64, I64, I64, I, I, D, P, P, P, P, P, P, P, P, SZ, P]),
+        "fp8_norm_quant_row": (I, [P, P, P, I64, I64, I, D, I, D, P, P, P, P, P]),
         "fp8_quant_dual_ws_bytes": (SZ, []),
         "fp8_quant_block": (I, [P, I64, I64, I64, I, I, I, D, P, P, P, P]),
         "fp8_quant_mx": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
@@ -159,6 +161,17 @@ def fp8_quant_col(x, fmt, eps, qT, scale, inv_scale=None, ws=None, stream=None):
     _check("fp8_quant_col", load().fp8_quant_col(
         _ptr(x), b, r, c, int(fmt), float(eps), _ptr(qT), _ptr(scale), _ptr(inv_scale),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+NORM_RMS, NORM_LAYER = 0, 1
+
+
+def fp8_norm_quant_row(x, gamma, beta, kind, norm_eps, fmt, eps, y, q, scale, inv_scale=None, stream=None):
+    """x [rows][cols] bf16 -> y (bf16, or None), q/scale/inv (rowwise FP8 of y, or q None)."""
+    rows, cols = x.shape
+    _check("fp8_norm_quant_row", load().fp8_norm_quant_row(
+        _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, int(kind), float(norm_eps), int(fmt), float(eps),
+        _ptr(y), _ptr(q), _ptr(scale), _ptr(inv_scale), _stream(stream)))
 
 
 def fp8_quant_dual_ws_bytes() -> int:

@@ -220,6 +220,29 @@ fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   return dev_err(launch_quant_col(a, ws));
 }
 
+fp8_status fp8_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
+                              int64_t cols, fp8_norm kind, double norm_eps, fp8_format fmt, double eps, uint16_t* y,
+                              uint8_t* q, float* scale, float* inv_scale, void* stream) {
+  if (rows < 0 || cols < 0 || bad_eps(eps) || !(std::isfinite(norm_eps) && norm_eps >= 0.0))
+    return FP8_ERR_INVALID_ARGUMENT;
+  if (kind != FP8_NORM_RMS && kind != FP8_NORM_LAYER) return FP8_ERR_INVALID_ARGUMENT;
+  if (kind == FP8_NORM_RMS && beta) return FP8_ERR_INVALID_ARGUMENT;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !gamma || (!y && !q) || (q && !scale)) return FP8_ERR_INVALID_ARGUMENT;
+  if (cols % 8 != 0) return FP8_ERR_ALIGNMENT;
+  if (cols > 16384) return FP8_ERR_UNSUPPORTED;  // the row lives in registers
+  if (!aligned(x, 16) || !aligned(gamma, 16) || (beta && !aligned(beta, 16)) || (y && !aligned(y, 16)) ||
+      (q && !aligned(q, 8)) || (scale && !aligned(scale, 4)) || (inv_scale && !aligned(inv_scale, 4)))
+    return FP8_ERR_ALIGNMENT;
+  bool e5;
+  double fm;
+  fp8_status st;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  NormQuantArgs a{x, gamma, beta, rows, cols, kind == FP8_NORM_LAYER, norm_eps, e5, fm, eps, y, q, scale, inv_scale,
+                  (hipStream_t)stream};
+  return dev_err(launch_norm_quant_row(a));
+}
+
 size_t fp8_quant_dual_ws_bytes(void) { return 256; }
 
 fp8_status fp8_quant_dual(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N, int64_t K, fp8_format g_fmt,

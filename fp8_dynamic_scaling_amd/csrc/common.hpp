@@ -82,6 +82,13 @@ __device__ __forceinline__ float exp2i(int k) {  // 2^k for k in [-126, 127]
   return __uint_as_float((uint32_t)(k + 127) << 23);
 }
 
+// fp32 -> bf16 bits, round to nearest, ties to even (finite values).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 __device__ __forceinline__ float clampf(float y, float fm) { return fminf(fmaxf(y, -fm), fm); }
 
 // Hardware convert of four fp32 values to four fp8 bytes (round to nearest

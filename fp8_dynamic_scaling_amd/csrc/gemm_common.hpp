@@ -25,12 +25,6 @@ struct GemmParams {
   void* out;
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // Tile bookkeeping shared by the workgroup.
 struct TileInfo {
   int64_t m0, m_end, n0;

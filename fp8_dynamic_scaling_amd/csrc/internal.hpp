@@ -29,6 +29,24 @@ hipError_t launch_quant_tensor(const QuantArgs& a, void* ws);  // ws >= 256 byte
 // tensorwise scale, transposed output qT[b][c][r]; needs cols % 8 == 0, rows % 16 == 0
 hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws);
 hipError_t launch_quant_block(const QuantArgs& a, int block_rows, int block_cols);
+// Row normalization fused with the rowwise quantization of its bf16 output.
+struct NormQuantArgs {
+  const uint16_t* x;      // [rows][cols], cols % 8 == 0, cols <= 16384, 16-byte aligned
+  const uint16_t* gamma;  // [cols]
+  const uint16_t* beta;   // [cols] or nullptr (LayerNorm)
+  int64_t rows, cols;
+  bool layer;             // LayerNorm (else RMSNorm)
+  double norm_eps;
+  bool e5;
+  double fmax, eps;
+  uint16_t* y;            // [rows][cols] bf16 or nullptr
+  uint8_t* q;             // [rows][cols] or nullptr (then y only)
+  float* scale;
+  float* inv;
+  hipStream_t stream;
+};
+hipError_t launch_norm_quant_row(const NormQuantArgs& a);
+
 // Tensorwise quantization of up to kMaxTJobs tensors in three launches (clear
 // the amax words, amax of every tensor, one cast launch): each tensor gets its
 // transposed output qT [cols][rows] and, when q is set, its row-major output

@@ -924,6 +924,160 @@ hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Normalization fused with the rowwise quantization of its output ("FP8
+// Training: Quantization, Autograd, Torchao", section 8: the norm's output
+// write and the next layer's amax pass become one memory pass). One
+// 256-thread workgroup per row; the row stays in registers from the load to
+// the FP8 store, so x is read once and y (bf16) is written only if asked.
+//  1. s1 = sum x, s2 = sum x^2 in fp64 (every bf16 value and square is exact
+//     in fp64, so while the row's sums fit in 53 bits they are exact in any
+//     order; s2 accumulates with fused multiply-adds, which round like the
+//     separate add because the product is exact);
+//  2. mean, mean square, var (LayerNorm) and rstd = 1 / sqrt(var + norm_eps):
+//     fp64 IEEE operations (no contraction);
+//  3. y = ((x - mean32) * rstd32) * gamma + beta (LayerNorm) or
+//     (x * rstd32) * gamma (RMSNorm), fp32 IEEE operations, stored as bf16
+//     (RNE);
+//  4. amax of the bf16 row, scale, clamp and cast as in k_quant_row.
+template <int TPR, int J, bool E5, bool LAYER>
+__global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ gamma,
+                                                        const uint16_t* __restrict__ beta, int64_t rows, int64_t cols,
+                                                        double norm_eps, uint16_t* __restrict__ y,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                        float* __restrict__ inv, double fmax, double eps) {
+  // TPR threads per row: 64 (one wavefront per row, 4 rows per workgroup, no
+  // LDS and no barrier) for rows up to 4096 elements, else 256
+  static_assert(TPR == 64 || TPR == 256, "threads per row");
+  __shared__ double red_d[2][4];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int t = TPR == 64 ? (tid & 63) : tid;
+  const int64_t row = TPR == 64 ? (int64_t)blockIdx.x * 4 + (tid >> 6) : (int64_t)blockIdx.x;
+  if (TPR == 64 && row >= rows) return;
+  const uint16_t* xr = x + row * cols;
+  uint4 v[J];
+  double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = 8 * (t + TPR * j);
+    v[j] = c < cols ? ld_nt16(xr + c) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
+      if constexpr (LAYER) s1 = __dadd_rn(__dadd_rn(s1, lo), hi);
+      // x * x is exact in fp64, so the fused multiply-add rounds exactly as
+      // s2 + x * x does, with one fp64 operation instead of two
+      s2 = __fma_rn(hi, hi, __fma_rn(lo, lo, s2));
+    }
+  }
+  // row sums (fp64): the wavefront, then (256 threads per row) the 4 waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    if constexpr (LAYER) s1 = __dadd_rn(s1, __shfl_xor(s1, o, 64));
+    s2 = __dadd_rn(s2, __shfl_xor(s2, o, 64));
+  }
+  if constexpr (TPR == 256) {
+    if ((tid & 63) == 0) {
+      red_d[0][tid >> 6] = s1;
+      red_d[1][tid >> 6] = s2;
+    }
+    __syncthreads();
+    s1 = __dadd_rn(__dadd_rn(red_d[0][0], red_d[0][1]), __dadd_rn(red_d[0][2], red_d[0][3]));
+    s2 = __dadd_rn(__dadd_rn(red_d[1][0], red_d[1][1]), __dadd_rn(red_d[1][2], red_d[1][3]));
+  }
+  const double n = (double)cols;
+  const double mean = __ddiv_rn(s1, n), ms = __ddiv_rn(s2, n);
+  const double var = LAYER ? __dsub_rn(ms, __dmul_rn(mean, mean)) : ms;
+  const double rstd = __ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(var, norm_eps)));
+  const float mean32 = __double2float_rn(mean), rstd32 = __double2float_rn(rstd);
+  // normalize, keep as bf16 in registers (and store to y)
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = 8 * (t + TPR * j);
+    if (c >= cols) continue;
+    const uint4 gv = *reinterpret_cast<const uint4*>(gamma + c);
+    const uint4 bv = LAYER && beta ? *reinterpret_cast<const uint4*>(beta + c) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float t0, t1;
+      if constexpr (LAYER) {
+        t0 = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(bf16_lo(w[k]), mean32), rstd32), bf16_lo(gw[k])),
+                       bf16_lo(bw[k]));
+        t1 = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(bf16_hi(w[k]), mean32), rstd32), bf16_hi(gw[k])),
+                       bf16_hi(bw[k]));
+      } else {
+        t0 = __fmul_rn(__fmul_rn(bf16_lo(w[k]), rstd32), bf16_lo(gw[k]));
+        t1 = __fmul_rn(__fmul_rn(bf16_hi(w[k]), rstd32), bf16_hi(gw[k]));
+      }
+      o[k] = (uint32_t)f32_to_bf16_rne(t0) | ((uint32_t)f32_to_bf16_rne(t1) << 16);
+    }
+    v[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    m = amax8(v[j], m);
+    if (y) *reinterpret_cast<uint4*>(y + row * cols + c) = v[j];
+  }
+  if (!q) return;
+  if constexpr (TPR == 64)
+    m = wave_max(m);
+  else
+    m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (t == 0) {
+    scale[row] = s;
+    if (inv) inv[row] = iv;
+  }
+  const float fm = (float)fmax;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = 8 * (t + TPR * j);
+    if (c < cols) st_nt8(q + row * cols + c, quant8<E5>(v[j], s, fm));
+  }
+}
+
+template <bool E5, bool LAYER>
+static void launch_norm_quant_t(const NormQuantArgs& a) {
+  const dim3 block(256);
+  auto go = [&](auto kern, int64_t blocks) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), block, 0, a.stream, a.x, a.gamma, a.beta, a.rows, a.cols,
+                       a.norm_eps, a.y, a.q, a.scale, a.inv, a.fmax, a.eps);
+  };
+  if (a.cols <= 512 * 8) {  // one wavefront per row
+    const int64_t J = (a.cols + 511) / 512, blocks = (a.rows + 3) / 4;
+    if (J <= 2)
+      go(k_norm_quant_row<64, 2, E5, LAYER>, blocks);
+    else if (J <= 4)
+      go(k_norm_quant_row<64, 4, E5, LAYER>, blocks);
+    else
+      go(k_norm_quant_row<64, 8, E5, LAYER>, blocks);
+  } else {
+    const int64_t J = (a.cols + 2047) / 2048;
+    if (J <= 4)
+      go(k_norm_quant_row<256, 4, E5, LAYER>, a.rows);
+    else
+      go(k_norm_quant_row<256, 8, E5, LAYER>, a.rows);
+  }
+}
+
+hipError_t launch_norm_quant_row(const NormQuantArgs& a) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.layer)
+    a.e5 ? launch_norm_quant_t<true, true>(a) : launch_norm_quant_t<false, true>(a);
+  else
+    a.e5 ? launch_norm_quant_t<true, false>(a) : launch_norm_quant_t<false, false>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_tensor(const QuantArgs& a, void* ws) {
   return a.e5 ? launch_tensor_t<true>(a, (uint32_t*)ws) : launch_tensor_t<false>(a, (uint32_t*)ws);
 }

@@ -95,6 +95,11 @@ typedef enum {
 } fp8_mx_mode;
 
 typedef enum {
+    FP8_NORM_RMS = 0,   /* y = x / sqrt(mean(x^2) + norm_eps) * gamma */
+    FP8_NORM_LAYER = 1  /* y = (x - mean) / sqrt(var + norm_eps) * gamma + beta */
+} fp8_norm;
+
+typedef enum {
     FP8_RECIPE_TENSORWISE = 0,        /* one scale per tensor, all GEMMs FP8 */
     FP8_RECIPE_ROWWISE_BF16_WGRAD = 1 /* rowwise FP8 forward and grad-input; BF16 grad-weight */
 } fp8_recipe;
@@ -153,6 +158,25 @@ FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t ro
                                     fp8_format fmt, double eps, uint8_t* qT, float* scale,
                                     float* inv_scale, void* ws, size_t ws_bytes, void* stream);
 FP8DYN_API size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/* Normalization fused with the rowwise quantization of its output ["FP8
+ * Training: Quantization, Autograd, Torchao" section 8: the norm's output
+ * write and the next layer's amax pass as one memory pass]. Per row of x
+ * [rows][cols] bf16: the row statistics in fp64 (sums of x and x^2; mean,
+ * var = E[x^2] - mean^2 for LAYER, rstd = 1/sqrt(var + norm_eps)), then
+ *   y = ((x - mean32) * rstd32) * gamma + beta   (LAYER; beta may be NULL = 0)
+ *   y = (x * rstd32) * gamma                     (RMS; beta must be NULL)
+ * in fp32 IEEE operations on mean32 = (float)mean, rstd32 = (float)rstd,
+ * stored as bf16 (RNE): the activation an unfused norm would write. q, scale,
+ * inv_scale are then exactly fp8_quant_row of that bf16 row. x is read once;
+ * y [rows][cols] is written only if non-NULL (the backward's copy); q may be
+ * NULL (normalization only). gamma, beta [cols] bf16. cols % 8 == 0 (else
+ * FP8_ERR_ALIGNMENT), cols <= 16384 (else FP8_ERR_UNSUPPORTED); x, gamma,
+ * beta, y 16-byte aligned, q 8-byte aligned. NATIVE formats only. */
+FP8DYN_API fp8_status fp8_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta,
+                                         int64_t rows, int64_t cols, fp8_norm kind, double norm_eps,
+                                         fp8_format fmt, double eps, uint16_t* y, uint8_t* q, float* scale,
+                                         float* inv_scale, void* stream);
 
 /* Dual tensorwise quantization for the all-FP8 Linear backward ["FP8
  * Training: Quantization, Autograd, Torchao" section 4: grad_weight =

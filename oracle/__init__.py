@@ -18,7 +18,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_SOURCES = ["codec.c", "quant.c", "gemm.c"]
+_SOURCES = ["codec.c", "quant.c", "gemm.c", "norm.c"]
 
 E4M3FN, E4M3FNUZ, E5M2, E5M2FNUZ = 0, 1, 2, 3
 FORMATS = {"e4m3fn": E4M3FN, "e4m3fnuz": E4M3FNUZ, "e5m2": E5M2, "e5m2fnuz": E5M2FNUZ}
@@ -64,6 +64,8 @@ def _load():
         "orc_quant_elem": (U8, [I, ctypes.c_uint16, F]),
         "orc_quant_tensor": (None, [P, I64, I, D, P, P, P, P]),
         "orc_quant_row": (None, [P, I64, I64, I64, I, D, P, P, P, I]),
+        "orc_norm_row": (None, [P, P, P, I64, I64, I, D, P]),
+        "orc_norm_quant_row": (None, [P, P, P, I64, I64, I, D, I, D, P, P, P, P]),
         "orc_quant_col": (None, [P, I64, I64, I64, I, D, P, P, P, I]),
         "orc_quant_block": (None, [P, I64, I64, I64, I64, I64, I, D, P, P, P, I]),
         "orc_quant_mx": (None, [P, I64, I64, I64, I, I, D, P, P, I]),
@@ -160,6 +162,27 @@ def quant_tensor(x, fmt, eps=1e-12):
     a = np.empty(1, np.float32)
     _load().orc_quant_tensor(_p(x), x.size, _fmt(fmt), float(eps), _p(q), _p(s), _p(i), _p(a))
     return q, s, i
+
+
+def norm_row(x, gamma, beta=None, layer=False, norm_eps=1e-6):
+    """RMSNorm (layer=False) or LayerNorm of each row of x, stored as bf16
+    (see norm.c for the steps). x [rows][cols], gamma/beta [cols] bf16 bits."""
+    x, g = _u16(x), _u16(gamma)
+    b = _u16(beta) if beta is not None else None
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.uint16)
+    _load().orc_norm_row(_p(x), _p(g), _p(b), rows, cols, int(bool(layer)), float(norm_eps), _p(y))
+    return y
+
+
+def norm_quant_row(x, gamma, beta=None, layer=False, norm_eps=1e-6, fmt="e4m3fn", eps=1e-12):
+    """The normalization, then quant_row of its bf16 output ("FP8 Training:
+    Quantization, Autograd, Torchao", section 8: the norm's output write and
+    the next layer's amax pass are one memory pass when fused).
+    Returns (y, q, scale, inv)."""
+    y = norm_row(x, gamma, beta, layer, norm_eps)
+    q, s, i = quant_row(y, fmt, eps)
+    return y, q, s, i
 
 
 def quant_dual(gy, x, g_fmt, x_fmt, eps=1e-12):

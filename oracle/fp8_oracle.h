@@ -94,6 +94,16 @@ void orc_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64_t col
 void orc_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                   int fmt, int mode, double eps, uint8_t* q, uint8_t* e8m0, int threads);
 
+/* ---- normalization, then rowwise quantization (norm.c) ---------------------
+ * x [rows][cols] bf16, gamma [cols] and beta [cols] (LayerNorm, may be NULL)
+ * bf16; layer: 1 LayerNorm, 0 RMSNorm. y [rows][cols] bf16 (the normalized
+ * activation); q/scale/inv as orc_quant_row of y. */
+void orc_norm_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
+                  int64_t cols, int layer, double norm_eps, uint16_t* y);
+void orc_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
+                        int64_t cols, int layer, double norm_eps, int fmt, double eps, uint16_t* y,
+                        uint8_t* q, float* scale, float* inv);
+
 /* ---- GEMMs in fp64 (results unrounded) -------------------------------------
  * a: [M][K] codes (row-major), b: [N][K] codes (the column-major K x N operand).
  * out[m][n] = inv_a * inv_b * sum_k dec(a[m][k]) * dec(b[n][k]).

@@ -255,6 +255,68 @@ def test_fnuz_rejected_where_no_encoder(f):
     assert e.value.status == f.ERR_UNSUPPORTED
 
 
+def _gamma(cols, seed, layer):
+    g = synth.normal_bf16((1, cols), seed, 0.1).reshape(cols)
+    g = oracle.bf16_to_f32(g) + 1.0  # weights near 1, as trained norms hold
+    gb = (g.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    b = synth.normal_bf16((1, cols), seed + 1, 0.1).reshape(cols) if layer else None
+    return gb, b
+
+
+@pytest.mark.parametrize("shape", [(3, 8), (7, 1016), (5, 4096), (4, 7168), (2, 16384), (33, 2056)])
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_quant_row(f, shape, kind):
+    """The fused normalization + rowwise quantization: the bf16 activation, the
+    codes and the scales equal the oracle's (norm, then quant_row), bit for bit."""
+    import torch
+    rows, cols = shape
+    layer = kind == "layer"
+    x = _x(shape, 800 + cols)
+    g, b = _gamma(cols, 810 + cols, layer)
+    for fmt, name in _natives(f):
+        y = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+        q, full = empty_u8(shape, 256)
+        s = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+        i = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+        f.fp8_norm_quant_row(to_dev_bf16(x), to_dev_bf16(g), None if b is None else to_dev_bf16(b),
+                             f.NORM_LAYER if layer else f.NORM_RMS, 1e-5, fmt, EPS, y, q, s, i)
+        torch.cuda.synchronize()
+        check_guard(full, 256)
+        ry, rq, rs, ri = oracle.norm_quant_row(x, g, b, layer, 1e-5, name, EPS)
+        gy = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(gy, ry), (kind, shape, np.nonzero(gy != ry)[0][:5])
+        assert np.array_equal(u8(q), rq), (kind, shape, name)
+        assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+
+
+def test_norm_quant_row_partial_outputs_and_errors(f):
+    """y only, q only; bad shapes and arguments are refused."""
+    import torch
+    x = _x((6, 512), 830)
+    g, _ = _gamma(512, 831, False)
+    xd, gd = to_dev_bf16(x), to_dev_bf16(g)
+    ry, rq, rs, _ = oracle.norm_quant_row(x, g, None, False, 1e-6, _natives(f)[0][1], EPS)
+    y = torch.empty((6, 512), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_norm_quant_row(xd, gd, None, f.NORM_RMS, 1e-6, f.E4M3_NATIVE, EPS, y, None, None)
+    q = torch.empty((6, 512), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty(6, dtype=torch.float32, device="cuda:0")
+    f.fp8_norm_quant_row(xd, gd, None, f.NORM_RMS, 1e-6, f.E4M3_NATIVE, EPS, None, q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ry)
+    assert np.array_equal(u8(q), rq) and np.array_equal(s.cpu().numpy(), rs)
+    bad = [((6, 500), {}, f.ERR_ALIGNMENT), ((2, 16392), {}, f.ERR_UNSUPPORTED),
+           ((6, 512), {"beta": True}, f.ERR_INVALID_ARGUMENT)]
+    for shape, kw, st in bad:
+        xx = torch.zeros(shape, dtype=torch.bfloat16, device="cuda:0")
+        gg = torch.zeros(shape[1], dtype=torch.bfloat16, device="cuda:0")
+        qq = torch.empty(shape, dtype=torch.uint8, device="cuda:0")
+        ss = torch.empty(shape[0], dtype=torch.float32, device="cuda:0")
+        with pytest.raises(f.Fp8Error) as e:
+            f.fp8_norm_quant_row(xx, gg, gg if kw.get("beta") else None, f.NORM_RMS, 1e-6, f.E4M3_NATIVE, EPS, None,
+                                 qq, ss)
+        assert e.value.status == st, (shape, kw, e.value.status)
+
+
 def _run_dual(f, M, N, K, seed, with_row=True, zero_rows=False):
     """fp8_quant_dual against the oracle's quant_dual, byte for byte, with
     guard bands after every output."""

@@ -113,6 +113,29 @@ def test_linear_rowwise_llama3_8b_mlp(f):
     check_gemm(_gather(gw, r, c), ref, S, True, "linear_rowwise grad-weight bf16 (sampled)")
 
 
+def test_fused_rmsnorm_quant_llama3_8b_activation(f):
+    """RMSNorm fused with the rowwise e4m3 quantization on the Llama3-8B MLP input
+    X [8192,4096] (0.1% outliers x50; weights 1 + N(0,0.1)): the stored bf16
+    activation and every code and scale equal the oracle's, over the whole tensor."""
+    import torch
+    e4, _ = _names(f)
+    wl = synth.linear_rowwise()
+    x = wl.tensors["x"]
+    M, K = x.shape
+    g32 = oracle.bf16_to_f32(synth.normal_bf16((1, K), 2004, 0.1).reshape(K)) + 1.0
+    g = (g32.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    i = torch.empty_like(s)
+    f.fp8_norm_quant_row(to_dev_bf16(x), to_dev_bf16(g), None, f.NORM_RMS, 1e-5, f.E4M3_NATIVE, EPS, y, q, s, i)
+    torch.cuda.synchronize()
+    ry, rq, rs, ri = oracle.norm_quant_row(x, g, None, False, 1e-5, e4, EPS)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ry)
+    assert np.array_equal(u8(q), rq)
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+
+
 def test_linear_tensorwise_all_fp8_backward_llama3_8b_mlp(f):
     """The all-FP8 tensorwise backward on the Llama3-8B MLP shapes (the same
     X, W and grad_out as the rowwise workload): the dual quantization's three
