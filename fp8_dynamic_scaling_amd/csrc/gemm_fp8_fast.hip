@@ -334,6 +334,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float s_sa[2][BM];
+  // each wave's B-block scale of the stage (64 copies: one wave-wide DMA)
+  __shared__ __attribute__((aligned(16))) float s_sb[2][NW][64];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int64_t s_pref[kMaxExperts + 1];
 
@@ -403,16 +405,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
     // this wave's B-block scales: inv_b[e][nb][kb], nb of its 64 columns
     const int64_t nb = (ti.n0 + wn * TN) / 128;
     const float* sb_row = reinterpret_cast<const float*>(p.sb) + ((int64_t)ti.e * nbt + (nb < nbt ? nb : nbt - 1)) * nk;
+    const uint8_t* sb_bytes = reinterpret_cast<const uint8_t*>(sb_row);
 
-    auto issue = [&](int64_t k) {
+    // this wave's operand pieces of stage k (A for waves 0-3, B for 4-7)
+    auto issue_ops = [&](int64_t k) {
       const uint32_t slot = lds0 + (uint32_t)((k & 1) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
       const uint8_t* bk = base + k * BK;
 #pragma unroll
       for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
+    };
+    // the A-block scales and this wave's B-block scale of stage k
+    auto issue_scales = [&](int64_t k) {
       const uint32_t sl = lds_addr(&s_sa[k & 1][64 * (wave & 3)]);
       asm volatile("global_load_lds_dword %0, %1" ::"v"(sa_off + (uint32_t)(4 * k)),
                    "s"(reinterpret_cast<const uint8_t*>(sa_base)), "{m0}"(sl)
                    : "memory");
+      // the B-block scale through LDS as well: a plain global load here would
+      // be waited for with a vmcnt that also covers the DMA just issued
+      const uint32_t bl = lds_addr(&s_sb[k & 1][wave][0]);
+      asm volatile("global_load_lds_dword %0, %1" ::"v"((uint32_t)(4 * k)), "s"(sb_bytes), "{m0}"(bl) : "memory");
     };
 
     v4f acc[MI][NI];
@@ -421,14 +432,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    issue(0);
-    float sbk = sb_row[0];
+    // A of stage k + 1 is loaded when stage k begins, into the slot of stage
+    // k - 1. B of stage k + 2 is loaded as soon as every wave holds its B
+    // fragments of stage k, into that stage's B half: the B operand, mostly
+    // fetched from HBM (each B tile serves few row tiles), gets one and a half
+    // stages to land, A (shared by the tile row, mostly L2 hits) one.
+    issue_ops(0);
+    issue_scales(0);
+    if (!loads_a && nk > 1) issue_ops(1);
     for (int64_t k = 0; k < nk; ++k) {
-      // stage k landed everywhere and every wave is done with stage k - 1,
-      // whose slot the loads of stage k + 1 now fill
-      wait_vm_lgkm_and_barrier<0>();
-      if (k + 1 < nk) issue(k + 1);
-      const float sbk_next = sb_row[k + 1 < nk ? k + 1 : k];
+      // stage k landed everywhere and every wave is done with stage k - 1
+      if (loads_a || k + 1 >= nk) wait_vm_lgkm_and_barrier<0>();
+      else wait_vm_lgkm_and_barrier<D>();  // B of stage k + 1 may stay in flight
+      if (k + 1 < nk) {
+        if (loads_a) issue_ops(k + 1);
+        issue_scales(k + 1);
+      }
+      const float sbk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_sb[k & 1][wave][0])));
       const uint8_t* st = lds + (k & 1) * STAGE;
       v8i bf[NI];
 #pragma unroll
@@ -437,29 +457,64 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
         const uint4 hi = *reinterpret_cast<const uint4*>(st + fb_hi[j]);
         bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
+      // every wave holds its B fragments: the B half of this slot is free
+      wait_lgkm_and_barrier();
+      if (!loads_a && k + 2 < nk) issue_ops(k + 2);
+      // software pipeline over the row blocks: the products of block i issue
+      // while the FMAs that scale block i - 1 into the result run on the VALU,
+      // and block i + 1's fragment is read meanwhile
+      auto ld_a = [&](int i, v8i& af, float4& sv) {
         const uint4 lo = *reinterpret_cast<const uint4*>(st + fa_lo[i]);
         const uint4 hi = *reinterpret_cast<const uint4*>(st + fa_hi[i]);
-        const v8i af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         // rows 16 i + 4 g + r (r < 4) of this lane's output block
-        const float4 sv = *reinterpret_cast<const float4*>(&s_sa[k & 1][wm * TM + 16 * i + 4 * lg]);
-        const float f0 = sv.x * sbk, f1 = sv.y * sbk, f2 = sv.z * sbk, f3 = sv.w * sbk;
+        sv = *reinterpret_cast<const float4*>(&s_sa[k & 1][wm * TM + 16 * i + 4 * lg]);
+      };
+      v8i af_c, af_n;
+      float4 sv_c, sv_n;
+      v4f pr_p[NI];
+      float fp[4];
+      ld_a(0, af_c, sv_c);
+      // the FMAs that scale the previous block's products into the result
+      auto fma_prev = [&](int i, int j) {
+        acc[i][j][0] += pr_p[j][0] * fp[0];
+        acc[i][j][1] += pr_p[j][1] * fp[1];
+        acc[i][j][2] += pr_p[j][2] * fp[2];
+        acc[i][j][3] += pr_p[j][3] * fp[3];
+      };
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-          const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], z, AE5 ? 1 : 0, BE5 ? 1 : 0,
-                                                                          0, 127, 0, 127);
-          // sources stay live until the result is used, so the compiler cannot
-          // hand their registers to the destination (not allowed for this MFMA)
-          asm volatile("" ::"v"(af), "v"(bf[j]), "v"(pr));
-          acc[i][j][0] += pr[0] * f0;
-          acc[i][j][1] += pr[1] * f1;
-          acc[i][j][2] += pr[2] * f2;
-          acc[i][j][3] += pr[3] * f3;
+      for (int i = 0; i <= MI; ++i) {
+        v4f pr_c[NI];
+        if (i < MI) {
+          if (i + 1 < MI) ld_a(i + 1, af_n, sv_n);
+          // product j, then (fixed order) the FMAs of product j of block i - 1
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+            __builtin_amdgcn_sched_barrier(0);
+            pr_c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_c, bf[j], z, AE5 ? 1 : 0, BE5 ? 1 : 0, 0,
+                                                                       127, 0, 127);
+            if (i > 0) fma_prev(i - 1, j);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // sources stay live until every product exists (the statement
+          // takes both), so the compiler cannot hand their registers to a
+          // destination (not allowed for this MFMA)
+          asm volatile("" ::"v"(af_c), "v"(bf[0]), "v"(bf[1]), "v"(bf[2]), "v"(bf[3]), "v"(pr_c[0]),
+                       "v"(pr_c[1]), "v"(pr_c[2]), "v"(pr_c[3]));
+#pragma unroll
+          for (int j = 0; j < NI; ++j) pr_p[j] = pr_c[j];
+          fp[0] = sv_c.x * sbk;
+          fp[1] = sv_c.y * sbk;
+          fp[2] = sv_c.z * sbk;
+          fp[3] = sv_c.w * sbk;
+          af_c = af_n;
+          sv_c = sv_n;
+        } else {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) fma_prev(MI - 1, j);
         }
       }
-      sbk = sbk_next;
     }
     // every wave is done reading the last stage before the next tile's loads
     // refill its slot
