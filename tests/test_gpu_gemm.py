@@ -187,8 +187,12 @@ def test_grouped_row(f, counts, N, K):
     check_gemm(got, ref, S, True, f"grouped row {counts}")
 
 
-@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256)])
-def test_grouped_block(f, counts, N, K):
+@pytest.mark.parametrize("counts,N,K,out_f32", [([100, 0, 200, 7], 256, 384, False), ([512, 512], 128, 256, False),
+                                                 ([64], 128, 128, False), ([300, 5, 0, 129], 384, 640, True),
+                                                 ([4096, 4096], 2304, 128, False)])
+def test_grouped_block(f, counts, N, K, out_f32):
+    """One K block (no prefetch), an odd number of K blocks, a partial B tile and fp32
+    output, and more tiles than workgroups (each walks several, reusing its LDS slots)."""
     import torch
     e4, _ = _names(f)
     rng = np.random.default_rng(11)
@@ -197,13 +201,13 @@ def test_grouped_block(f, counts, N, K):
     a, b = _codes(e4, (Mt, K), rng), _codes(e4, (E, N, K), rng)
     sa = rng.uniform(0.01, 4, (Mt, K // 128)).astype(np.float32)
     sb = rng.uniform(0.01, 4, (E, N // 128, K // 128)).astype(np.float32)
-    out = _out((Mt, N), False)
+    out = _out((Mt, N), out_f32)
     f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_BLOCK128, to_dev(sa), to_dev(sb),
-                     to_dev(off), f.OUT_BF16, out)
+                     to_dev(off), f.OUT_F32 if out_f32 else f.OUT_BF16, out)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off)
     S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off, absolute=True)
-    check_gemm(_host(out), ref, S, True, f"grouped block {counts}")
+    check_gemm(_host(out), ref, S, not out_f32, f"grouped block {counts} K={K}")
 
 
 @pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256), ([33], 48, 96),
