@@ -178,11 +178,26 @@ static fp8_status check_quant_common(const uint16_t* x, int64_t batch, int64_t r
   return FP8_OK;
 }
 
+// Groups with no elements still get their scales: amax 0, so the eps-clamped
+// value. Nothing is read; scale (and inv, when given) must hold n floats.
+// fnuz: whether the calling quantizer offers the fnuz outputs.
+static fp8_status empty_group_scales(fp8_format fmt, bool fnuz, double eps, float* scale, float* inv, int64_t n,
+                                     void* stream) {
+  if (n == 0) return FP8_OK;
+  if (!scale) return FP8_ERR_INVALID_ARGUMENT;
+  if (!aligned(scale, 4) || (inv && !aligned(inv, 4))) return FP8_ERR_ALIGNMENT;
+  bool e5, nz;
+  double fm;
+  fp8_status st = fnuz ? resolve_out(fmt, &e5, &fm, &nz) : resolve(fmt, &e5, &fm);
+  if (st != FP8_OK) return st;
+  return dev_err(launch_empty_group_scales(scale, inv, n, fm, eps, (hipStream_t)stream));
+}
+
 fp8_status fp8_quant_tensor(const uint16_t* x, int64_t n, fp8_format fmt, double eps, uint8_t* q, float* scale,
                             float* inv_scale, void* ws, size_t ws_bytes, void* stream) {
   fp8_status st = check_quant_common(x, 1, 1, n, eps, q, scale);
   if (st != FP8_OK) return st;
-  if (n == 0) return FP8_OK;
+  if (n == 0) return empty_group_scales(fmt, true, eps, scale, inv_scale, 1, stream);
   if (!ws || ws_bytes < fp8_quant_tensor_ws_bytes()) return FP8_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
   bool e5, nz;
@@ -195,7 +210,9 @@ fp8_status fp8_quant_tensor(const uint16_t* x, int64_t n, fp8_format fmt, double
 fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
                          uint8_t* q, float* scale, float* inv_scale, void* stream) {
   fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
-  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  if (st != FP8_OK) return st;
+  if (cols == 0) return empty_group_scales(fmt, true, eps, scale, inv_scale, batch * rows, stream);
+  if (batch * rows == 0) return FP8_OK;
   bool e5, nz;
   double fm;
   if ((st = resolve_out(fmt, &e5, &fm, &nz)) != FP8_OK) return st;
@@ -206,7 +223,9 @@ fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t
 fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
                          uint8_t* qT, float* scale, float* inv_scale, void* ws, size_t ws_bytes, void* stream) {
   fp8_status st = check_quant_common(x, batch, rows, cols, eps, qT, scale);
-  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  if (st != FP8_OK) return st;
+  if (rows == 0) return empty_group_scales(fmt, false, eps, scale, inv_scale, batch * cols, stream);
+  if (batch * cols == 0) return FP8_OK;
   const size_t need = quant_col_ws_bytes(batch, rows, cols);
   const bool vec_path = cols % 8 == 0 && rows % 16 == 0;
   if (need > 0 && vec_path) {
@@ -227,7 +246,9 @@ fp8_status fp8_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const ui
     return FP8_ERR_INVALID_ARGUMENT;
   if (kind != FP8_NORM_RMS && kind != FP8_NORM_LAYER) return FP8_ERR_INVALID_ARGUMENT;
   if (kind == FP8_NORM_RMS && beta) return FP8_ERR_INVALID_ARGUMENT;
-  if (rows == 0 || cols == 0) return FP8_OK;
+  if (rows == 0) return FP8_OK;
+  // empty rows: nothing to normalize, and the quantization's groups are empty
+  if (cols == 0) return empty_group_scales(fmt, false, eps, scale, inv_scale, scale ? rows : 0, stream);
   if (!x || !gamma || (!y && !q) || (q && !scale)) return FP8_ERR_INVALID_ARGUMENT;
   if (cols % 8 != 0) return FP8_ERR_ALIGNMENT;
   if (cols > 16384) return FP8_ERR_UNSUPPORTED;  // the row lives in registers
@@ -249,21 +270,35 @@ fp8_status fp8_quant_dual(const uint16_t* gy, const uint16_t* x, int64_t M, int6
                           fp8_format x_fmt, double eps, uint8_t* gq, uint8_t* gqT, float* g_scale, float* g_inv,
                           uint8_t* xqT, float* x_scale, float* x_inv, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0 || bad_eps(eps)) return FP8_ERR_INVALID_ARGUMENT;
-  if (M == 0 || N == 0 || K == 0) return FP8_OK;
-  if (!gy || !x || !gqT || !g_scale || !xqT || !x_scale) return FP8_ERR_INVALID_ARGUMENT;
-  if (M % 16 != 0 || N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
-  if (M * N >= ((int64_t)1 << 30) || M * K >= ((int64_t)1 << 30)) return FP8_ERR_UNSUPPORTED;
-  if (!aligned(gy, 16) || !aligned(x, 16) || !aligned(gqT, 16) || !aligned(xqT, 16) || (gq && !aligned(gq, 8)) ||
-      !aligned(g_scale, 4) || !aligned(x_scale, 4) || (g_inv && !aligned(g_inv, 4)) || (x_inv && !aligned(x_inv, 4)))
-    return FP8_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < fp8_quant_dual_ws_bytes()) return FP8_ERR_WORKSPACE;
-  if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
   bool ge5, xe5;
   double gfm, xfm;
   fp8_status st;
   if ((st = resolve(g_fmt, &ge5, &gfm)) != FP8_OK || (st = resolve(x_fmt, &xe5, &xfm)) != FP8_OK) return st;
-  const TJobSpec jobs[2] = {{gy, M, N, ge5, gfm, gq, gqT, g_scale, g_inv}, {x, M, K, xe5, xfm, nullptr, xqT, x_scale, x_inv}};
-  return dev_err(launch_quant_tensor_multi_t(jobs, 2, eps, (uint32_t*)ws, (hipStream_t)stream));
+  // each tensor has one group and so one scale, even when it is empty
+  const bool g_has = M * N > 0, x_has = M * K > 0;
+  if (!g_scale || !x_scale) return FP8_ERR_INVALID_ARGUMENT;
+  if ((g_has && (!gy || !gqT)) || (x_has && (!x || !xqT))) return FP8_ERR_INVALID_ARGUMENT;
+  if ((g_has || x_has) && M % 16 != 0) return FP8_ERR_ALIGNMENT;
+  if ((g_has && N % 8 != 0) || (x_has && K % 8 != 0)) return FP8_ERR_ALIGNMENT;
+  if (M * N >= ((int64_t)1 << 30) || M * K >= ((int64_t)1 << 30)) return FP8_ERR_UNSUPPORTED;
+  if ((gy && !aligned(gy, 16)) || (x && !aligned(x, 16)) || (gqT && !aligned(gqT, 16)) || (xqT && !aligned(xqT, 16)) ||
+      (gq && !aligned(gq, 8)) || !aligned(g_scale, 4) || !aligned(x_scale, 4) || (g_inv && !aligned(g_inv, 4)) ||
+      (x_inv && !aligned(x_inv, 4)))
+    return FP8_ERR_ALIGNMENT;
+  TJobSpec jobs[2];
+  int nj = 0;
+  if (g_has) jobs[nj++] = {gy, M, N, ge5, gfm, gq, gqT, g_scale, g_inv};
+  if (x_has) jobs[nj++] = {x, M, K, xe5, xfm, nullptr, xqT, x_scale, x_inv};
+  if (nj > 0) {
+    if (!ws || ws_bytes < fp8_quant_dual_ws_bytes()) return FP8_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return FP8_ERR_ALIGNMENT;
+    if ((st = dev_err(launch_quant_tensor_multi_t(jobs, nj, eps, (uint32_t*)ws, (hipStream_t)stream))) != FP8_OK)
+      return st;
+  }
+  if (!g_has && (st = dev_err(launch_empty_group_scales(g_scale, g_inv, 1, gfm, eps, (hipStream_t)stream))) != FP8_OK)
+    return st;
+  if (!x_has) return dev_err(launch_empty_group_scales(x_scale, x_inv, 1, xfm, eps, (hipStream_t)stream));
+  return FP8_OK;
 }
 
 fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int block_rows,
@@ -319,6 +354,8 @@ fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_
   double fm;
   if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
   if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  // no contraction terms: the empty sum (nothing is read)
+  if (K == 0) return dev_err(launch_zero_fill(out, M * N * (out_type == FP8_OUT_F32 ? 4 : 2), (hipStream_t)stream));
   GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
   return dev_err(launch_gemm_fp8(g));
@@ -337,6 +374,9 @@ fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8
   double fm;
   if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
   if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  // no contraction terms: every row of every expert is the empty sum
+  if (K == 0)
+    return dev_err(launch_zero_fill(out, Mtot * N * (out_type == FP8_OUT_F32 ? 4 : 2), (hipStream_t)stream));
   GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
   return dev_err(launch_gemm_fp8(g));
@@ -349,6 +389,8 @@ fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int6
   if (!gw || (M > 0 && (!gy || !x))) return FP8_ERR_INVALID_ARGUMENT;
   if (N % 8 != 0 || K % 8 != 0) return FP8_ERR_ALIGNMENT;
   if ((gy && !aligned(gy, 16)) || (x && !aligned(x, 16)) || !aligned(gw, 4)) return FP8_ERR_ALIGNMENT;
+  // no rows: the empty sum
+  if (M == 0) return dev_err(launch_zero_fill(gw, N * K * 2, (hipStream_t)stream));
   WgradArgs w{gy, x, M, N, K, gw, (hipStream_t)stream};
   return dev_err(launch_wgrad_bf16(w));
 }

@@ -115,4 +115,10 @@ struct GroupedWgradArgs {
 };
 hipError_t launch_grouped_wgrad_bf16(const GroupedWgradArgs& w);
 
+// Degenerate sizes (fill.hip): the eps-clamped scale of an empty group into
+// scale[0..n) (and inv), and zeros over bytes (2-byte aligned, even count).
+hipError_t launch_empty_group_scales(float* scale, float* inv, int64_t n, double fmax, double eps,
+                                     hipStream_t stream);
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t stream);
+
 }  // namespace fp8dyn

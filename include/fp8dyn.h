@@ -32,10 +32,16 @@
  *    been synchronized. No call synchronizes the device or reads device
  *    data back to the host.
  *  - Every argument is validated on the host before anything is launched; on
- *    any error nothing is launched and the status says why. A problem with a
- *    zero dimension is a successful no-op. Launch failures return
+ *    any error nothing is launched and the status says why. Launch failures return
  *    FP8_ERR_DEVICE; faults inside a kernel surface at the caller's next
  *    synchronization (fp8_last_device_error keeps the last HIP error seen).
+ *  - Zero dimensions. Whatever holds no elements is neither read nor written
+ *    (its pointer may be NULL). A quantization group with no elements (a row
+ *    of 0 columns, a column of 0 rows, a tensor of 0 elements) still gets its
+ *    scale: amax over an empty set is 0, so scale = fp8_max / eps. A GEMM
+ *    with K = 0, and a weight gradient over M = 0 rows, write zeros (the
+ *    empty sum) without reading any operand or scale. Anything else with a
+ *    zero dimension does nothing.
  *  - eps must be finite and > 0; 1e-12 is the usual value.
  *  - Quantization writes `scale` (the quantize multiplier fp8_max/amax) and,
  *    when inv_scale is not NULL, its fp64 reciprocal rounded to fp32. GEMMs

@@ -65,9 +65,13 @@ def test_host_validation_without_gpu(f):
     assert lib.fp8_quant_row(None, 1, 4, 8, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None) == f.ERR_INVALID_ARGUMENT
     # misaligned data pointer
     assert lib.fp8_quant_row(FAKE + 2, 1, 4, 8, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None) == f.ERR_ALIGNMENT
-    # zero-size problems are a no-op success
+    # zero-size problems without groups are a no-op success
     assert lib.fp8_quant_row(None, 0, 4, 8, f.E4M3_NATIVE, 1e-12, None, None, None, None) == f.OK
-    assert lib.fp8_quant_col(None, 1, 0, 8, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.OK
+    assert lib.fp8_quant_col(None, 0, 0, 8, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.OK
+    # ... but empty groups still get their (eps-clamped) scales, so those must be given
+    assert lib.fp8_quant_col(None, 1, 0, 8, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.ERR_INVALID_ARGUMENT
+    assert lib.fp8_quant_row(None, 1, 4, 0, f.E4M3_NATIVE, 1e-12, None, None, None, None) == f.ERR_INVALID_ARGUMENT
+    assert lib.fp8_quant_tensor(None, 0, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.ERR_INVALID_ARGUMENT
     # MX needs cols % 32 == 0
     assert lib.fp8_quant_mx(FAKE, 1, 4, 48, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
     # block geometry
