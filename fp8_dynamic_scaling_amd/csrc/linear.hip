@@ -134,7 +134,16 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
                           void* stream) {
   if (recipe != FP8_RECIPE_TENSORWISE && recipe != FP8_RECIPE_ROWWISE_BF16_WGRAD) return FP8_ERR_INVALID_ARGUMENT;
   if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
-  if (M == 0 || N == 0 || K == 0) return FP8_OK;
+  if (K == 0) return FP8_OK;  // both gradients are empty
+  // the empty sums: grad-weight over no rows, grad-input over no outputs
+  if (M == 0 || N == 0) {
+    uint16_t* z = M == 0 ? gw : gx;
+    const int64_t n = (M == 0 ? N : M) * K;
+    if (n == 0) return FP8_OK;
+    if (!z) return FP8_ERR_INVALID_ARGUMENT;
+    if (!aligned(z, 4)) return FP8_ERR_ALIGNMENT;
+    return as_status(launch_zero_fill(z, n * 2, (hipStream_t)stream));
+  }
   if (!gy || !x || !w || !gx || !gw) return FP8_ERR_INVALID_ARGUMENT;
   if (N % 16 != 0 || K % 16 != 0) return FP8_ERR_ALIGNMENT;
   size_t need = 0;

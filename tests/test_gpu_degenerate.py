@@ -173,3 +173,26 @@ def test_wgrad_over_no_rows_is_zero(f):
     torch.cuda.synchronize()
     ref = oracle.wgrad_bf16(np.zeros((0, N), np.uint16), np.zeros((0, K), np.uint16))
     assert np.array_equal(gw.float().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("recipe", ["rowwise", "tensorwise"])
+def test_linear_empty_sums(f, recipe):
+    """The linear layer's empty sums: the forward with K = 0, the grad-weight over
+    M = 0 rows and the grad-input over N = 0 outputs are zeros."""
+    import torch
+    R = f.RECIPE_ROWWISE_BF16_WGRAD if recipe == "rowwise" else f.RECIPE_TENSORWISE
+
+    def ws(M, N, K):
+        return torch.empty(max(1, f.fp8_linear_ws_bytes(M, N, K, R)), dtype=torch.uint8, device="cuda:0")
+
+    def nan16(shape):
+        return torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    y = nan16((48, 32))
+    f.fp8_linear_fwd(_bf16((48, 0)), _bf16((32, 0)), R, EPS, f.OUT_BF16, y, ws(48, 32, 0))
+    gw = nan16((32, 48))
+    f.fp8_linear_bwd(_bf16((0, 32)), _bf16((0, 48)), _bf16((32, 48)), R, EPS, _bf16((0, 48)), gw, ws(0, 32, 48))
+    gx = nan16((48, 32))
+    f.fp8_linear_bwd(_bf16((48, 0)), _bf16((48, 32)), _bf16((0, 32)), R, EPS, gx, _bf16((0, 32)), ws(48, 0, 32))
+    torch.cuda.synchronize()
+    for name, t in (("y", y), ("grad-weight", gw), ("grad-input", gx)):
+        assert np.array_equal(t.float().cpu().numpy(), np.zeros(t.shape)), name
