@@ -72,8 +72,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
   __shared__ int32_t s_off[GR ? kMaxExperts + 1 : 2];
   __shared__ int64_t s_pref[GR ? kMaxExperts + 1 : 2];
-  // MX: E8M0 scales of a stage pair, A rows then B rows, in a ring of 4 pairs
-  __shared__ __attribute__((aligned(16))) uint32_t s_scl[MXS ? 4 : 1][MXS ? BM + BN : 1];
+  // MX: E8M0 scales, A rows then B rows. Either a ring of 4 stage pairs, one
+  // dword per row each, or (K % 512 == 0, 16-byte aligned scales) a ring of 2
+  // blocks of 4 pairs, 16 bytes per row each
+  __shared__ __attribute__((aligned(16))) uint32_t s_scl[MXS ? 4 * (BM + BN) * 2 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,6 +86,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   const int64_t nt = (N + BN - 1) / BN;
   const int64_t nk = K / BK;
   const uint32_t lds0 = lds_addr(lds);
+  // MX scales 16 bytes per row at a time: a dword per row touches a cache
+  // line per lane, and the DMA pays per line touched
+  const bool scl16 = MXS && nk % 8 == 0 && ((uintptr_t)p.sa % 16) == 0 && ((uintptr_t)p.sb % 16) == 0;
 
   int64_t total;
   if constexpr (GR) {
@@ -162,9 +167,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
 #pragma unroll
       for (int d = 0; d < DH; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
       if constexpr (MXS) {
-        if ((s & 1) == 0) {
-          const uint32_t l = lds_addr(&s_scl[(s >> 1) & 3][0]) + sc_lds;
-          const uint32_t o = sc_off + (uint32_t)(2 * s);
+        const uint32_t o = sc_off + (uint32_t)(2 * s);  // byte 4 (s / 2) of the row
+        if (scl16) {
+          if ((s & 7) == 0) {  // pairs s / 2 .. s / 2 + 3
+            const uint32_t l = lds_addr(&s_scl[((s >> 3) & 1) * 4 * (BM + BN)]) + 4 * sc_lds;
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(o), "s"(sc_base), "{m0}"(l) : "memory");
+          }
+        } else if ((s & 1) == 0) {
+          const uint32_t l = lds_addr(&s_scl[((s >> 1) & 3) * (BM + BN)]) + sc_lds;
           asm volatile("global_load_lds_dword %0, %1" ::"v"(o), "s"(sc_base), "{m0}"(l) : "memory");
         }
       }
@@ -172,21 +182,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     v8i fa[MI], fb[NI];
     int sa[MI], sb[NI];
     auto read = [&](int64_t s) {
-      if constexpr (MXS) {
-        // this lane's E8M0 byte: K block 2 s + g of its row, byte 2 (s % 2) + g
-        // of the row's dword in the pair
-        const uint8_t* sp = reinterpret_cast<const uint8_t*>(&s_scl[(s >> 1) & 3][0]) + 2 * (int)(s & 1) + lg;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) sa[i] = sp[4 * (wm * TM + 32 * i + lrow)];
-#pragma unroll
-        for (int j = 0; j < NI; ++j) sb[j] = sp[4 * (BM + wn * TN + 32 * j + lrow)];
-        // final values here, in the memory phase: no VALU op on a scale
-        // operand may sit right before its MFMA
-#pragma unroll
-        for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(sa[i]));
-#pragma unroll
-        for (int j = 0; j < NI; ++j) asm volatile("" : "+v"(sb[j]));
-      }
       // slot offset opaque per call: the 12 addresses are formed per read, not
       // precomputed for all 4 slots (48 registers)
       uint32_t so = (uint32_t)((s & (NS - 1)) * STAGE);
@@ -202,6 +197,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
         const uint4 lo = *reinterpret_cast<const uint4*>(lds + so + fb_lo[j]);
         const uint4 hi = *reinterpret_cast<const uint4*>(lds + so + fb_hi[j]);
         fb[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      if constexpr (MXS) {
+        // this lane's E8M0 byte: K block 2 s + g of its row, byte 2 (s % 2) + g
+        // of the row's dword of the pair (16-byte rows: dword (s / 2) % 4)
+        const uint8_t* sp;
+        int rs;  // bytes per row
+        if (scl16) {
+          sp = reinterpret_cast<const uint8_t*>(&s_scl[((s >> 3) & 1) * 4 * (BM + BN)]) + 4 * (int)((s >> 1) & 3);
+          rs = 16;
+        } else {
+          sp = reinterpret_cast<const uint8_t*>(&s_scl[((s >> 1) & 3) * (BM + BN)]);
+          rs = 4;
+        }
+        sp += 2 * (int)(s & 1) + lg;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) sa[i] = sp[rs * (wm * TM + 32 * i + lrow)];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sb[j] = sp[rs * (BM + wn * TN + 32 * j + lrow)];
+      }
+    };
+    // MX: the scale operands take their final values here, in the memory
+    // phase, so no VALU op on one can sit right before its MFMA. Called after
+    // the fragment reads and the DMA issue: the wait these pins imply then
+    // costs one LDS round trip for all reads of the phase.
+    auto pin_scales = [&]() {
+      if constexpr (MXS) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(sa[i]));
+#pragma unroll
+        for (int j = 0; j < NI; ++j) asm volatile("" : "+v"(sb[j]));
       }
     };
     v16f acc[MI][NI];
@@ -228,10 +253,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     // this wave's loads of stage u + 1 have landed: those issued after it
     // (stages u + 2 .. min(u + 3, nk - 1); one of two consecutive stages is
     // even and carries a scale load) may stay in flight
+    // (16-byte scale rows: a scale load rides with one stage in 8; waiting as
+    // if none were in flight waits at most one load longer)
     auto wait_next = [&](int64_t u) {
-      if (u + 3 < nk) wait_vm_lgkm_and_barrier<2 * DH + X>();
-      else if (u + 2 < nk) wait_vm_lgkm_and_barrier<DH>();  // stage nk - 1 is odd
-      else wait_vm_lgkm_and_barrier<0>();
+      if (u + 3 < nk) {
+        if (scl16) wait_vm_lgkm_and_barrier<2 * DH>();
+        else wait_vm_lgkm_and_barrier<2 * DH + X>();
+      } else if (u + 2 < nk) {
+        wait_vm_lgkm_and_barrier<DH>();  // stage nk - 1 is odd
+      } else {
+        wait_vm_lgkm_and_barrier<0>();
+      }
     };
 
     // prologue: stages 0 .. min(nk, 3) - 1; then stage 0 has landed
@@ -239,7 +271,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     issue(1);
     if (nk >= 4) {
       issue(2);
-      wait_vm_lgkm_and_barrier<2 * DH + X>();
+      if (scl16) wait_vm_lgkm_and_barrier<2 * DH>();
+      else wait_vm_lgkm_and_barrier<2 * DH + X>();
     } else {
       wait_vm_lgkm_and_barrier<DH>();
     }
@@ -250,6 +283,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     for (int64_t u = 0; u < nk; ++u) {
       read(u);
       if (u + 3 < nk) issue(u + 3);
+      pin_scales();
       wait_next(u);
       __builtin_amdgcn_sched_barrier(0);
       mma();

@@ -210,9 +210,14 @@ def test_grouped_block(f, counts, N, K, out_f32):
     check_gemm(_host(out), ref, S, not out_f32, f"grouped block {counts} K={K}")
 
 
-@pytest.mark.parametrize("counts,N,K", [([100, 0, 200, 7], 256, 384), ([512, 512], 128, 256), ([33], 48, 96),
-                                         ([300, 5, 0, 129], 320, 640), ([64], 192, 128), ([600, 0, 3], 512, 1152)])
-def test_grouped_mx(f, counts, N, K):
+@pytest.mark.parametrize("counts,N,K,shift", [([100, 0, 200, 7], 256, 384, 0), ([512, 512], 128, 256, 0),
+                                               ([33], 48, 96, 0), ([300, 5, 0, 129], 320, 640, 0),
+                                               ([64], 192, 128, 0), ([600, 0, 3], 512, 1152, 0),
+                                               ([300, 5, 0, 129], 320, 1024, 0), ([64], 192, 512, 0),
+                                               ([600, 0, 3], 512, 2048, 0), ([300, 5, 0, 129], 320, 1024, 4)])
+def test_grouped_mx(f, counts, N, K, shift):
+    """K % 512 == 0 with 16-byte aligned scales takes the kernel's 16-bytes-per-row
+    scale loads; other K, or scales at a 4-byte offset (shift), the dword loads."""
     import torch
     e4, _ = _names(f)
     rng = np.random.default_rng(13)
@@ -222,7 +227,14 @@ def test_grouped_mx(f, counts, N, K):
     sa = rng.integers(117, 137, (Mt, K // 32)).astype(np.uint8)
     sb = rng.integers(117, 137, (E, N, K // 32)).astype(np.uint8)
     out = _out((Mt, N), False)
-    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_MX32, to_dev(sa), to_dev(sb),
+
+    def shifted(x):
+        # the same bytes at a device address `shift` bytes past a 256-byte boundary
+        buf = torch.zeros(x.size + 256, dtype=torch.uint8, device="cuda:0")
+        v = buf[shift:shift + x.size]
+        v.copy_(to_dev(x).reshape(-1))
+        return v
+    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_MX32, shifted(sa), shifted(sb),
                      to_dev(off), f.OUT_BF16, out)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_MX32, sa, sb, off)
