@@ -214,7 +214,8 @@ def test_grouped_block(f, counts, N, K, out_f32):
                                                ([33], 48, 96, 0), ([300, 5, 0, 129], 320, 640, 0),
                                                ([64], 192, 128, 0), ([600, 0, 3], 512, 1152, 0),
                                                ([300, 5, 0, 129], 320, 1024, 0), ([64], 192, 512, 0),
-                                               ([600, 0, 3], 512, 2048, 0), ([300, 5, 0, 129], 320, 1024, 4)])
+                                               ([600, 0, 3], 512, 2048, 0), ([300, 5, 0, 129], 320, 1024, 4),
+                                               ([1536, 1536], 6144, 512, 0)])
 def test_grouped_mx(f, counts, N, K, shift):
     """K % 512 == 0 with 16-byte aligned scales takes the kernel's 16-bytes-per-row
     scale loads; other K, or scales at a 4-byte offset (shift), the dword loads."""
