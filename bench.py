@@ -73,6 +73,28 @@ class Step:
                 fn()
 
 
+# sha256 (first 16 hex digits) of the host inputs that build_step draws beside
+# the workloads' own tensors, filled in as it draws them
+EXTRA_INPUT_SHA = {}
+
+
+def input_digests(wls):
+    """sha256 of every generated host input: each workload's tensors and
+    offsets, then the extra inputs the step draws."""
+    import numpy as np
+    import synth
+    d = {}
+    for n, w in wls.items():
+        if w is None:
+            continue
+        for k, v in w.tensors.items():
+            d[f"{n}.{k}"] = synth.sha256(v)
+        if "offsets" in w.meta:
+            d[f"{n}.offsets"] = synth.sha256(np.asarray(w.meta["offsets"]))
+    d.update(EXTRA_INPUT_SHA)
+    return d
+
+
 def build_step(f, torch, dev, wls, dev_of):
     """Allocates outputs and returns a Step whose calls cover every step of the path."""
     st = Step(torch)
@@ -124,6 +146,7 @@ def build_step(f, torch, dev, wls, dev_of):
     import synth as _synth
     # RMSNorm weights 1 + N(0, 0.1), truncated to bf16
     gn = _synth.normal_bf16((1, K), 2004, 0.1).reshape(K)
+    EXTRA_INPUT_SHA["linear_rowwise.norm_weight_delta"] = _synth.sha256(gn)
     gn32 = (gn.astype(np.uint32) << 16).view(np.float32) + np.float32(1.0)
     gnd = dev_of((gn32.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
     yn = torch.empty((M, K), **bf)
@@ -185,7 +208,9 @@ def build_step(f, torch, dev, wls, dev_of):
     # (its W has the layer's [32][2048][7168] shape); grouped BF16
     # grad-weight over the offsets ----
     import synth as _synth
-    go4 = dev_of(_synth.normal_bf16((Mt, N4), 4003, 1e-3))
+    go4_h = _synth.normal_bf16((Mt, N4), 4003, 1e-3)
+    EXTRA_INPUT_SHA["moe_grouped.grad_out"] = _synth.sha256(go4_h)
+    go4 = dev_of(go4_h)
     qgo4, sgo4, igo4 = torch.empty((Mt, N4), **u8), torch.empty(Mt, **f32), torch.empty(Mt, **f32)
     gx4 = torch.empty((Mt, K4), **bf)
     gw4 = torch.empty((E4n, N4, K4), **bf)
@@ -438,6 +463,7 @@ def main():
         out["roofline"]["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         out["roofline"]["sources"] = sources_digest(kind)
     out["rows"] = rows
+    out["inputs_sha256"] = input_digests(wls)
     if not args.no_cpu_baseline and "moe_grouped" in wls:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(wls, args.cpu_budget)
