@@ -540,21 +540,29 @@ __global__ __launch_bounds__(256) void k_quant_group1d(const uint16_t* __restric
   }
 }
 
-// 128 x 128 blocks: one workgroup of 256 threads per block; thread t owns
-// column chunk t % 16 of rows t / 16 + 16 j.
-template <bool E5>
-__global__ __launch_bounds__(256) void k_quant_block128(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                        int64_t nbr, int64_t nbc, uint8_t* __restrict__ q,
-                                                        float* __restrict__ scale, float* __restrict__ inv,
-                                                        double fmax, double eps) {
-  __shared__ float red[4];
+// 128 x 128 blocks: one workgroup of NB * 256 threads per NB neighbouring
+// blocks of a 128-row band. 16 NB lanes cover NB * 256 contiguous bytes of a
+// row (a thread: 8 columns of rows ro + 16 j, j < 8). On the 16 x 8192 x 5120
+// MoE weights two blocks per workgroup (512-byte row pieces) measured 6% faster
+// than one; four (1024 threads) leave one workgroup per CU and were slower.
+template <bool E5, int NB>
+__global__ __launch_bounds__(NB * 256) void k_quant_block128(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                             int64_t nbr, int64_t nbc, uint8_t* __restrict__ q,
+                                                             float* __restrict__ scale, float* __restrict__ inv,
+                                                             double fmax, double eps) {
+  constexpr int LPR = NB * 16;  // lanes per row
+  constexpr int NW = NB * 4;    // waves
+  __shared__ float red[NW][NB];
+  const int64_t ngrp = nbc / NB;
   int64_t blk = blockIdx.x;
-  const int64_t cb = blk % nbc;
-  blk /= nbc;
+  const int64_t cg = blk % ngrp;
+  blk /= ngrp;
   const int64_t rb = blk % nbr;
   const int64_t b = blk / nbr;
-  const int cc = threadIdx.x & 15, ro = threadIdx.x >> 4;
-  const int64_t c = cb * 128 + cc * 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cc = tid % LPR, ro = tid / LPR;
+  const int sub = cc >> 4;  // block of the group
+  const int64_t c = cg * NB * 128 + cc * 8;
   const bool cok = c < C;
   const uint16_t* xb = x + b * R * C;
   uint4 v[8];
@@ -567,12 +575,22 @@ __global__ __launch_bounds__(256) void k_quant_block128(const uint16_t* __restri
       m = amax8(v[j], m);
     }
   }
-  m = block_max<256>(m, red);
+  // the 16 lanes of one block in one row, then the rows a wave holds
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane < LPR && (lane & 15) == 0) red[wave][lane >> 4] = m;
+  __syncthreads();
+  m = red[0][sub];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][sub]);
   float s, iv;
   scale_from_amax(m, fmax, eps, s, iv);
-  if (threadIdx.x == 0) {
-    scale[blockIdx.x] = s;
-    if (inv) inv[blockIdx.x] = iv;
+  const int64_t si = (b * nbr + rb) * nbc + cg * NB + sub;
+  if (ro == 0 && (cc & 15) == 0) {
+    scale[si] = s;
+    if (inv) inv[si] = iv;
   }
   const float fm = (float)fmax;
 #pragma unroll
@@ -1099,9 +1117,12 @@ static hipError_t launch_block_t(const QuantArgs& a, int br, int bc) {
     else
       hipLaunchKernelGGL((k_quant_group1d<E5, 128, false, 1>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
                          B * R, C, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
+  } else if (vec && br == 128 && bc == 128 && C % 256 == 0) {
+    hipLaunchKernelGGL((k_quant_block128<E5, 2>), dim3((unsigned)(B * nbr * nbc / 2)), dim3(512), 0, a.stream, a.x, R,
+                       C, nbr, nbc, a.q, a.scale, a.inv, a.fmax, a.eps);
   } else if (vec && br == 128 && bc == 128) {
-    hipLaunchKernelGGL((k_quant_block128<E5>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x, R, C, nbr,
-                       nbc, a.q, a.scale, a.inv, a.fmax, a.eps);
+    hipLaunchKernelGGL((k_quant_block128<E5, 1>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x, R, C,
+                       nbr, nbc, a.q, a.scale, a.inv, a.fmax, a.eps);
   } else {
     hipLaunchKernelGGL((k_quant_block_generic<E5, false>), dim3((unsigned)(B * nbr * nbc)), dim3(256), 0, a.stream, a.x,
                        R, C, (int64_t)br, (int64_t)bc, nbr, nbc, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);

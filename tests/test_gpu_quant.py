@@ -382,7 +382,8 @@ def test_quant_dual_rejects_bad_shapes(f):
 
 
 @pytest.mark.parametrize("br,shape", [(1, (3, 300)), (1, (5, 1024)), (1, (2, 7, 640)), (128, (130, 260)),
-                                      (128, (2, 256, 384)), (128, (300, 136))])
+                                      (128, (2, 256, 384)), (128, (300, 136)), (128, (300, 768)),
+                                      (128, (3, 200, 512)), (128, (64, 256))])
 def test_quant_block(f, br, shape):
     import torch
     x = _x(shape, 500 + shape[-1])
