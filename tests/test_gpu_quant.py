@@ -132,7 +132,8 @@ def _run_col(f, fmt, name, x, guard=256):
 
 
 @pytest.mark.parametrize("shape", [(16, 8), (2048, 64), (2048, 72), (48, 200), (100, 24), (4096, 128),
-                                   (3, 48, 40), (2, 2064, 64), (1024, 2064, 8)])
+                                   (3, 48, 40), (2, 2064, 64), (1024, 2064, 8), (64, 64, 512), (70, 32, 520),
+                                   (9, 2048, 3648), (40, 2000, 840)])
 def test_quant_col(f, shape):
     x = _x(shape, 300 + shape[-1], spread=False)
     for fmt, name in _natives(f):
