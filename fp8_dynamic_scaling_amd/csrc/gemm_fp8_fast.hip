@@ -54,10 +54,12 @@ namespace fp8dyn {
 //    of stage u + 3 into the slot of stage u - 1 (free once group 1 read it at
 //    the end of phase 2u - 1); stage u + 1 has landed (each wave waits for its
 //    own loads before the barrier that ends phase 2u + 1).
-//  - MX: the E8M0 bytes of a stage pair (one dword per row and 128-deep K)
-//    ride in an LDS ring of 4 pairs, one wave-wide dword load per wave with the
-//    even stage's loads; each lane reads its byte straight into the MFMA's
-//    scale operand in the memory phase.
+//  - MX: when K % 512 == 0 and the scale pointers are 16-byte aligned, a row's
+//    E8M0 bytes for four stage pairs (512-deep K) come in one 16-byte load per
+//    lane with one stage in eight, into an LDS ring of two such blocks;
+//    otherwise a stage pair's bytes (one dword per row, 128-deep K) ride in a
+//    ring of 4 pairs with each even stage's loads. Each lane reads its byte
+//    straight into the MFMA's scale operand in the memory phase.
 template <bool AE5, bool BE5, int SK, bool OF32, bool GR>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 64, NS = 4;

@@ -284,8 +284,9 @@ __global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict
 // consecutive rows. It reduces the CW column maxima, then casts and stores
 // from the same registers with the transposed 16-byte packing described above
 // (each store instruction writes CW / 8 columns x 16 * 64 / (CW / 8)
-// contiguous bytes). Several workgroups share a CU, so some load while others
-// cast and store. Consecutive strips go to the same XCD (strips narrower
+// contiguous bytes). With fewer rows several workgroups share a CU, so some
+// load while others cast and store; at 2048 rows (1024 threads of about 90
+// VGPRs) one fits. Consecutive strips go to the same XCD (strips narrower
 // than 64 columns share 128-byte lines of x).
 #ifndef FP8DYN_COL_CW
 #define FP8DYN_COL_CW 64
