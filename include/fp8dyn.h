@@ -257,9 +257,10 @@ FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint
 FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N,
                                      int64_t K, uint16_t* gw, void* stream);
 
-/* Grouped BF16 weight gradient of an MoE layer over device offsets [SURVEY
- * next step "MoE backward"; "FP8 training on AMD GPUs with TorchTitan and
- * TorchAO" Figure 1 caption: the weight-update GEMM stays in BF16; section
+/* Grouped BF16 weight gradient of an MoE layer over device offsets, the
+ * weight side of the grouped GEMM's backward ["FP8 training on AMD GPUs with
+ * TorchTitan and TorchAO" Figure 1 caption: the weight-update GEMM stays in
+ * BF16; section
  * "Scaling FP8 to MoE Architectures": expert e owns rows [off[e], off[e+1])]:
  *   gw[e][n][k] = sum over m in [off[e], off[e+1]) of gy[m][n] * x[m][k],
  * fp32 accumulation, bf16 out (RNE); an expert with no rows gets zeros.
