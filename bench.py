@@ -11,7 +11,8 @@ already resident in HBM:
                      the FP8 weight-gradient GEMM and the whole fp8_linear_bwd call
   expert_colwise     per-expert column scales + transposed cast, 32 x [2048,7168]
   moe_grouped        rowwise quant of A [131072,7168] and of W [32][2048][7168] (per
-                     expert column), FP8 grouped GEMM over int32[33] offsets -> bf16; beside
+                     expert column; W's codes k-packed, 1 KB chunks of 16 rows x 64 K),
+                     FP8 grouped GEMM over int32[33] offsets -> bf16; beside
                      it (per row, outside the aggregates) the layer's backward: grad_out
                      [131072,2048] per-row e5m2, the grouped grad-input GEMM against
                      expert_colwise's transposed per-column weights, the grouped BF16
@@ -197,10 +198,12 @@ def build_step(f, torch, dev, wls, dev_of):
     out4 = torch.empty((Mt, N4), **bf)
     st.add("moe_grouped.quant_row_a", "quant", 3 * Mt * K4 + 8 * Mt,
            lambda: f.fp8_quant_row(a4, E4, EPS, qa4, sa4, ia4))
+    # the weights' codes k-packed (1 KB chunks of 16 rows x 64 K) by their
+    # quantization, the layout the grouped GEMM loads B from in whole lines
     st.add("moe_grouped.quant_expert_cols_w", "quant", 3 * E4n * N4 * K4 + 8 * E4n * N4,
-           lambda: f.fp8_quant_row(we4, E4, EPS, qw4, sw4, iw4))
+           lambda: f.fp8_quant_row_kpacked(we4, E4, EPS, qw4, sw4, iw4))
     st.add("moe_grouped.grouped_gemm", "gemm8", 2.0 * Mt * N4 * K4,
-           lambda: f.fp8_grouped_mm(qa4, E4, qw4, E4, f.SCALE_ROW, ia4, iw4, off4, f.OUT_BF16, out4))
+           lambda: f.fp8_grouped_mm_kpacked(qa4, E4, qw4, E4, f.SCALE_ROW, ia4, iw4, off4, f.OUT_BF16, out4, N4))
 
     # ---- the MoE layer's backward on the same routing (outside the
     # aggregates): grad_out quantized per row (e5m2); grouped grad-input
@@ -481,7 +484,7 @@ def build_step_subset(f, torch, dev, wls, dev_of):
         "linear_tensorwise": synth.linear_tensorwise,
         "linear_rowwise": lambda: synth.linear_rowwise(M=64, K=64, N=64),
         "expert_colwise": lambda: synth.expert_colwise(E=1, R=64, C=64),
-        "moe_grouped": lambda: synth.moe_grouped(tokens=64, topk=2, E=4, N=64, K=64, n_empty=0),
+        "moe_grouped": lambda: synth.moe_grouped(tokens=64, topk=2, E=4, N=64, K=128, n_empty=0),
         "moe_block_mx": lambda: synth.moe_block_mx(E=2, K=256, N=256, rows=64),
     }
     allw = {n: (wls[n] if n in wls else small[n]()) for n in full_names}

@@ -24,11 +24,11 @@ RECIPE_TENSORWISE, RECIPE_ROWWISE_BF16_WGRAD = range(2)
 
 EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
-    "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_col",
+    "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_col",
     "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
     "fp8_quant_block", "fp8_quant_mx",
     "fp8_scaled_mm",
-    "fp8_grouped_mm", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
+    "fp8_grouped_mm", "fp8_grouped_mm_kpacked", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
 ]
 
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_tensor": (I, [P, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_tensor_ws_bytes": (SZ, []),
         "fp8_quant_row": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
+        "fp8_quant_row_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
         "fp8_quant_dual": (I, [P, P, I64, I64, I64, I, I, D, P, P, P, P, P, P, P, P, SZ, P]),
@@ -71,6 +72,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_mx": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
         "fp8_scaled_mm": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
         "fp8_grouped_mm": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, P]),
+        "fp8_grouped_mm_kpacked": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, P]),
         "fp8_wgrad_bf16": (I, [P, P, I64, I64, I64, P, P]),
         "fp8_grouped_wgrad_bf16": (I, [P, P, P, I32, I64, I64, I64, P, P]),
         "fp8_linear_fwd": (I, [P, P, I64, I64, I64, I, D, I, P, P, SZ, P]),
@@ -152,6 +154,16 @@ def fp8_quant_row(x, fmt, eps, q, scale, inv_scale=None, stream=None):
         _ptr(x), b, r, c, int(fmt), float(eps), _ptr(q), _ptr(scale), _ptr(inv_scale), _stream(stream)))
 
 
+def fp8_quant_row_kpacked(x, fmt, eps, q, scale, inv_scale=None, stream=None):
+    """fp8_quant_row with the codes in 1 KB chunks of 16 rows x 64 columns (q: any
+    uint8 tensor of x.numel() bytes); the B layout of fp8_grouped_mm_kpacked."""
+    b, r, c = _brc(x)
+    if q.numel() * q.element_size() != b * r * c:
+        raise ValueError("fp8_quant_row_kpacked: q must hold one byte per element of x")
+    _check("fp8_quant_row_kpacked", load().fp8_quant_row_kpacked(
+        _ptr(x), b, r, c, int(fmt), float(eps), _ptr(q), _ptr(scale), _ptr(inv_scale), _stream(stream)))
+
+
 def fp8_quant_col_ws_bytes(batch: int, rows: int, cols: int) -> int:
     return load().fp8_quant_col_ws_bytes(int(batch), int(rows), int(cols))
 
@@ -215,6 +227,18 @@ def fp8_grouped_mm(a, fa, b, fb, scaling, a_scale, b_scale, offsets, out_type, o
     Mtot, K = a.shape
     E, N, _ = b.shape
     _check("fp8_grouped_mm", load().fp8_grouped_mm(
+        _ptr(a), int(fa), _ptr(b), int(fb), int(scaling), _ptr(a_scale), _ptr(b_scale),
+        _ptr(offsets), E, Mtot, N, K, int(out_type), _ptr(out), _stream(stream)))
+
+
+def fp8_grouped_mm_kpacked(a, fa, b, fb, scaling, a_scale, b_scale, offsets, out_type, out, N, stream=None):
+    """fp8_grouped_mm with b k-packed (fp8_quant_row_kpacked's layout of the [E][N][K]
+    codes); b is any uint8 tensor of E * N * K bytes with b.shape[0] == E."""
+    Mtot, K = a.shape
+    E = b.shape[0]
+    if b.numel() * b.element_size() != E * N * K:
+        raise ValueError("fp8_grouped_mm_kpacked: b must hold E * N * K bytes")
+    _check("fp8_grouped_mm_kpacked", load().fp8_grouped_mm_kpacked(
         _ptr(a), int(fa), _ptr(b), int(fb), int(scaling), _ptr(a_scale), _ptr(b_scale),
         _ptr(offsets), E, Mtot, N, K, int(out_type), _ptr(out), _stream(stream)))
 

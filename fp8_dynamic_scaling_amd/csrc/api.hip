@@ -220,6 +220,21 @@ fp8_status fp8_quant_row(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   return dev_err(launch_quant_row(a));
 }
 
+fp8_status fp8_quant_row_kpacked(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                 double eps, uint8_t* q, float* scale, float* inv_scale, void* stream) {
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
+  if (st != FP8_OK) return st;
+  if (rows % 16 != 0 || cols % 64 != 0) return FP8_ERR_ALIGNMENT;
+  if (cols > 16384) return FP8_ERR_UNSUPPORTED;
+  if (cols == 0) return empty_group_scales(fmt, false, eps, scale, inv_scale, batch * rows, stream);
+  if (batch * rows == 0) return FP8_OK;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_row_kpacked(a));
+}
+
 fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
                          uint8_t* qT, float* scale, float* inv_scale, void* ws, size_t ws_bytes, void* stream) {
   fp8_status st = check_quant_common(x, batch, rows, cols, eps, qT, scale);
@@ -380,6 +395,28 @@ fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8
   GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
   return dev_err(launch_gemm_fp8(g));
+}
+
+fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
+                                  fp8_scaling scaling, const void* a_scale, const void* b_scale,
+                                  const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N, int64_t K,
+                                  fp8_out out_type, void* out, void* stream) {
+  if (scaling != FP8_SCALE_ROW && scaling != FP8_SCALE_MX32) return FP8_ERR_UNSUPPORTED;
+  if (E < 1 || E > 1024) return FP8_ERR_INVALID_ARGUMENT;
+  fp8_status st = check_gemm(a, b, a_scale, b_scale, Mtot, N, K, scaling, out_type, out);
+  if (st != FP8_OK || Mtot == 0 || N == 0) return st;
+  if (!offsets) return FP8_ERR_INVALID_ARGUMENT;
+  if (!aligned(offsets, 4)) return FP8_ERR_ALIGNMENT;
+  if (N % 16 != 0 || K % 128 != 0) return FP8_ERR_ALIGNMENT;
+  if (N * K >= ((int64_t)1 << 31)) return FP8_ERR_UNSUPPORTED;  // 32-bit offsets in an expert's B
+  bool ea, eb;
+  double fm;
+  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
+  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+             (hipStream_t)stream, true};
+  if (!gemm_fp8_fast_eligible(g)) return FP8_ERR_UNSUPPORTED;
+  return dev_err(launch_gemm_fp8_fast(g));
 }
 
 fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N, int64_t K, uint16_t* gw,

@@ -60,7 +60,7 @@ namespace fp8dyn {
 //    otherwise a stage pair's bytes (one dword per row, 128-deep K) ride in a
 //    ring of 4 pairs with each even stage's loads. Each lane reads its byte
 //    straight into the MFMA's scale operand in the memory phase.
-template <bool AE5, bool BE5, int SK, bool OF32, bool GR>
+template <bool AE5, bool BE5, int SK, bool OF32, bool GR, bool PKB>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 64, NS = 4;
   constexpr int TM = 128, TN = 64, MI = TM / 32, NI = TN / 32;
@@ -136,15 +136,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     const int32_t K32 = (int32_t)K;
     const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);
     const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
-    const uint8_t* base = grp == 0 ? p.a + ti.m0 * K : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    // B k-packed: the expert's [N][K] codes as 1 KB chunks of 16 rows x 64 K,
+    // chunk (n / 16, k / 64) at ((n / 16) * (K / 64) + k / 64) * 1024, so one
+    // stage's load of 16 rows is one contiguous KB (whole cache lines) and the
+    // next stage is 1 KB further
+    const bool pk = PKB && grp == 1;
+    const uint8_t* base = grp == 0 ? p.a + ti.m0 * K
+                          : pk     ? p.b + (int64_t)ti.e * N * K
+                                   : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    const int64_t sstride = pk ? 1024 : BK;
     const int32_t rows = grp == 0 ? a_rows : b_rows;
     uint32_t off[DH];
 #pragma unroll
     for (int d = 0; d < DH; ++d) {
       const int r = 64 * wn + 16 * d + ld_row;
       const int c = ld_pch ^ ((r >> 2) & 3);
-      const int32_t rr = r < rows ? r : rows - 1;
-      off[d] = (uint32_t)(rr * K32 + 16 * c);
+      if (pk) {
+        // groups past N (N % 16 == 0) fetch the last group; never stored
+        int64_t gi = ti.n0 / 16 + 4 * wn + d;
+        gi = gi < N / 16 ? gi : N / 16 - 1;
+        off[d] = (uint32_t)(gi * (K / 64) * 1024 + ld_row * 64 + 16 * c);
+      } else {
+        const int32_t rr = r < rows ? r : rows - 1;
+        off[d] = (uint32_t)(rr * K32 + 16 * c);
+      }
     }
     const uint32_t part_lds = (grp == 0 ? 0u : (uint32_t)SA_BYTES) + (uint32_t)(wn * 4096);
     // MX: this wave's 64 rows (those of its stage loads) of its operand's
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     // the loads of stage s (and, s even, the scales of its pair)
     auto issue = [&](int64_t s) {
       const uint32_t slot = lds0 + (uint32_t)((s & (NS - 1)) * STAGE) + part_lds;
-      const uint8_t* bk = base + s * BK;
+      const uint8_t* bk = base + s * sstride;
 #pragma unroll
       for (int d = 0; d < DH; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
       if constexpr (MXS) {
@@ -591,10 +606,15 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
   if constexpr (SK == kScaleBlock) {
     hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
   } else {
-    if (g.offsets)
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+    if (g.offsets && g.b_kpacked)
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, true>), dim3((unsigned)grid), dim3(512), 0, g.stream,
+                         p);
+    else if (g.offsets)
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, false>), dim3((unsigned)grid), dim3(512), 0,
+                         g.stream, p);
     else
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, false>), dim3((unsigned)grid), dim3(512), 0,
+                         g.stream, p);
   }
   return hipGetLastError();
 }

@@ -56,6 +56,52 @@ __global__ __launch_bounds__(256) void k_quant_row(const uint16_t* __restrict__ 
   }
 }
 
+// Rowwise groups with the codes written k-packed: row r, column c of a batch
+// slice's [rows][cols] codes lands at ((r / 16) * (cols / 64) + c / 64) * 1024
+// + (r % 16) * 64 + c % 64, i.e. 1 KB chunks of 16 rows x 64 columns (the
+// layout the grouped GEMM loads a stage of B from in whole cache lines). One
+// 256-thread workgroup per row as in k_quant_row; a row's 64-byte pieces are
+// half lines whose other halves belong to the neighbouring row, so rows are
+// dealt to XCDs in contiguous ranges (workgroup i runs on XCD i % 8) and the
+// two halves meet in one L2; plain stores let it merge them.
+template <int J, bool E5>
+__global__ __launch_bounds__(256) void k_quant_row_kpacked(const uint16_t* __restrict__ x, int64_t nrows,
+                                                           int64_t cols, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale, float* __restrict__ inv,
+                                                           double fmax, double eps) {
+  __shared__ float red[4];
+  const int64_t G = gridDim.x;
+  int64_t row = blockIdx.x;
+  if (G % 8 == 0) row = (row % 8) * (G / 8) + row / 8;
+  const uint16_t* xr = x + row * cols;
+  // chunk row (row / 16, 0) of the packed codes, then this row's 64 bytes in it
+  uint8_t* qg = q + (row / 16) * 16 * cols + (row % 16) * 64;
+  const int tid = threadIdx.x;
+  uint4 v[J];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(tid + 256 * j) * 8;
+    if (c < cols) {
+      v[j] = ld_nt16(xr + c);
+      m = amax8(v[j], m);
+    }
+  }
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, fmax, eps, s, iv);
+  if (tid == 0) {
+    scale[row] = s;
+    if (inv) inv[row] = iv;
+  }
+  const float fm = (float)fmax;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = (int64_t)(tid + 256 * j) * 8;
+    if (c < cols) *reinterpret_cast<uint2*>(qg + (c / 64) * 1024 + c % 64) = quant8<E5>(v[j], s, fm);
+  }
+}
+
 // Row groups, one wavefront per row (4 rows per 256-thread workgroup): the
 // row (up to 512 * J elements) stays in registers, the amax is reduced with
 // wavefront shuffles only (no LDS, no workgroup barrier), so each wave
@@ -686,6 +732,32 @@ static hipError_t launch_row_t(const QuantArgs& a) {
 }
 
 hipError_t launch_quant_row(const QuantArgs& a) { return a.e5 ? launch_row_t<true>(a) : launch_row_t<false>(a); }
+
+// rows % 16 == 0 and cols % 64 == 0 (the caller checks), cols <= 16384
+template <bool E5>
+static hipError_t launch_row_kpacked_t(const QuantArgs& a) {
+  const int64_t R = a.batch * a.rows, C = a.cols;
+  if (R == 0 || C == 0) return hipSuccess;
+  dim3 grid((unsigned)R), block(256);
+  const int64_t J = (C + 2047) / 2048;
+  if (J <= 1)
+    hipLaunchKernelGGL((k_quant_row_kpacked<1, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+                       a.eps);
+  else if (J <= 2)
+    hipLaunchKernelGGL((k_quant_row_kpacked<2, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+                       a.eps);
+  else if (J <= 4)
+    hipLaunchKernelGGL((k_quant_row_kpacked<4, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+                       a.eps);
+  else
+    hipLaunchKernelGGL((k_quant_row_kpacked<8, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+                       a.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row_kpacked(const QuantArgs& a) {
+  return a.e5 ? launch_row_kpacked_t<true>(a) : launch_row_kpacked_t<false>(a);
+}
 
 // The fused form (one workgroup per 64-column strip over all rows) when it
 // gives enough workgroups to fill the chip, else the split form over row

@@ -87,6 +87,20 @@ def test_host_validation_without_gpu(f):
     assert lib.fp8_grouped_mm(*args, f.SCALE_MX32, FAKE, FAKE, FAKE, 2, 16, 128, 48, f.OUT_BF16, FAKE, None) == f.ERR_ALIGNMENT
     assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 0, 16, 128, 64, f.OUT_BF16, FAKE, None) == f.ERR_INVALID_ARGUMENT
     assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, None, 2, 16, 128, 64, f.OUT_BF16, FAKE, None) == f.ERR_INVALID_ARGUMENT
+    # k-packed rowwise codes: rows % 16, cols % 64, at most 16384 columns
+    kp = (f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None)
+    assert lib.fp8_quant_row_kpacked(FAKE, 1, 8, 64, *kp) == f.ERR_ALIGNMENT
+    assert lib.fp8_quant_row_kpacked(FAKE, 1, 16, 32, *kp) == f.ERR_ALIGNMENT
+    assert lib.fp8_quant_row_kpacked(FAKE, 1, 16, 16448, *kp) == f.ERR_UNSUPPORTED
+    # k-packed grouped GEMM: ROW or MX32 only, N % 16, K % 128, N * K < 2^31
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_BLOCK128, FAKE, FAKE, FAKE, 2, 16, 128, 128, f.OUT_BF16, FAKE,
+                                      None) == f.ERR_UNSUPPORTED
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 40, 128, f.OUT_BF16, FAKE,
+                                      None) == f.ERR_ALIGNMENT
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 64, 64, f.OUT_BF16, FAKE,
+                                      None) == f.ERR_ALIGNMENT
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 65536, 32768, f.OUT_BF16, FAKE,
+                                      None) == f.ERR_UNSUPPORTED
     # linear: workspace too small
     need = lib.fp8_linear_ws_bytes(64, 64, 64, f.RECIPE_ROWWISE_BF16_WGRAD)
     assert need > 64 * 64 * 2

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import check_gemm, gpu, have_gpu, lib, to_dev, to_dev_bf16, u8
+from tests.gpu_util import check_gemm, gpu, have_gpu, kpack, lib, to_dev, to_dev_bf16, u8
 
 pytestmark = [gpu, pytest.mark.skipif(not have_gpu(), reason="needs an MI355X")]
 EPS = 1e-12
@@ -219,14 +219,26 @@ def test_moe_grouped_forward(f):
     f.fp8_quant_row(wd, f.E4M3_NATIVE, EPS, qw, sw, iw)
     out = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ia, iw, to_dev(off), f.OUT_BF16, out)
+    # the k-packed weight path the benchmark times: quantization into 1 KB
+    # chunks of 16 rows x 64 K, then the grouped GEMM reading them
+    qwp = torch.empty((E, N * K), dtype=torch.uint8, device="cuda:0")
+    swp, iwp = torch.empty_like(sw), torch.empty_like(iw)
+    f.fp8_quant_row_kpacked(wd, f.E4M3_NATIVE, EPS, qwp, swp, iwp)
+    outp = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm_kpacked(qa, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, ia, iwp, to_dev(off), f.OUT_BF16,
+                             outp, N)
     torch.cuda.synchronize()
     del ad, wd
+    assert torch.equal(outp.view(torch.int16), out.view(torch.int16)), "k-packed GEMM differs from row-major"
+    assert torch.equal(iwp, iw) and torch.equal(swp, sw)
+    del outp
     r_qa, _, r_ia = oracle.quant_row(a, e4, EPS)
     assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
     del a
     r_qw, _, r_iw = oracle.quant_row(w, e4, EPS)
     assert np.array_equal(u8(qw), r_qw) and np.array_equal(iw.cpu().numpy(), r_iw)
-    _log("moe_grouped quantization bit-exact")
+    assert np.array_equal(u8(qwp).reshape(-1), kpack(r_qw))
+    _log("moe_grouped quantization bit-exact (row-major and k-packed)")
     r, c = _samples(Mt, N, 4, offsets=off)
     ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c)
     S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c, absolute=True)
