@@ -4,8 +4,9 @@ One step runs every step of the path over the five synthetic workloads, inputs
 already resident in HBM:
   linear_tensorwise  fp8_linear_fwd, X [256,512] W [512,512], one scale each, fp32 out
   linear_rowwise     Llama3-8B MLP (tokens 8192, K 4096, N 14336): rowwise quant of X, W
-                     (e4m3) and grad_out (e5m2), per-column transposed quant of W, FP8
-                     forward and grad-input GEMMs, BF16 weight-gradient GEMM; beside it
+                     (e4m3) and grad_out (e5m2), per-column transposed quant of W (both
+                     W codes k-packed), FP8 forward and grad-input GEMMs, BF16
+                     weight-gradient GEMM; beside it
                      (reported per row, outside the aggregates) the all-FP8 tensorwise
                      backward of the same layer: the dual quantization of grad_out and X,
                      the FP8 weight-gradient GEMM and the whole fp8_linear_bwd call
@@ -128,16 +129,18 @@ def build_step(f, torch, dev, wls, dev_of):
     gw2 = torch.empty((N, K), **bf)
     st.add("linear_rowwise.quant_row_x", "quant", 3 * M * K + 8 * M,
            lambda: f.fp8_quant_row(x2, E4, EPS, qx, sx, ix))
+    # W's codes k-packed by both of its quantizations (1 KB chunks of 16 rows
+    # x 64 K of the GEMM's B operand): the forward's and the grad-input's
     st.add("linear_rowwise.quant_row_w", "quant", 3 * N * K + 8 * N,
-           lambda: f.fp8_quant_row(wt2, E4, EPS, qw, sw, iw))
+           lambda: f.fp8_quant_row_kpacked(wt2, E4, EPS, qw, sw, iw))
     st.add("linear_rowwise.gemm_fwd", "gemm8", 2.0 * M * N * K,
-           lambda: f.fp8_scaled_mm(qx, E4, qw, E4, f.SCALE_ROW, ix, iw, f.OUT_BF16, y2))
+           lambda: f.fp8_scaled_mm_kpacked(qx, E4, qw, E4, f.SCALE_ROW, ix, iw, f.OUT_BF16, y2, N))
     st.add("linear_rowwise.quant_row_gy_e5m2", "quant", 3 * M * N + 8 * M,
            lambda: f.fp8_quant_row(g2, E5, EPS, qg, sg, ig))
     st.add("linear_rowwise.quant_col_w", "quant", 3 * N * K + 8 * K,
-           lambda: f.fp8_quant_col(wt2, E4, EPS, qwt, swc, iwc, colws))
+           lambda: f.fp8_quant_col_kpacked(wt2, E4, EPS, qwt, swc, iwc, colws))
     st.add("linear_rowwise.gemm_dgrad", "gemm8", 2.0 * M * N * K,
-           lambda: f.fp8_scaled_mm(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2, use_fast_accum=False))
+           lambda: f.fp8_scaled_mm_kpacked(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2, K))
     st.add("linear_rowwise.wgrad_bf16", "gemm16", 2.0 * M * N * K,
            lambda: f.fp8_wgrad_bf16(g2, x2, gw2))
 
@@ -482,7 +485,7 @@ def build_step_subset(f, torch, dev, wls, dev_of):
         return build_step(f, torch, dev, wls, dev_of)
     small = {
         "linear_tensorwise": synth.linear_tensorwise,
-        "linear_rowwise": lambda: synth.linear_rowwise(M=64, K=64, N=64),
+        "linear_rowwise": lambda: synth.linear_rowwise(M=64, K=128, N=128),
         "expert_colwise": lambda: synth.expert_colwise(E=1, R=64, C=64),
         "moe_grouped": lambda: synth.moe_grouped(tokens=64, topk=2, E=4, N=64, K=128, n_empty=0),
         "moe_block_mx": lambda: synth.moe_block_mx(E=2, K=256, N=256, rows=64),

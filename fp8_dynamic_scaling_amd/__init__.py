@@ -25,9 +25,10 @@ RECIPE_TENSORWISE, RECIPE_ROWWISE_BF16_WGRAD = range(2)
 EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_col",
+    "fp8_quant_col_kpacked",
     "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
     "fp8_quant_block", "fp8_quant_mx",
-    "fp8_scaled_mm",
+    "fp8_scaled_mm", "fp8_scaled_mm_kpacked",
     "fp8_grouped_mm", "fp8_grouped_mm_kpacked", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
 ]
@@ -64,6 +65,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_row": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_row_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
+        "fp8_quant_col_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
         "fp8_quant_dual": (I, [P, P, I64, I64, I64, I, I, D, P, P, P, P, P, P, P, P, SZ, P]),
         "fp8_norm_quant_row": (I, [P, P, P, I64, I64, I, D, I, D, P, P, P, P, P]),
@@ -71,6 +73,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_block": (I, [P, I64, I64, I64, I, I, I, D, P, P, P, P]),
         "fp8_quant_mx": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
         "fp8_scaled_mm": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
+        "fp8_scaled_mm_kpacked": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, P]),
         "fp8_grouped_mm": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, P]),
         "fp8_grouped_mm_kpacked": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, P]),
         "fp8_wgrad_bf16": (I, [P, P, I64, I64, I64, P, P]),
@@ -178,6 +181,17 @@ def fp8_quant_col(x, fmt, eps, qT, scale, inv_scale=None, ws=None, stream=None):
 NORM_RMS, NORM_LAYER = 0, 1
 
 
+def fp8_quant_col_kpacked(x, fmt, eps, qT, scale, inv_scale=None, ws=None, stream=None):
+    """fp8_quant_col with qT k-packed as the [cols][rows] B operand (qT: any uint8
+    tensor of x.numel() bytes)."""
+    b, r, c = _brc(x)
+    if qT.numel() * qT.element_size() != b * r * c:
+        raise ValueError("fp8_quant_col_kpacked: qT must hold one byte per element of x")
+    _check("fp8_quant_col_kpacked", load().fp8_quant_col_kpacked(
+        _ptr(x), b, r, c, int(fmt), float(eps), _ptr(qT), _ptr(scale), _ptr(inv_scale),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def fp8_norm_quant_row(x, gamma, beta, kind, norm_eps, fmt, eps, y, q, scale, inv_scale=None, stream=None):
     """x [rows][cols] bf16 -> y (bf16, or None), q/scale/inv (rowwise FP8 of y, or q None)."""
     rows, cols = x.shape
@@ -229,6 +243,17 @@ def fp8_grouped_mm(a, fa, b, fb, scaling, a_scale, b_scale, offsets, out_type, o
     _check("fp8_grouped_mm", load().fp8_grouped_mm(
         _ptr(a), int(fa), _ptr(b), int(fb), int(scaling), _ptr(a_scale), _ptr(b_scale),
         _ptr(offsets), E, Mtot, N, K, int(out_type), _ptr(out), _stream(stream)))
+
+
+def fp8_scaled_mm_kpacked(a, fa, b, fb, scaling, a_inv, b_inv, out_type, out, N, stream=None):
+    """fp8_scaled_mm with b k-packed ([N][K] codes in 1 KB chunks of 16 rows x 64 K);
+    b is any uint8 tensor of N * K bytes."""
+    M, K = a.shape
+    if b.numel() * b.element_size() != N * K:
+        raise ValueError("fp8_scaled_mm_kpacked: b must hold N * K bytes")
+    _check("fp8_scaled_mm_kpacked", load().fp8_scaled_mm_kpacked(
+        _ptr(a), int(fa), _ptr(b), int(fb), int(scaling), _ptr(a_inv), _ptr(b_inv), M, N, K,
+        int(out_type), _ptr(out), _stream(stream)))
 
 
 def fp8_grouped_mm_kpacked(a, fa, b, fb, scaling, a_scale, b_scale, offsets, out_type, out, N, stream=None):

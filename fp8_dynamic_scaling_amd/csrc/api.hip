@@ -254,6 +254,27 @@ fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   return dev_err(launch_quant_col(a, ws));
 }
 
+fp8_status fp8_quant_col_kpacked(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                 double eps, uint8_t* qT, float* scale, float* inv_scale, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, qT, scale);
+  if (st != FP8_OK) return st;
+  if (rows % 64 != 0 || cols % 16 != 0) return FP8_ERR_ALIGNMENT;
+  if (rows * cols >= ((int64_t)1 << 30)) return FP8_ERR_UNSUPPORTED;  // 32-bit offsets in a batch slice
+  if (rows == 0) return empty_group_scales(fmt, false, eps, scale, inv_scale, batch * cols, stream);
+  if (batch * cols == 0) return FP8_OK;
+  const size_t need = quant_col_ws_bytes(batch, rows, cols);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return FP8_ERR_WORKSPACE;
+    if (!aligned(ws, 4)) return FP8_ERR_ALIGNMENT;
+  }
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, qT, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_col_kpacked(a, ws));
+}
+
 fp8_status fp8_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
                               int64_t cols, fp8_norm kind, double norm_eps, fp8_format fmt, double eps, uint16_t* y,
                               uint8_t* q, float* scale, float* inv_scale, void* stream) {
@@ -395,6 +416,24 @@ fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8
   GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
   return dev_err(launch_gemm_fp8(g));
+}
+
+fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
+                                 fp8_scaling scaling, const float* a_inv, const float* b_inv, int64_t M, int64_t N,
+                                 int64_t K, fp8_out out_type, void* out, void* stream) {
+  if (scaling != FP8_SCALE_TENSOR && scaling != FP8_SCALE_ROW) return FP8_ERR_UNSUPPORTED;
+  fp8_status st = check_gemm(a, b, a_inv, b_inv, M, N, K, scaling, out_type, out);
+  if (st != FP8_OK || M == 0 || N == 0) return st;
+  if (N % 16 != 0 || K % 128 != 0) return FP8_ERR_ALIGNMENT;
+  if (N * K >= ((int64_t)1 << 31)) return FP8_ERR_UNSUPPORTED;  // 32-bit offsets in B
+  bool ea, eb;
+  double fm;
+  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
+  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+             (hipStream_t)stream, true};
+  if (!gemm_fp8_fast_eligible(g)) return FP8_ERR_UNSUPPORTED;
+  return dev_err(launch_gemm_fp8_fast(g));
 }
 
 fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,

@@ -136,8 +136,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     const int32_t K32 = (int32_t)K;
     const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);
     const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
-    // B k-packed: the expert's [N][K] codes as 1 KB chunks of 16 rows x 64 K,
-    // chunk (n / 16, k / 64) at ((n / 16) * (K / 64) + k / 64) * 1024, so one
+    // B k-packed: the expert's (or the dense) [N][K] codes as 1 KB chunks of
+    // 16 rows x 64 K, chunk (n / 16, k / 64) at ((n / 16) * (K / 64) + k / 64)
+    // * 1024, so one
     // stage's load of 16 rows is one contiguous KB (whole cache lines) and the
     // next stage is 1 KB further
     const bool pk = PKB && grp == 1;
@@ -611,6 +612,9 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
                          p);
     else if (g.offsets)
       hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, false>), dim3((unsigned)grid), dim3(512), 0,
+                         g.stream, p);
+    else if (g.b_kpacked)
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, true>), dim3((unsigned)grid), dim3(512), 0,
                          g.stream, p);
     else
       hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, false>), dim3((unsigned)grid), dim3(512), 0,

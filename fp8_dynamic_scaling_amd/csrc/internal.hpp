@@ -26,6 +26,8 @@ hipError_t launch_quant_row(const QuantArgs& a);
 // codes k-packed (1 KB chunks of 16 rows x 64 columns); rows % 16 == 0, cols % 64 == 0, cols <= 16384
 hipError_t launch_quant_row_kpacked(const QuantArgs& a);
 hipError_t launch_quant_col(const QuantArgs& a, void* ws);
+// qT k-packed as the [cols][rows] B operand; rows % 64 == 0, cols % 16 == 0, the vector path's conditions
+hipError_t launch_quant_col_kpacked(const QuantArgs& a, void* ws);
 size_t quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
 hipError_t launch_quant_tensor(const QuantArgs& a, void* ws);  // ws >= 256 bytes
 // tensorwise scale, transposed output qT[b][c][r]; needs cols % 8 == 0, rows % 16 == 0
@@ -91,7 +93,7 @@ struct GemmArgs {
   bool out_f32;
   void* out;          // [M][N]
   hipStream_t stream;
-  bool b_kpacked = false;  // B in 1 KB chunks of 16 rows x 64 K (grouped, fast kernel only)
+  bool b_kpacked = false;  // B in 1 KB chunks of 16 rows x 64 K (fast kernel, ROW/TENSOR/MX scales)
 };
 hipError_t launch_gemm_fp8(const GemmArgs& g);
 // the direct-to-LDS kernel (K % 128 == 0, aligned operands); launch_gemm_fp8 picks it

@@ -190,7 +190,20 @@ __global__ __launch_bounds__(256) void k_quant_row_generic(const uint16_t* __res
 constexpr int kColRPT = 16;     // rows per thread in pass 2
 constexpr int kColChunk = 1024; // rows per workgroup in the split form
 
-template <bool E5, int MODE>
+// The 16 codes of column n, rows k0 .. k0 + 15 (k0 % 16 == 0) of a transposed
+// [N][K] operand: k-packed (1 KB chunks of 16 n x 64 k, see k_quant_row_kpacked)
+// with a plain store, so the L2 merges the half lines of neighbouring n; else
+// row-major with a non-temporal store.
+template <bool PK>
+__device__ __forceinline__ void store_col16(uint8_t* qs, uint32_t n, uint32_t k0, uint32_t K, const uint4& v) {
+  if constexpr (PK) {
+    *reinterpret_cast<uint4*>(qs + ((n >> 4) * (K >> 6) + (k0 >> 6)) * 1024u + (n & 15u) * 64u + (k0 & 63u)) = v;
+  } else {
+    st_nt16(qs + n * K + k0, v);
+  }
+}
+
+template <bool E5, int MODE, bool PK = false>
 __global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                    int64_t strips, int64_t rchunks, int64_t rows_per_blk,
                                                    uint8_t* __restrict__ qT, float* __restrict__ scale,
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      st_nt16(qs + (uint32_t)(l8 * 8 + i) * R32 + r0, make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
+      store_col16<PK>(qs, (uint32_t)(l8 * 8 + i), r0, R32, make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]));
   }
 }
 
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict
 #endif
 constexpr int kColCW = FP8DYN_COL_CW;
 
-template <bool E5, int CW>
+template <bool E5, int CW, bool PK = false>
 __global__ __launch_bounds__(2048 / 16 * (CW / 8)) void k_quant_col_reg(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t strips, uint8_t* __restrict__ qT,
     float* __restrict__ scale, float* __restrict__ inv, double fmax, double eps) {
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(2048 / 16 * (CW / 8)) void k_quant_col_reg(
     o.y = cvt4<E5>(f[4], f[5], f[6], f[7]);
     o.z = cvt4<E5>(f[8], f[9], f[10], f[11]);
     o.w = cvt4<E5>(f[12], f[13], f[14], f[15]);
-    st_nt16(qs + (uint32_t)(lc * 8 + i) * R32 + (uint32_t)r0, o);
+    store_col16<PK>(qs, (uint32_t)(lc * 8 + i), (uint32_t)r0, R32, o);
   }
 }
 
@@ -772,7 +785,7 @@ size_t quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
   return (size_t)(batch * cols) * sizeof(uint32_t);
 }
 
-template <bool E5>
+template <bool E5, bool PK>
 static hipError_t launch_col_t(const QuantArgs& a, uint32_t* colmax) {
   const int64_t B = a.batch, R = a.rows, C = a.cols;
   if (B == 0 || R == 0 || C == 0) return hipSuccess;
@@ -788,13 +801,13 @@ static hipError_t launch_col_t(const QuantArgs& a, uint32_t* colmax) {
     // kColCW / 8 threads per 16-row group, whole waves
     int64_t threads = (R / kColRPT) * (kColCW / 8);
     threads = (threads + 63) / 64 * 64;
-    hipLaunchKernelGGL((k_quant_col_reg<E5, kColCW>), dim3((unsigned)(B * stripsw)), dim3((unsigned)threads), 0,
+    hipLaunchKernelGGL((k_quant_col_reg<E5, kColCW, PK>), dim3((unsigned)(B * stripsw)), dim3((unsigned)threads), 0,
                        a.stream, a.x, R, C, stripsw, a.q, a.scale, a.inv, a.fmax, a.eps);
     return hipGetLastError();
   }
   const int64_t strips = (C + 63) / 64;
   if (!col_split(B, R, C)) {
-    hipLaunchKernelGGL((k_quant_col<E5, 0>), dim3((unsigned)(B * strips)), dim3(256), 0, a.stream, a.x, R, C,
+    hipLaunchKernelGGL((k_quant_col<E5, 0, PK>), dim3((unsigned)(B * strips)), dim3(256), 0, a.stream, a.x, R, C,
                        strips, (int64_t)1, R, a.q, a.scale, a.inv, (uint32_t*)nullptr, (int64_t)1, a.fmax, a.eps);
     return hipGetLastError();
   }
@@ -803,7 +816,7 @@ static hipError_t launch_col_t(const QuantArgs& a, uint32_t* colmax) {
   hipLaunchKernelGGL(k_clear_words, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, a.stream, colmax, nwords);
   hipLaunchKernelGGL((k_quant_col<E5, 2>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
                      strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
-  hipLaunchKernelGGL((k_quant_col<E5, 1>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
+  hipLaunchKernelGGL((k_quant_col<E5, 1, PK>), dim3((unsigned)(B * strips * rchunks)), dim3(256), 0, a.stream, a.x, R, C,
                      strips, rchunks, (int64_t)kColChunk, a.q, a.scale, a.inv, colmax, (int64_t)1, a.fmax, a.eps);
   return hipGetLastError();
 }
@@ -833,7 +846,11 @@ hipError_t launch_quant_tensor_transposed(const QuantArgs& a, void* ws) {
 }
 
 hipError_t launch_quant_col(const QuantArgs& a, void* ws) {
-  return a.e5 ? launch_col_t<true>(a, (uint32_t*)ws) : launch_col_t<false>(a, (uint32_t*)ws);
+  return a.e5 ? launch_col_t<true, false>(a, (uint32_t*)ws) : launch_col_t<false, false>(a, (uint32_t*)ws);
+}
+
+hipError_t launch_quant_col_kpacked(const QuantArgs& a, void* ws) {
+  return a.e5 ? launch_col_t<true, true>(a, (uint32_t*)ws) : launch_col_t<false, true>(a, (uint32_t*)ws);
 }
 
 template <bool E5>

@@ -175,6 +175,16 @@ FP8DYN_API fp8_status fp8_quant_row_kpacked(const uint16_t* x, int64_t batch, in
 FP8DYN_API fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                     fp8_format fmt, double eps, uint8_t* qT, float* scale,
                                     float* inv_scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Column groups as fp8_quant_col (same scales, same codes), with qT written
+ * k-packed as the [cols][rows] B operand of fp8_scaled_mm_kpacked: within each
+ * batch slice, code (n = column, k = row) at byte ((n / 16) * (rows / 64) +
+ * k / 64) * 1024 + (n % 16) * 64 + k % 64. rows % 64 == 0, cols % 16 == 0
+ * (else FP8_ERR_ALIGNMENT), rows * cols < 2^30 (else FP8_ERR_UNSUPPORTED);
+ * native formats only; the same workspace as fp8_quant_col. */
+FP8DYN_API fp8_status fp8_quant_col_kpacked(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                            fp8_format fmt, double eps, uint8_t* qT, float* scale,
+                                            float* inv_scale, void* ws, size_t ws_bytes, void* stream);
 FP8DYN_API size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
 
 /* Normalization fused with the rowwise quantization of its output ["FP8
@@ -249,6 +259,16 @@ FP8DYN_API fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8
                                     fp8_scaling scaling, const float* a_inv, const float* b_inv,
                                     int64_t M, int64_t N, int64_t K, fp8_out out_type, void* out,
                                     int use_fast_accum, void* stream);
+
+/* fp8_scaled_mm with b k-packed ([N][K] codes in 1 KB chunks of 16 rows x
+ * 64 K, as fp8_quant_row_kpacked writes a weight and fp8_quant_col_kpacked a
+ * transposed one): the same result. Scaling TENSOR or ROW. N % 16 == 0 and
+ * K % 128 == 0 (else FP8_ERR_ALIGNMENT); N * K < 2^31 and 16-byte aligned a,
+ * b (else FP8_ERR_UNSUPPORTED). No use_fast_accum argument. */
+FP8DYN_API fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
+                                            fp8_scaling scaling, const float* a_inv, const float* b_inv,
+                                            int64_t M, int64_t N, int64_t K, fp8_out out_type, void* out,
+                                            void* stream);
 
 /* MoE grouped GEMM in one launch: rows [offsets[e], offsets[e+1]) of a use
  * expert e's b[e] ([E][N][K]) and scales. offsets: DEVICE int32 [E+1] with

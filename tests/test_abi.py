@@ -101,6 +101,20 @@ def test_host_validation_without_gpu(f):
                                       None) == f.ERR_ALIGNMENT
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 65536, 32768, f.OUT_BF16, FAKE,
                                       None) == f.ERR_UNSUPPORTED
+    # k-packed transposed column codes: rows % 64, cols % 16, a workspace for the split form
+    assert lib.fp8_quant_col_kpacked(FAKE, 1, 32, 16, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None, 0,
+                                     None) == f.ERR_ALIGNMENT
+    assert lib.fp8_quant_col_kpacked(FAKE, 1, 64, 8, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None, 0,
+                                     None) == f.ERR_ALIGNMENT
+    assert lib.fp8_quant_col_kpacked(FAKE, 1, 14336, 4096, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None, 0,
+                                     None) == f.ERR_WORKSPACE
+    # k-packed dense GEMM: TENSOR or ROW, N % 16, K % 128
+    assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_BLOCK128, FAKE, FAKE, 16, 16, 128, f.OUT_BF16, FAKE,
+                                     None) == f.ERR_UNSUPPORTED
+    assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, 16, 24, 128, f.OUT_BF16, FAKE,
+                                     None) == f.ERR_ALIGNMENT
+    assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, 16, 16, 64, f.OUT_BF16, FAKE,
+                                     None) == f.ERR_ALIGNMENT
     # linear: workspace too small
     need = lib.fp8_linear_ws_bytes(64, 64, 64, f.RECIPE_ROWWISE_BF16_WGRAD)
     assert need > 64 * 64 * 2

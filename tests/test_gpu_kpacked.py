@@ -135,3 +135,59 @@ def test_quant_then_gemm_kpacked(f):
     ref = oracle.grouped_mm(qa, e4, rq, e4, oracle.SCALE_ROW, ia, ri, off)
     S = oracle.grouped_mm(qa, e4, rq, e4, oracle.SCALE_ROW, ia, ri, off, absolute=True)
     check_gemm(y.float().cpu().numpy().astype(np.float64), ref, S, True, "quant + grouped kpacked")
+
+
+@pytest.mark.parametrize("shape", [(128, 64), (2, 256, 48), (2048, 144), (4096, 128), (2112, 64),
+                                   (1024, 2112, 64)])
+def test_quant_col_kpacked(f, shape):
+    """The three column paths: up to 2048 rows in registers, the split form (column amax
+    over row chunks, then the cast) and the fused two-read form (many strips)."""
+    import torch
+    x = synth.normal_bf16(shape, 920 + shape[-2], 0.02)
+    x.reshape(-1, shape[-1])[:, 3] = 0  # an all-zero column
+    b = 1 if len(shape) == 2 else shape[0]
+    R, C = shape[-2], shape[-1]
+    for fmt, name in _natives(f):
+        print("col kpacked", shape, name, flush=True)
+        q, full = empty_u8((b * R * C,), 256)
+        s = torch.empty(shape[:-2] + (C,), dtype=torch.float32, device="cuda:0")
+        i = torch.empty_like(s)
+        ws = torch.empty(max(f.fp8_quant_col_ws_bytes(b, R, C), 4), dtype=torch.uint8, device="cuda:0")
+        f.fp8_quant_col_kpacked(to_dev_bf16(x), fmt, EPS, q, s, i, ws)
+        torch.cuda.synchronize()
+        check_guard(full, 256)
+        rq, rs, ri = oracle.quant_col(x, name, EPS)
+        assert np.array_equal(u8(q), kpack(rq))
+        assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("M,N,K,scaling,out_f32", [(256, 512, 512, "tensor", False), (256, 512, 512, "row", False),
+                                                   (300, 208, 384, "row", True), (513, 272, 1152, "row", False),
+                                                   (2100, 8192, 128, "row", False)])
+def test_scaled_mm_kpacked(f, M, N, K, scaling, out_f32):
+    import torch
+    e4 = _natives(f)[0][1]
+    rng = np.random.default_rng(M + N + K)
+    a, b = _codes(e4, (M, K), rng), _codes(e4, (N, K), rng)
+    if scaling == "tensor":
+        sa, sb, sk, osk = np.float32([0.37]), np.float32([2.5]), f.SCALE_TENSOR, oracle.SCALE_TENSOR
+    else:
+        sa = rng.uniform(0.01, 3, M).astype(np.float32)
+        sb = rng.uniform(0.01, 3, N).astype(np.float32)
+        sk, osk = f.SCALE_ROW, oracle.SCALE_ROW
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    ot = f.OUT_F32 if out_f32 else f.OUT_BF16
+    print("scaled_mm kpacked", M, N, K, scaling, flush=True)
+    y_rm = torch.full((M, N), float("nan"), dtype=dt, device="cuda:0")
+    y_pk = torch.full((M, N), float("nan"), dtype=dt, device="cuda:0")
+    da, dsa, dsb = to_dev(a), to_dev(sa), to_dev(sb)
+    f.fp8_scaled_mm(da, f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, sk, dsa, dsb, ot, y_rm)
+    f.fp8_scaled_mm_kpacked(da, f.E4M3_NATIVE, to_dev(kpack(b)), f.E4M3_NATIVE, sk, dsa, dsb, ot, y_pk, N)
+    torch.cuda.synchronize()
+    got = y_pk.float().cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(got))
+    iv = torch.int32 if out_f32 else torch.int16
+    assert torch.equal(y_pk.view(iv), y_rm.view(iv))
+    ref = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb)
+    S = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb, absolute=True)
+    check_gemm(got, ref, S, not out_f32, f"scaled_mm kpacked {M}x{N}x{K} {scaling}")

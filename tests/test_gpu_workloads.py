@@ -91,6 +91,27 @@ def test_linear_rowwise_llama3_8b_mlp(f):
     assert np.array_equal(u8(qwt), r_qwt) and np.array_equal(iwc.cpu().numpy(), r_iwc)
     _log("linear_rowwise quantization bit-exact")
 
+    # the k-packed weight path the benchmark times for the forward and grad-input
+    # GEMMs: the same codes permuted, and the same output bits as row-major B
+    qwp = torch.empty(N * K, dtype=torch.uint8, device="cuda:0")
+    qwtp = torch.empty(N * K, dtype=torch.uint8, device="cuda:0")
+    swp, iwp, swcp, iwcp = (torch.empty_like(t) for t in (sw, iw, swc, iwc))
+    f.fp8_quant_row_kpacked(wd, f.E4M3_NATIVE, EPS, qwp, swp, iwp)
+    f.fp8_quant_col_kpacked(wd, f.E4M3_NATIVE, EPS, qwtp, swcp, iwcp, ws)
+    pair = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0") for _ in range(2)]
+    f.fp8_scaled_mm(qx, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ix, iw, f.OUT_BF16, pair[0])
+    f.fp8_scaled_mm_kpacked(qx, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, ix, iwp, f.OUT_BF16, pair[1], N)
+    gpair = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0") for _ in range(2)]
+    f.fp8_scaled_mm(qg, f.E5M2_NATIVE, qwt, f.E4M3_NATIVE, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gpair[0])
+    f.fp8_scaled_mm_kpacked(qg, f.E5M2_NATIVE, qwtp, f.E4M3_NATIVE, f.SCALE_ROW, ig, iwcp, f.OUT_BF16, gpair[1], K)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(qwp), kpack(r_qw)) and np.array_equal(u8(qwtp), kpack(r_qwt))
+    assert torch.equal(iwp, iw) and torch.equal(iwcp, iwc)
+    assert torch.equal(pair[1].view(torch.int16), pair[0].view(torch.int16)), "k-packed forward differs"
+    assert torch.equal(gpair[1].view(torch.int16), gpair[0].view(torch.int16)), "k-packed grad-input differs"
+    del qwp, qwtp, pair, gpair
+    _log("linear_rowwise k-packed weights and GEMMs bit-identical")
+
     rc = f.RECIPE_ROWWISE_BF16_WGRAD
     lws = torch.empty(f.fp8_linear_ws_bytes(M, N, K, rc), dtype=torch.uint8, device="cuda:0")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
