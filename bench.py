@@ -12,7 +12,8 @@ already resident in HBM:
                      the FP8 weight-gradient GEMM and the whole fp8_linear_bwd call
   expert_colwise     per-expert column scales + transposed cast, 32 x [2048,7168]
   moe_grouped        rowwise quant of A [131072,7168] and of W [32][2048][7168] (per
-                     expert column; W's codes k-packed, 1 KB chunks of 16 rows x 64 K),
+                     expert column; W's codes k-packed, 1 KB chunks of 16 rows x 64 K,
+                     A's pair-interleaved),
                      FP8 grouped GEMM over int32[33] offsets -> bf16; beside
                      it (per row, outside the aggregates) the layer's backward: grad_out
                      [131072,2048] per-row e5m2, the grouped grad-input GEMM against
@@ -199,8 +200,10 @@ def build_step(f, torch, dev, wls, dev_of):
     qa4, sa4, ia4 = torch.empty((Mt, K4), **u8), torch.empty(Mt, **f32), torch.empty(Mt, **f32)
     qw4, sw4, iw4 = torch.empty((E4n, N4, K4), **u8), torch.empty((E4n, N4), **f32), torch.empty((E4n, N4), **f32)
     out4 = torch.empty((Mt, N4), **bf)
+    # the activations' codes pair-interleaved (rows 2i, 2i + 1 share each
+    # 128-byte line), the A layout of the k-packed grouped GEMM
     st.add("moe_grouped.quant_row_a", "quant", 3 * Mt * K4 + 8 * Mt,
-           lambda: f.fp8_quant_row(a4, E4, EPS, qa4, sa4, ia4))
+           lambda: f.fp8_quant_row_kpaired(a4, E4, EPS, qa4, sa4, ia4))
     # the weights' codes k-packed (1 KB chunks of 16 rows x 64 K) by their
     # quantization, the layout the grouped GEMM loads B from in whole lines
     st.add("moe_grouped.quant_expert_cols_w", "quant", 3 * E4n * N4 * K4 + 8 * E4n * N4,

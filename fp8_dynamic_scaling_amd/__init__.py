@@ -24,7 +24,7 @@ RECIPE_TENSORWISE, RECIPE_ROWWISE_BF16_WGRAD = range(2)
 
 EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
-    "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_col",
+    "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_row_kpaired", "fp8_quant_col",
     "fp8_quant_col_kpacked",
     "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
     "fp8_quant_block", "fp8_quant_mx",
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_tensor_ws_bytes": (SZ, []),
         "fp8_quant_row": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_row_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
+        "fp8_quant_row_kpaired": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
@@ -167,6 +168,16 @@ def fp8_quant_row_kpacked(x, fmt, eps, q, scale, inv_scale=None, stream=None):
         _ptr(x), b, r, c, int(fmt), float(eps), _ptr(q), _ptr(scale), _ptr(inv_scale), _stream(stream)))
 
 
+def fp8_quant_row_kpaired(x, fmt, eps, q, scale, inv_scale=None, stream=None):
+    """fp8_quant_row with the codes pair-interleaved (rows 2i and 2i + 1 share each
+    128-byte line of a 64-column block); the A layout of fp8_grouped_mm_kpacked."""
+    b, r, c = _brc(x)
+    if q.numel() * q.element_size() != b * r * c:
+        raise ValueError("fp8_quant_row_kpaired: q must hold one byte per element of x")
+    _check("fp8_quant_row_kpaired", load().fp8_quant_row_kpaired(
+        _ptr(x), b, r, c, int(fmt), float(eps), _ptr(q), _ptr(scale), _ptr(inv_scale), _stream(stream)))
+
+
 def fp8_quant_col_ws_bytes(batch: int, rows: int, cols: int) -> int:
     return load().fp8_quant_col_ws_bytes(int(batch), int(rows), int(cols))
 
@@ -257,7 +268,8 @@ def fp8_scaled_mm_kpacked(a, fa, b, fb, scaling, a_inv, b_inv, out_type, out, N,
 
 
 def fp8_grouped_mm_kpacked(a, fa, b, fb, scaling, a_scale, b_scale, offsets, out_type, out, N, stream=None):
-    """fp8_grouped_mm with b k-packed (fp8_quant_row_kpacked's layout of the [E][N][K]
+    """fp8_grouped_mm with a pair-interleaved (fp8_quant_row_kpaired's layout; a is
+    [Mtot][K] shaped) and b k-packed (fp8_quant_row_kpacked's layout of the [E][N][K]
     codes); b is any uint8 tensor of E * N * K bytes with b.shape[0] == E."""
     Mtot, K = a.shape
     E = b.shape[0]

@@ -232,7 +232,22 @@ fp8_status fp8_quant_row_kpacked(const uint16_t* x, int64_t batch, int64_t rows,
   double fm;
   if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
   QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
-  return dev_err(launch_quant_row_kpacked(a));
+  return dev_err(launch_quant_row_kpacked(a, 16));
+}
+
+fp8_status fp8_quant_row_kpaired(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                 double eps, uint8_t* q, float* scale, float* inv_scale, void* stream) {
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, scale);
+  if (st != FP8_OK) return st;
+  if (rows % 2 != 0 || cols % 64 != 0) return FP8_ERR_ALIGNMENT;
+  if (cols > 16384) return FP8_ERR_UNSUPPORTED;
+  if (cols == 0) return empty_group_scales(fmt, false, eps, scale, inv_scale, batch * rows, stream);
+  if (batch * rows == 0) return FP8_OK;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, scale, inv_scale, (hipStream_t)stream};
+  return dev_err(launch_quant_row_kpacked(a, 2));
 }
 
 fp8_status fp8_quant_col(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt, double eps,
@@ -446,8 +461,9 @@ fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t
   if (st != FP8_OK || Mtot == 0 || N == 0) return st;
   if (!offsets) return FP8_ERR_INVALID_ARGUMENT;
   if (!aligned(offsets, 4)) return FP8_ERR_ALIGNMENT;
-  if (N % 16 != 0 || K % 128 != 0) return FP8_ERR_ALIGNMENT;
-  if (N * K >= ((int64_t)1 << 31)) return FP8_ERR_UNSUPPORTED;  // 32-bit offsets in an expert's B
+  if (N % 16 != 0 || K % 128 != 0 || Mtot % 2 != 0) return FP8_ERR_ALIGNMENT;
+  // 32-bit offsets in an expert's B and in a tile's pairs of A rows
+  if (N * K >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 22)) return FP8_ERR_UNSUPPORTED;
   bool ea, eb;
   double fm;
   if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;

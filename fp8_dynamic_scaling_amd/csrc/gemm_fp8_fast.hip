@@ -141,11 +141,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     // * 1024, so one
     // stage's load of 16 rows is one contiguous KB (whole cache lines) and the
     // next stage is 1 KB further
+    // Grouped k-packed: A pair-interleaved, rows 2i and 2i + 1 sharing a
+    // 128-byte line per 64-deep K block (row m, block s at (m / 2) * 2K +
+    // s * 128 + (m % 2) * 64), so a 16-row load touches 8 or 9 whole lines
+    // however the expert's rows start
     const bool pk = PKB && grp == 1;
-    const uint8_t* base = grp == 0 ? p.a + ti.m0 * K
-                          : pk     ? p.b + (int64_t)ti.e * N * K
-                                   : p.b + ((int64_t)ti.e * N + ti.n0) * K;
-    const int64_t sstride = pk ? 1024 : BK;
+    const bool pa = PKB && GR && grp == 0;
+    const int64_t m0e = ti.m0 & ~(int64_t)1;
+    const uint8_t* base = pa ? p.a + m0e * K
+                          : grp == 0 ? p.a + ti.m0 * K
+                          : pk       ? p.b + (int64_t)ti.e * N * K
+                                     : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    const int64_t sstride = pk ? 1024 : pa ? 128 : BK;
     const int32_t rows = grp == 0 ? a_rows : b_rows;
     uint32_t off[DH];
 #pragma unroll
@@ -157,6 +164,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
         int64_t gi = ti.n0 / 16 + 4 * wn + d;
         gi = gi < N / 16 ? gi : N / 16 - 1;
         off[d] = (uint32_t)(gi * (K / 64) * 1024 + ld_row * 64 + 16 * c);
+      } else if (pa) {
+        const int32_t rr = r < rows ? r : rows - 1;
+        const int64_t m = ti.m0 + rr;
+        off[d] = (uint32_t)(((m >> 1) - (m0e >> 1)) * 2 * K + (m & 1) * 64 + 16 * c);
       } else {
         const int32_t rr = r < rows ? r : rows - 1;
         off[d] = (uint32_t)(rr * K32 + 16 * c);

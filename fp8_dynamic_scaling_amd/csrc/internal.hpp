@@ -23,8 +23,9 @@ struct QuantArgs {
 };
 
 hipError_t launch_quant_row(const QuantArgs& a);
-// codes k-packed (1 KB chunks of 16 rows x 64 columns); rows % 16 == 0, cols % 64 == 0, cols <= 16384
-hipError_t launch_quant_row_kpacked(const QuantArgs& a);
+// codes k-packed in chunks of group_rows (16 or 2) rows x 64 columns; rows % group_rows == 0,
+// cols % 64 == 0, cols <= 16384
+hipError_t launch_quant_row_kpacked(const QuantArgs& a, int group_rows);
 hipError_t launch_quant_col(const QuantArgs& a, void* ws);
 // qT k-packed as the [cols][rows] B operand; rows % 64 == 0, cols % 16 == 0, the vector path's conditions
 hipError_t launch_quant_col_kpacked(const QuantArgs& a, void* ws);

@@ -64,18 +64,20 @@ __global__ __launch_bounds__(256) void k_quant_row(const uint16_t* __restrict__ 
 // half lines whose other halves belong to the neighbouring row, so rows are
 // dealt to XCDs in contiguous ranges (workgroup i runs on XCD i % 8) and the
 // two halves meet in one L2; plain stores let it merge them.
-template <int J, bool E5>
+// G = 2: the pair-interleaved rows of a grouped GEMM's A (chunks of 2 rows x
+// 64 columns, 128 bytes), otherwise G = 16.
+template <int J, bool E5, int G>
 __global__ __launch_bounds__(256) void k_quant_row_kpacked(const uint16_t* __restrict__ x, int64_t nrows,
                                                            int64_t cols, uint8_t* __restrict__ q,
                                                            float* __restrict__ scale, float* __restrict__ inv,
                                                            double fmax, double eps) {
   __shared__ float red[4];
-  const int64_t G = gridDim.x;
+  const int64_t nwg = gridDim.x;
   int64_t row = blockIdx.x;
-  if (G % 8 == 0) row = (row % 8) * (G / 8) + row / 8;
+  if (nwg % 8 == 0) row = (row % 8) * (nwg / 8) + row / 8;
   const uint16_t* xr = x + row * cols;
-  // chunk row (row / 16, 0) of the packed codes, then this row's 64 bytes in it
-  uint8_t* qg = q + (row / 16) * 16 * cols + (row % 16) * 64;
+  // chunk row (row / G, 0) of the packed codes, then this row's 64 bytes in it
+  uint8_t* qg = q + (row / G) * G * cols + (row % G) * 64;
   const int tid = threadIdx.x;
   uint4 v[J];
   float m = 0.0f;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void k_quant_row_kpacked(const uint16_t* __res
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int64_t c = (int64_t)(tid + 256 * j) * 8;
-    if (c < cols) *reinterpret_cast<uint2*>(qg + (c / 64) * 1024 + c % 64) = quant8<E5>(v[j], s, fm);
+    if (c < cols) *reinterpret_cast<uint2*>(qg + (c / 64) * (64 * G) + c % 64) = quant8<E5>(v[j], s, fm);
   }
 }
 
@@ -746,30 +748,31 @@ static hipError_t launch_row_t(const QuantArgs& a) {
 
 hipError_t launch_quant_row(const QuantArgs& a) { return a.e5 ? launch_row_t<true>(a) : launch_row_t<false>(a); }
 
-// rows % 16 == 0 and cols % 64 == 0 (the caller checks), cols <= 16384
-template <bool E5>
+// rows % G == 0 and cols % 64 == 0 (the caller checks), cols <= 16384
+template <bool E5, int G>
 static hipError_t launch_row_kpacked_t(const QuantArgs& a) {
   const int64_t R = a.batch * a.rows, C = a.cols;
   if (R == 0 || C == 0) return hipSuccess;
   dim3 grid((unsigned)R), block(256);
   const int64_t J = (C + 2047) / 2048;
   if (J <= 1)
-    hipLaunchKernelGGL((k_quant_row_kpacked<1, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+    hipLaunchKernelGGL((k_quant_row_kpacked<1, E5, G>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
                        a.eps);
   else if (J <= 2)
-    hipLaunchKernelGGL((k_quant_row_kpacked<2, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+    hipLaunchKernelGGL((k_quant_row_kpacked<2, E5, G>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
                        a.eps);
   else if (J <= 4)
-    hipLaunchKernelGGL((k_quant_row_kpacked<4, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+    hipLaunchKernelGGL((k_quant_row_kpacked<4, E5, G>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
                        a.eps);
   else
-    hipLaunchKernelGGL((k_quant_row_kpacked<8, E5>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
+    hipLaunchKernelGGL((k_quant_row_kpacked<8, E5, G>), grid, block, 0, a.stream, a.x, R, C, a.q, a.scale, a.inv, a.fmax,
                        a.eps);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_row_kpacked(const QuantArgs& a) {
-  return a.e5 ? launch_row_kpacked_t<true>(a) : launch_row_kpacked_t<false>(a);
+hipError_t launch_quant_row_kpacked(const QuantArgs& a, int group_rows) {
+  if (group_rows == 2) return a.e5 ? launch_row_kpacked_t<true, 2>(a) : launch_row_kpacked_t<false, 2>(a);
+  return a.e5 ? launch_row_kpacked_t<true, 16>(a) : launch_row_kpacked_t<false, 16>(a);
 }
 
 // The fused form (one workgroup per 64-column strip over all rows) when it

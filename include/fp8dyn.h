@@ -165,6 +165,17 @@ FP8DYN_API fp8_status fp8_quant_row_kpacked(const uint16_t* x, int64_t batch, in
                                             fp8_format fmt, double eps, uint8_t* q, float* scale,
                                             float* inv_scale, void* stream);
 
+/* Row groups as fp8_quant_row (same scales, same codes), with the codes
+ * pair-interleaved for fp8_grouped_mm_kpacked's A operand: within each batch
+ * slice, code (r, c) goes to byte ((r / 2) * (cols / 64) + c / 64) * 128 +
+ * (r % 2) * 64 + c % 64, so rows 2i and 2i + 1 share each 128-byte line of a
+ * 64-column block. rows % 2 == 0 and cols % 64 == 0 (else
+ * FP8_ERR_ALIGNMENT), cols <= 16384 (else FP8_ERR_UNSUPPORTED); native
+ * formats only. */
+FP8DYN_API fp8_status fp8_quant_row_kpaired(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                            fp8_format fmt, double eps, uint8_t* q, float* scale,
+                                            float* inv_scale, void* stream);
+
 /* Column groups with the transposed output the GEMM's column-major operand
  * needs [P-TAO section 4; P-AMD Level 1 and Level 2]: x [batch][rows][cols] ->
  * qT [batch][cols][rows], scale/inv [batch][cols]. One launch when rows <=
@@ -282,14 +293,16 @@ FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint
                                      const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N,
                                      int64_t K, fp8_out out_type, void* out, void* stream);
 
-/* fp8_grouped_mm with b k-packed as fp8_quant_row_kpacked writes it (each
- * expert's [N][K] codes as 1 KB chunks of 16 rows x 64 K): the same result.
- * The matrix-core kernel loads a 64-deep stage of 16 rows of B from HBM into
- * LDS; row-major, that is 16 half cache lines, k-packed one contiguous KB.
+/* fp8_grouped_mm with a pair-interleaved as fp8_quant_row_kpaired writes it
+ * and b k-packed as fp8_quant_row_kpacked writes it (each expert's [N][K]
+ * codes as 1 KB chunks of 16 rows x 64 K): the same result. The
+ * matrix-core kernel loads a 64-deep stage of 16 rows of each operand from
+ * HBM into LDS; row-major, that is 16 half cache lines, here 8 or 9 whole
+ * lines of A (an expert may start at an odd row) and one contiguous KB of B.
  * Scaling ROW or MX32 (scales as for fp8_grouped_mm, row-major); BLOCK128
- * and TENSOR return FP8_ERR_UNSUPPORTED. N % 16 == 0 and K % 128 == 0 (else
- * FP8_ERR_ALIGNMENT); N * K < 2^31 and 16-byte aligned a, b (else
- * FP8_ERR_UNSUPPORTED). */
+ * and TENSOR return FP8_ERR_UNSUPPORTED. N % 16 == 0, K % 128 == 0 and
+ * Mtot % 2 == 0 (else FP8_ERR_ALIGNMENT); N * K < 2^31, K < 2^22 and
+ * 16-byte aligned a, b (else FP8_ERR_UNSUPPORTED). */
 FP8DYN_API fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                              fp8_scaling scaling, const void* a_scale, const void* b_scale,
                                              const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N,

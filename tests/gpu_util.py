@@ -116,10 +116,11 @@ def check_gemm(y, r, S, out_bf16: bool, label: str = ""):
 gpu = pytest.mark.gpu
 
 
-def kpack(q):
-    """[..., R, C] row-major codes -> the flat k-packed bytes of fp8_quant_row_kpacked:
-    per batch slice, chunk (r // 16, c // 64) of 16 x 64 bytes at
-    ((r // 16) * (C // 64) + c // 64) * 1024, row r % 16 at 64 (r % 16) in it."""
+def kpack(q, g: int = 16):
+    """[..., R, C] row-major codes -> the flat k-packed bytes: per batch slice, chunk
+    (r // g, c // 64) of g x 64 bytes at ((r // g) * (C // 64) + c // 64) * 64 g, row
+    r % g at 64 (r % g) in it. g = 16: fp8_quant_row_kpacked / fp8_quant_col_kpacked;
+    g = 2: fp8_quant_row_kpaired's pair-interleaved rows."""
     *lead, R, C = q.shape
     B = int(np.prod(lead)) if lead else 1
-    return np.ascontiguousarray(q.reshape(B, R // 16, 16, C // 64, 64).transpose(0, 1, 3, 2, 4)).reshape(-1)
+    return np.ascontiguousarray(q.reshape(B, R // g, g, C // 64, 64).transpose(0, 1, 3, 2, 4)).reshape(-1)

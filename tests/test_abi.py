@@ -101,6 +101,11 @@ def test_host_validation_without_gpu(f):
                                       None) == f.ERR_ALIGNMENT
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 65536, 32768, f.OUT_BF16, FAKE,
                                       None) == f.ERR_UNSUPPORTED
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 17, 64, 128, f.OUT_BF16, FAKE,
+                                      None) == f.ERR_ALIGNMENT
+    # pair-interleaved rowwise codes: rows % 2, cols % 64
+    assert lib.fp8_quant_row_kpaired(FAKE, 1, 3, 64, *kp) == f.ERR_ALIGNMENT
+    assert lib.fp8_quant_row_kpaired(FAKE, 1, 2, 96, *kp) == f.ERR_ALIGNMENT
     # k-packed transposed column codes: rows % 64, cols % 16, a workspace for the split form
     assert lib.fp8_quant_col_kpacked(FAKE, 1, 32, 16, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None, 0,
                                      None) == f.ERR_ALIGNMENT

@@ -1,8 +1,8 @@
-"""GPU parity of the k-packed B path: fp8_quant_row_kpacked writes the oracle's rowwise
-codes (bit-exact) permuted into 1 KB chunks of 16 rows x 64 columns, and
-fp8_grouped_mm_kpacked on those chunks gives the oracle's grouped product (to the
-GEMM bar of tests/gpu_util.check_gemm) and the same bits as fp8_grouped_mm on the
-row-major codes. The permutation (tests/gpu_util.kpack) is numpy reshapes of the layout
+"""GPU parity of the packed-operand paths: fp8_quant_row_kpacked / fp8_quant_col_kpacked
+write the oracle's codes (bit-exact) permuted into 1 KB chunks of 16 rows x 64 columns,
+fp8_quant_row_kpaired into pair-interleaved rows, and the k-packed GEMMs on those give
+the oracle's products (to the GEMM bar of tests/gpu_util.check_gemm) and the same bits
+as the row-major GEMMs. The permutation (tests/gpu_util.kpack) is numpy reshapes of the layout
 the header states; nothing of it is shared with the library."""
 import numpy as np
 import pytest
@@ -65,12 +65,12 @@ def _codes(name, shape, rng):
 
 
 @pytest.mark.parametrize("counts,N,K,scaling,out_f32", [
-    ([37, 0, 300, 1, 0, 513], 272, 384, "row", False),   # N past a whole tile, empty experts
+    ([37, 0, 300, 1, 0, 514], 272, 384, "row", False),   # N past a whole tile, empty experts, odd starts
     ([0, 0, 64], 128, 128, "row", False),                 # two stages
     ([300, 5, 0, 129], 320, 640, "row", True),            # fp32 out
-    ([600, 0, 3], 512, 1152, "row", False),
+    ([600, 0, 4], 512, 1152, "row", False),
     ([4096, 4096], 2304, 128, "row", False),              # more tiles than workgroups
-    ([100, 0, 200, 7], 256, 384, "mx", False),            # dword scale loads
+    ([101, 0, 200, 7], 256, 384, "mx", False),            # dword scale loads, odd starts
     ([300, 5, 0, 129], 320, 1024, "mx", False),           # 16-byte scale loads
     ([1536, 1536], 6144, 512, "mx", False),
 ])
@@ -97,7 +97,8 @@ def test_grouped_mm_kpacked(f, counts, N, K, scaling, out_f32):
     da, dsa, dsb, doff = to_dev(a), to_dev(sa), to_dev(sb), to_dev(off)
     f.fp8_grouped_mm(da, f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, sk, dsa, dsb, doff, ot, y_rm)
     bp = to_dev(kpack(b)).reshape(E, -1)
-    f.fp8_grouped_mm_kpacked(da, f.E4M3_NATIVE, bp, f.E4M3_NATIVE, sk, dsa, dsb, doff, ot, y_pk, N)
+    ap = to_dev(kpack(a, 2)).reshape(Mt, K)
+    f.fp8_grouped_mm_kpacked(ap, f.E4M3_NATIVE, bp, f.E4M3_NATIVE, sk, dsa, dsb, doff, ot, y_pk, N)
     torch.cuda.synchronize()
     got = y_pk.float().cpu().numpy().astype(np.float64)
     assert not np.any(np.isnan(got)), "rows left unwritten"
@@ -110,11 +111,12 @@ def test_grouped_mm_kpacked(f, counts, N, K, scaling, out_f32):
 
 
 def test_quant_then_gemm_kpacked(f):
-    """The weight path as the MoE layer runs it: rowwise e4m3 quantization of
-    W [E][N][K] straight into the k-packed layout, then the grouped GEMM on it."""
+    """The MoE layer's path: rowwise e4m3 quantization of the activations into the
+    pair-interleaved layout and of W [E][N][K] into the k-packed one, then the grouped
+    GEMM on both."""
     import torch
     e4 = _natives(f)[0][1]
-    counts = [200, 0, 77, 300]
+    counts = [200, 0, 77, 301]
     E, N, K = len(counts), 256, 512
     off = _offsets(counts)
     Mt = int(off[-1])
@@ -122,14 +124,18 @@ def test_quant_then_gemm_kpacked(f):
     xa = synth.normal_bf16((Mt, K), 911, 1.0)
     qa, sa, ia = oracle.quant_row(xa, e4, EPS)
     rq, rs, ri = oracle.quant_row(w, e4, EPS)
+    qap = torch.empty((Mt, K), dtype=torch.uint8, device="cuda:0")
+    sap, iap = (torch.empty(Mt, dtype=torch.float32, device="cuda:0") for _ in range(2))
+    f.fp8_quant_row_kpaired(to_dev_bf16(xa), f.E4M3_NATIVE, EPS, qap, sap, iap)
     qw = torch.empty(E * N * K, dtype=torch.uint8, device="cuda:0").reshape(E, -1)
     sw = torch.empty((E, N), dtype=torch.float32, device="cuda:0")
     iw = torch.empty_like(sw)
     f.fp8_quant_row_kpacked(to_dev_bf16(w), f.E4M3_NATIVE, EPS, qw, sw, iw)
     y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
-    f.fp8_grouped_mm_kpacked(to_dev(qa), f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, to_dev(ia), iw, to_dev(off),
+    f.fp8_grouped_mm_kpacked(qap, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, iap, iw, to_dev(off),
                              f.OUT_BF16, y, N)
     torch.cuda.synchronize()
+    assert np.array_equal(u8(qap).reshape(-1), kpack(qa, 2)) and np.array_equal(iap.cpu().numpy(), ia)
     assert np.array_equal(u8(qw).reshape(-1), kpack(rq))
     assert np.array_equal(iw.cpu().numpy(), ri)
     ref = oracle.grouped_mm(qa, e4, rq, e4, oracle.SCALE_ROW, ia, ri, off)
@@ -191,3 +197,22 @@ def test_scaled_mm_kpacked(f, M, N, K, scaling, out_f32):
     ref = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb)
     S = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb, absolute=True)
     check_gemm(got, ref, S, not out_f32, f"scaled_mm kpacked {M}x{N}x{K} {scaling}")
+
+
+@pytest.mark.parametrize("shape", [(2, 64), (98, 7168), (2, 6, 192), (64, 16384), (3, 10, 4160)])
+def test_quant_row_kpaired(f, shape):
+    import torch
+    x = synth.normal_bf16(shape, 930 + shape[-1], 1.0)
+    x.reshape(-1, shape[-1])[1] = 0
+    n = int(np.prod(shape))
+    for fmt, name in _natives(f):
+        print("row kpaired", shape, name, flush=True)
+        q, full = empty_u8((n,), 256)
+        s = torch.empty(shape[:-1], dtype=torch.float32, device="cuda:0")
+        i = torch.empty_like(s)
+        f.fp8_quant_row_kpaired(to_dev_bf16(x), fmt, EPS, q, s, i)
+        torch.cuda.synchronize()
+        check_guard(full, 256)
+        rq, rs, ri = oracle.quant_row(x, name, EPS)
+        assert np.array_equal(u8(q), kpack(rq, 2))
+        assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)

@@ -240,21 +240,27 @@ def test_moe_grouped_forward(f):
     f.fp8_quant_row(wd, f.E4M3_NATIVE, EPS, qw, sw, iw)
     out = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ia, iw, to_dev(off), f.OUT_BF16, out)
-    # the k-packed weight path the benchmark times: quantization into 1 KB
-    # chunks of 16 rows x 64 K, then the grouped GEMM reading them
+    # the packed path the benchmark times: the weights quantized into 1 KB
+    # chunks of 16 rows x 64 K, the activations into pair-interleaved rows,
+    # then the grouped GEMM reading both
     qwp = torch.empty((E, N * K), dtype=torch.uint8, device="cuda:0")
     swp, iwp = torch.empty_like(sw), torch.empty_like(iw)
     f.fp8_quant_row_kpacked(wd, f.E4M3_NATIVE, EPS, qwp, swp, iwp)
+    qap = torch.empty((Mt, K), dtype=torch.uint8, device="cuda:0")
+    sap, iap = torch.empty_like(sa), torch.empty_like(ia)
+    f.fp8_quant_row_kpaired(ad, f.E4M3_NATIVE, EPS, qap, sap, iap)
     outp = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
-    f.fp8_grouped_mm_kpacked(qa, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, ia, iwp, to_dev(off), f.OUT_BF16,
+    f.fp8_grouped_mm_kpacked(qap, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, iap, iwp, to_dev(off), f.OUT_BF16,
                              outp, N)
     torch.cuda.synchronize()
     del ad, wd
     assert torch.equal(outp.view(torch.int16), out.view(torch.int16)), "k-packed GEMM differs from row-major"
-    assert torch.equal(iwp, iw) and torch.equal(swp, sw)
+    assert torch.equal(iwp, iw) and torch.equal(swp, sw) and torch.equal(iap, ia) and torch.equal(sap, sa)
     del outp
     r_qa, _, r_ia = oracle.quant_row(a, e4, EPS)
     assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
+    assert np.array_equal(u8(qap).reshape(-1), kpack(r_qa, 2))
+    del qap
     del a
     r_qw, _, r_iw = oracle.quant_row(w, e4, EPS)
     assert np.array_equal(u8(qw), r_qw) and np.array_equal(iw.cpu().numpy(), r_iw)

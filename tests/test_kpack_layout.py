@@ -20,3 +20,12 @@ def test_kpack_matches_the_formula():
 def test_one_chunk_is_16_rows_of_64():
     q = np.arange(16 * 64, dtype=np.int64).reshape(16, 64)
     assert np.array_equal(kpack(q), q.reshape(-1))
+
+
+def test_pair_interleave_matches_the_formula():
+    R, C = 6, 128
+    q = np.arange(R * C, dtype=np.int64).reshape(R, C)
+    p = kpack(q, 2)
+    for r in range(R):
+        for c in range(C):
+            assert p[((r // 2) * (C // 64) + c // 64) * 128 + (r % 2) * 64 + c % 64] == q[r, c]
