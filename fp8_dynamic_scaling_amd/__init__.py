@@ -26,7 +26,7 @@ EXPORTS = [
     "fp8_probe", "fp8_status_string", "fp8_last_device_error", "fp8_format_max",
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_row_kpaired", "fp8_quant_col",
     "fp8_quant_col_kpacked",
-    "fp8_quant_col_ws_bytes", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
+    "fp8_quant_col_ws_bytes", "fp8_quant_col_noalloc", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
     "fp8_quant_block", "fp8_quant_mx",
     "fp8_scaled_mm", "fp8_scaled_mm_kpacked",
     "fp8_grouped_mm", "fp8_grouped_mm_kpacked", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH):
         "fp8_quant_col": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_kpacked": (I, [P, I64, I64, I64, I, D, P, P, P, P, SZ, P]),
         "fp8_quant_col_ws_bytes": (SZ, [I64, I64, I64]),
+        "fp8_quant_col_noalloc": (I, [P, I64, I64, I64, I, D, P, P, P, P]),
         "fp8_quant_dual": (I, [P, P, I64, I64, I64, I, I, D, P, P, P, P, P, P, P, P, SZ, P]),
         "fp8_norm_quant_row": (I, [P, P, P, I64, I64, I, D, I, D, P, P, P, P, P]),
         "fp8_quant_dual_ws_bytes": (SZ, []),
@@ -187,6 +188,14 @@ def fp8_quant_col(x, fmt, eps, qT, scale, inv_scale=None, ws=None, stream=None):
     _check("fp8_quant_col", load().fp8_quant_col(
         _ptr(x), b, r, c, int(fmt), float(eps), _ptr(qT), _ptr(scale), _ptr(inv_scale),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def fp8_quant_col_noalloc(x, fmt, eps, qT, scale, inv_scale=None, stream=None):
+    """fp8_quant_col without a workspace argument: the library's own device buffer
+    holds the column-amax words (for callers that cannot allocate)."""
+    b, r, c = _brc(x)
+    _check("fp8_quant_col_noalloc", load().fp8_quant_col_noalloc(
+        _ptr(x), b, r, c, int(fmt), float(eps), _ptr(qT), _ptr(scale), _ptr(inv_scale), _stream(stream)))
 
 
 NORM_RMS, NORM_LAYER = 0, 1

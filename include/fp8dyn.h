@@ -25,7 +25,8 @@
  *  - Pointers named x, w, gy, a, b, q, scale, inv_scale, out, y, gx, gw, ws,
  *    offsets are DEVICE pointers owned by the caller. The library never
  *    allocates or frees memory in a call and keeps no pointer after it
- *    returns. Its only state is a per-device cache of fp8_probe's answer.
+ *    returns. Its only state is a per-device cache of fp8_probe's answer and,
+ *    for fp8_quant_col_noalloc, one 64 KiB device buffer per GPU.
  *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
  *  - stream is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on it and returns; results are valid once the stream has
@@ -197,6 +198,22 @@ FP8DYN_API fp8_status fp8_quant_col_kpacked(const uint16_t* x, int64_t batch, in
                                             fp8_format fmt, double eps, uint8_t* qT, float* scale,
                                             float* inv_scale, void* ws, size_t ws_bytes, void* stream);
 FP8DYN_API size_t fp8_quant_col_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fp8_quant_col with no workspace argument -- the same kernels, codes and
+ * scales. The split form's column-amax words live in a 64 KiB buffer the
+ * library keeps in device memory, one per GPU, held until the process ends;
+ * its device address is looked up once per device on the first call there.
+ * Limit: fp8_quant_col_ws_bytes(batch, rows, cols) <= 65536, i.e. at most
+ * 16384 columns (batch * cols) when the split form is used; larger problems
+ * return FP8_ERR_UNSUPPORTED before anything is launched. Nothing is
+ * allocated or freed. Every call on one GPU shares that GPU's buffer and
+ * clears the words it uses with a fill kernel on its stream: calls on
+ * streams of one GPU that are not ordered with each other race on it. */
+FP8DYN_API fp8_status fp8_quant_col_noalloc(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                            fp8_format fmt, double eps, uint8_t* qT, float* scale,
+                                            float* inv_scale, void* stream);
 
 /* Normalization fused with the rowwise quantization of its output ["FP8
  * Training: Quantization, Autograd, Torchao" section 8: the norm's output
