@@ -394,59 +394,66 @@ static fp8_status check_gemm(const void* a, const void* b, const void* sa, const
   return FP8_OK;
 }
 
+// A in {e4m3, e5m2} (native variants), B the e4m3 native variant.
+static fp8_status resolve_ab(fp8_format fa, fp8_format fb, bool* ea) {
+  if (fb == FP8_E5M2 || fb == FP8_E5M2FNUZ || fb == FP8_E5M2_NATIVE) return FP8_ERR_UNSUPPORTED;
+  bool eb;
+  double fm;
+  fp8_status st;
+  if ((st = resolve(fa, ea, &fm)) != FP8_OK) return st;
+  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  return eb ? FP8_ERR_UNSUPPORTED : FP8_OK;
+}
+
 fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb, fp8_scaling scaling,
                          const float* a_inv, const float* b_inv, int64_t M, int64_t N, int64_t K, fp8_out out_type,
                          void* out, int use_fast_accum, void* stream) {
-  (void)use_fast_accum;  // matrix cores accumulate in fp32 either way
   if (scaling != FP8_SCALE_TENSOR && scaling != FP8_SCALE_ROW) return FP8_ERR_UNSUPPORTED;
   fp8_status st = check_gemm(a, b, a_inv, b_inv, M, N, K, scaling, out_type, out);
   if (st != FP8_OK || M == 0 || N == 0) return st;
-  bool ea, eb;
-  double fm;
-  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
-  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  bool ea;
+  if ((st = resolve_ab(fa, fb, &ea)) != FP8_OK) return st;
   // no contraction terms: the empty sum (nothing is read)
   if (K == 0) return dev_err(launch_zero_fill(out, M * N * (out_type == FP8_OUT_F32 ? 4 : 2), (hipStream_t)stream));
-  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, false, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
+  g.exact = !use_fast_accum;
   return dev_err(launch_gemm_fp8(g));
 }
 
 fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb, fp8_scaling scaling,
                           const void* a_scale, const void* b_scale, const int32_t* offsets, int32_t E, int64_t Mtot,
-                          int64_t N, int64_t K, fp8_out out_type, void* out, void* stream) {
+                          int64_t N, int64_t K, fp8_out out_type, void* out, int use_fast_accum, void* stream) {
   if (scaling == FP8_SCALE_TENSOR) return FP8_ERR_UNSUPPORTED;
   if (E < 1 || E > 1024) return FP8_ERR_INVALID_ARGUMENT;
   fp8_status st = check_gemm(a, b, a_scale, b_scale, Mtot, N, K, scaling, out_type, out);
   if (st != FP8_OK || Mtot == 0 || N == 0) return st;
   if (!offsets) return FP8_ERR_INVALID_ARGUMENT;
   if (!aligned(offsets, 4)) return FP8_ERR_ALIGNMENT;
-  bool ea, eb;
-  double fm;
-  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
-  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
+  bool ea;
+  if ((st = resolve_ab(fa, fb, &ea)) != FP8_OK) return st;
   // no contraction terms: every row of every expert is the empty sum
   if (K == 0)
     return dev_err(launch_zero_fill(out, Mtot * N * (out_type == FP8_OUT_F32 ? 4 : 2), (hipStream_t)stream));
-  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, false, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream};
+  g.exact = !use_fast_accum;
   return dev_err(launch_gemm_fp8(g));
 }
 
 fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                  fp8_scaling scaling, const float* a_inv, const float* b_inv, int64_t M, int64_t N,
-                                 int64_t K, fp8_out out_type, void* out, void* stream) {
+                                 int64_t K, fp8_out out_type, void* out, int use_fast_accum, void* stream) {
   if (scaling != FP8_SCALE_TENSOR && scaling != FP8_SCALE_ROW) return FP8_ERR_UNSUPPORTED;
   fp8_status st = check_gemm(a, b, a_inv, b_inv, M, N, K, scaling, out_type, out);
   if (st != FP8_OK || M == 0 || N == 0) return st;
   if (N % 16 != 0 || K % 128 != 0) return FP8_ERR_ALIGNMENT;
   if (N * K >= ((int64_t)1 << 31)) return FP8_ERR_UNSUPPORTED;  // 32-bit offsets in B
-  bool ea, eb;
-  double fm;
-  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
-  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
-  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+  bool ea;
+  if ((st = resolve_ab(fa, fb, &ea)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_inv, b_inv, nullptr, 1, M, N, K, ea, false, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream, true};
+  g.exact = !use_fast_accum;
   if (!gemm_fp8_fast_eligible(g)) return FP8_ERR_UNSUPPORTED;
   return dev_err(launch_gemm_fp8_fast(g));
 }
@@ -454,8 +461,9 @@ fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t*
 fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                   fp8_scaling scaling, const void* a_scale, const void* b_scale,
                                   const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N, int64_t K,
-                                  fp8_out out_type, void* out, void* stream) {
+                                  fp8_out out_type, void* out, int use_fast_accum, void* stream) {
   if (scaling != FP8_SCALE_ROW && scaling != FP8_SCALE_MX32) return FP8_ERR_UNSUPPORTED;
+  if (!use_fast_accum && scaling != FP8_SCALE_ROW) return FP8_ERR_UNSUPPORTED;
   if (E < 1 || E > 1024) return FP8_ERR_INVALID_ARGUMENT;
   fp8_status st = check_gemm(a, b, a_scale, b_scale, Mtot, N, K, scaling, out_type, out);
   if (st != FP8_OK || Mtot == 0 || N == 0) return st;
@@ -464,12 +472,11 @@ fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t
   if (N % 16 != 0 || K % 128 != 0 || Mtot % 2 != 0) return FP8_ERR_ALIGNMENT;
   // 32-bit offsets in an expert's B and in a tile's pairs of A rows
   if (N * K >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 22)) return FP8_ERR_UNSUPPORTED;
-  bool ea, eb;
-  double fm;
-  if ((st = resolve(fa, &ea, &fm)) != FP8_OK) return st;
-  if ((st = resolve(fb, &eb, &fm)) != FP8_OK) return st;
-  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, eb, (int)scaling, out_type == FP8_OUT_F32, out,
+  bool ea;
+  if ((st = resolve_ab(fa, fb, &ea)) != FP8_OK) return st;
+  GemmArgs g{a, b, a_scale, b_scale, offsets, E, Mtot, N, K, ea, false, (int)scaling, out_type == FP8_OUT_F32, out,
              (hipStream_t)stream, true};
+  g.exact = !use_fast_accum;
   if (!gemm_fp8_fast_eligible(g)) return FP8_ERR_UNSUPPORTED;
   return dev_err(launch_gemm_fp8_fast(g));
 }

@@ -234,6 +234,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
     for (int i = tid; i <= E; i += 256) s_off[i] = offsets[i];
     __syncthreads();
     if (tid == 0) {
+      clamp_offsets_serial(s_off, E, M);
       int64_t acc = 0;
       for (int32_t e = 0; e < E; ++e) {
         s_cum[e] = acc;

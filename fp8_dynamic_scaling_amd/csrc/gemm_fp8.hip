@@ -36,7 +36,12 @@
 
 namespace fp8dyn {
 
-template <int BM, int BN, int WM, int WN, bool AE5, bool BE5, int SK, bool OF32>
+// EX: full-precision accumulation. Each 16x16x128 FP8 step becomes four
+// v_mfma_f32_16x16x32_bf16 on the codes decoded to bf16: bytes [8 q, 8 q + 8)
+// of every lane feed instruction q on both operands. MX scales are powers of
+// two and are folded into the decode: a lane's low 16 bytes lie in 32-element
+// group g / 2 of the 128-deep step and its high 16 bytes in group 2 + g / 2.
+template <int BM, int BN, int WM, int WN, bool AE5, bool BE5, int SK, bool OF32, bool EX = false>
 __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int BK = 128;
@@ -61,24 +66,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
   const int64_t nk = (K + BK - 1) / BK;
 
   // ---- tile prefix over experts (offsets live in device memory) ----
-  if (p.offsets) {
-    for (int i = tid; i <= E; i += NT) s_off[i] = p.offsets[i];
-  } else if (tid == 0) {
-    s_off[0] = 0;
-    s_off[1] = (int32_t)p.M;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int e = 0; e < E; ++e) {
-      s_pref[e] = acc;
-      const int64_t mrows = (int64_t)s_off[e + 1] - s_off[e];
-      acc += (mrows > 0 ? (mrows + BM - 1) / BM : 0) * nt;
-    }
-    s_pref[E] = acc;
-  }
-  __syncthreads();
-  const int64_t total = s_pref[E];
+  const int64_t total = build_tile_prefix<BM, NT>(p, nt, s_off, s_pref);
 
   // ---- XCD-aware assignment: XCD x owns tiles [x*total/8, (x+1)*total/8) ----
   const int64_t G = gridDim.x;
@@ -163,7 +151,29 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
 
       // per-lane MX scales for this K step
       int sa_w[MI], sb_w[NI];
-      if constexpr (SK == kScaleMX) {
+      float sa_x[MI][2], sb_x[NI][2];  // EX: decode scales of the low and high 16 bytes
+      if constexpr (EX && SK == kScaleMX) {
+        const int64_t kb32 = K / 32;
+        const uint8_t* SA = reinterpret_cast<const uint8_t*>(p.sa);
+        const uint8_t* SB = reinterpret_cast<const uint8_t*>(p.sb);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t kg = kt * 4 + 2 * h + (lk >> 1);
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const int64_t m = ti.m0 + wm * TM + 16 * i + lr;
+            const int e = (m < ti.m_end && kg < kb32) ? (int)SA[m * kb32 + kg] : 127;
+            sa_x[i][h] = e8m0_to_f32(e);
+          }
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int64_t n = ti.n0 + wn * TN + 16 * j + lr;
+            const int e = (n < N && kg < kb32) ? (int)SB[((int64_t)ti.e * N + n) * kb32 + kg] : 127;
+            sb_x[j][h] = e8m0_to_f32(e);
+          }
+        }
+      }
+      if constexpr (SK == kScaleMX && !EX) {
         const int64_t kb32 = K / 32;
         const int64_t kg = kt * 4 + lk;
         const uint8_t* SA = reinterpret_cast<const uint8_t*>(p.sa);
@@ -208,7 +218,41 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
         const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * (lk ^ (r & 7)));
         const uint4 hi = *reinterpret_cast<const uint4*>(base + 16 * ((lk + 4) ^ (r & 7)));
         const v8i af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        if constexpr (SK == kScaleBlock) {
+        if constexpr (EX) {
+          // decode, two wait states, four BF16 instructions per (i, j)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            v8bf ab[4], bb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if constexpr (SK == kScaleMX) {
+                ab[q] = bf16x8_scaled<AE5>(af, q, sa_x[i][q >> 1]);
+                bb[q] = bf16x8_scaled<BE5>(bf[j], q, sb_x[j][q >> 1]);
+              } else {
+                ab[q] = bf16x8<AE5>(af, q);
+                bb[q] = bf16x8<BE5>(bf[j], q);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 1" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            v4f t4 = SK == kScaleBlock ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : acc[i][j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[q], bb[q], t4, 0, 0, 0);
+            asm volatile("" ::"v"(ab[0]), "v"(ab[1]), "v"(ab[2]), "v"(ab[3]), "v"(bb[0]), "v"(bb[1]), "v"(bb[2]),
+                         "v"(bb[3]));
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (SK == kScaleBlock) {
+              const float4 s4 = *reinterpret_cast<const float4*>(&lds_sa[buf][wm * TM + 16 * i + 4 * lk]);
+              acc[i][j][0] += t4[0] * (s4.x * sbk);
+              acc[i][j][1] += t4[1] * (s4.y * sbk);
+              acc[i][j][2] += t4[2] * (s4.z * sbk);
+              acc[i][j][3] += t4[3] * (s4.w * sbk);
+            } else {
+              acc[i][j] = t4;
+            }
+          }
+        } else if constexpr (SK == kScaleBlock) {
           const float4 s4 = *reinterpret_cast<const float4*>(&lds_sa[buf][wm * TM + 16 * i + 4 * lk]);
           const float s0 = s4.x * sbk, s1 = s4.y * sbk, s2 = s4.z * sbk, s3 = s4.w * sbk;
 #pragma unroll
@@ -269,28 +313,25 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void k_gemm_fp8(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool AE5, bool BE5, int SK, bool OF32>
+template <int BM, int BN, int WM, int WN, bool AE5, bool BE5, int SK, bool OF32, bool EX>
 static hipError_t launch_cfg(const GemmArgs& g) {
   GemmParams p{g.a, g.b, g.sa, g.sb, g.offsets, g.E, g.M, g.N, g.K, g.out};
   const int64_t nt = (g.N + BN - 1) / BN;
   const int64_t tiles_ub = g.offsets ? ((g.M + BM - 1) / BM + g.E) * nt : ((g.M + BM - 1) / BM) * nt;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
-  int64_t grid = cus;
+  int64_t grid = device_cus();
   if (tiles_ub < grid) grid = tiles_ub;
   if (grid >= kNumXcd) grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((k_gemm_fp8<BM, BN, WM, WN, AE5, BE5, SK, OF32>), dim3((unsigned)grid), dim3(WM * WN * 64), 0,
-                     g.stream, p);
+  hipLaunchKernelGGL((k_gemm_fp8<BM, BN, WM, WN, AE5, BE5, SK, OF32, EX>), dim3((unsigned)grid),
+                     dim3(WM * WN * 64), 0, g.stream, p);
   return hipGetLastError();
 }
 
 template <bool AE5, bool BE5, int SK, bool OF32>
 static hipError_t launch_sk(const GemmArgs& g) {
-  return launch_cfg<256, 256, 2, 2, AE5, BE5, SK, OF32>(g);
+  // full precision: 64 x 64 per wave (the decoded operands need registers)
+  if (g.exact) return launch_cfg<128, 128, 2, 2, AE5, BE5, SK, OF32, true>(g);
+  return launch_cfg<256, 256, 2, 2, AE5, BE5, SK, OF32, false>(g);
 }
 
 template <bool AE5, bool BE5>
@@ -310,8 +351,9 @@ static hipError_t launch_fmt(const GemmArgs& g) {
 hipError_t launch_gemm_fp8(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (gemm_fp8_fast_eligible(g)) return launch_gemm_fp8_fast(g);
-  if (g.a_e5) return g.b_e5 ? launch_fmt<true, true>(g) : launch_fmt<true, false>(g);
-  return g.b_e5 ? launch_fmt<false, true>(g) : launch_fmt<false, false>(g);
+  // B is always the e4m3 variant (the API rejects e5m2 B)
+  if (g.b_e5) return hipErrorInvalidValue;
+  return g.a_e5 ? launch_fmt<true, false>(g) : launch_fmt<false, false>(g);
 }
 
 }  // namespace fp8dyn

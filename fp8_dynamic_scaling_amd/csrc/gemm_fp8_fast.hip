@@ -60,7 +60,12 @@ namespace fp8dyn {
 //    otherwise a stage pair's bytes (one dword per row, 128-deep K) ride in a
 //    ring of 4 pairs with each even stage's loads. Each lane reads its byte
 //    straight into the MFMA's scale operand in the memory phase.
-template <bool AE5, bool BE5, int SK, bool OF32, bool GR, bool PKB>
+//  - EX (tensorwise and rowwise scales): full-precision accumulation. The
+//    compute phase decodes each pair of 32-byte fragments to bf16 and runs
+//    four v_mfma_f32_32x32x16_bf16 instead of one FP8 instruction: bytes
+//    [8 q, 8 q + 8) of every lane feed instruction q, on both operands, so
+//    the four instructions together take each K of the stage exactly once.
+template <bool AE5, bool BE5, int SK, bool OF32, bool GR, bool PKB, bool EX = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 64, NS = 4;
   constexpr int TM = 128, TN = 64, MI = TM / 32, NI = TN / 32;
@@ -70,6 +75,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
   constexpr bool MXS = SK == kScaleMX;
   constexpr int X = MXS ? 1 : 0;  // scale loads of an even stage
   static_assert(SK == kScaleTensor || SK == kScaleRow || MXS, "tensorwise, rowwise or MX");
+  static_assert(!(EX && MXS), "full-precision accumulation: tensorwise or rowwise scales");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
   __shared__ int32_t s_off[GR ? kMaxExperts + 1 : 2];
@@ -267,6 +273,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     auto mma = [&]() {
       __builtin_amdgcn_s_setprio(1);
+      if constexpr (EX) {
+        // decode, two wait states (a VALU write right before a matrix-core
+        // read of the same register is not seen), four BF16 instructions;
+        // sources stay live past the instructions that read them
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            v8bf ab[4], bb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              ab[q] = bf16x8<AE5>(fa[i], q);
+              bb[q] = bf16x8<BE5>(fb[j], q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 1" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[q], bb[q], acc[i][j], 0, 0, 0);
+            asm volatile("" ::"v"(ab[0]), "v"(ab[1]), "v"(ab[2]), "v"(ab[3]), "v"(bb[0]), "v"(bb[1]), "v"(bb[2]),
+                         "v"(bb[3]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        __builtin_amdgcn_s_setprio(0);
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -605,7 +638,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
   }
 }
 
-template <bool AE5, bool BE5, int SK, bool OF32>
+template <bool AE5, bool BE5, int SK, bool OF32, bool EX>
 static hipError_t launch_fast_cfg(const GemmArgs& g) {
   GemmParams p{g.a, g.b, g.sa, g.sb, g.offsets, g.E, g.M, g.N, g.K, g.out};
   constexpr int BM = 256, BN = 256;
@@ -619,16 +652,16 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
     hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
   } else {
     if (g.offsets && g.b_kpacked)
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, true>), dim3((unsigned)grid), dim3(512), 0, g.stream,
-                         p);
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, true, EX>), dim3((unsigned)grid), dim3(512), 0,
+                         g.stream, p);
     else if (g.offsets)
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, false>), dim3((unsigned)grid), dim3(512), 0,
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, false, EX>), dim3((unsigned)grid), dim3(512), 0,
                          g.stream, p);
     else if (g.b_kpacked)
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, true>), dim3((unsigned)grid), dim3(512), 0,
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, true, EX>), dim3((unsigned)grid), dim3(512), 0,
                          g.stream, p);
     else
-      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, false>), dim3((unsigned)grid), dim3(512), 0,
+      hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, false, false, EX>), dim3((unsigned)grid), dim3(512), 0,
                          g.stream, p);
   }
   return hipGetLastError();
@@ -638,20 +671,30 @@ template <bool AE5, bool BE5>
 static hipError_t launch_fast_fmt(const GemmArgs& g) {
   switch (g.scale_kind) {
     case kScaleTensor:
-      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleTensor, true>(g)
-                       : launch_fast_cfg<AE5, BE5, kScaleTensor, false>(g);
+      if (g.exact)
+        return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleTensor, true, true>(g)
+                         : launch_fast_cfg<AE5, BE5, kScaleTensor, false, true>(g);
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleTensor, true, false>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleTensor, false, false>(g);
     case kScaleRow:
-      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleRow, true>(g) : launch_fast_cfg<AE5, BE5, kScaleRow, false>(g);
+      if (g.exact)
+        return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleRow, true, true>(g)
+                         : launch_fast_cfg<AE5, BE5, kScaleRow, false, true>(g);
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleRow, true, false>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleRow, false, false>(g);
     case kScaleBlock:
-      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleBlock, true>(g)
-                       : launch_fast_cfg<AE5, BE5, kScaleBlock, false>(g);
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleBlock, true, false>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleBlock, false, false>(g);
     default:
-      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleMX, true>(g) : launch_fast_cfg<AE5, BE5, kScaleMX, false>(g);
+      return g.out_f32 ? launch_fast_cfg<AE5, BE5, kScaleMX, true, false>(g)
+                       : launch_fast_cfg<AE5, BE5, kScaleMX, false, false>(g);
   }
 }
 
 bool gemm_fp8_fast_eligible(const GemmArgs& g) {
   const auto al = [](const void* q, uintptr_t a) { return ((uintptr_t)q % a) == 0; };
+  // full precision: the ping-pong kernel's tensorwise and rowwise forms
+  if (g.exact && g.scale_kind != kScaleTensor && g.scale_kind != kScaleRow) return false;
   if (g.N > (1 << 22)) return false;  // 32-bit in-tile output offsets
   if (g.K % 128 != 0 || g.K == 0) return false;
   if (g.K > (1 << 23)) return false;  // 32-bit in-tile offsets: 256 rows * K < 2^31
@@ -661,8 +704,9 @@ bool gemm_fp8_fast_eligible(const GemmArgs& g) {
 }
 
 hipError_t launch_gemm_fp8_fast(const GemmArgs& g) {
-  if (g.a_e5) return g.b_e5 ? launch_fast_fmt<true, true>(g) : launch_fast_fmt<true, false>(g);
-  return g.b_e5 ? launch_fast_fmt<false, true>(g) : launch_fast_fmt<false, false>(g);
+  // B is always the e4m3 variant (the API rejects e5m2 B)
+  if (g.b_e5) return hipErrorInvalidValue;
+  return g.a_e5 ? launch_fast_fmt<true, false>(g) : launch_fast_fmt<false, false>(g);
 }
 
 }  // namespace fp8dyn

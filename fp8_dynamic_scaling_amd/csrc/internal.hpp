@@ -95,6 +95,7 @@ struct GemmArgs {
   void* out;          // [M][N]
   hipStream_t stream;
   bool b_kpacked = false;  // B in 1 KB chunks of 16 rows x 64 K (fast kernel, ROW/TENSOR/MX scales)
+  bool exact = false;      // full-precision accumulation (codes decoded to bf16, BF16 matrix cores)
 };
 hipError_t launch_gemm_fp8(const GemmArgs& g);
 // the direct-to-LDS kernel (K % 128 == 0, aligned operands); launch_gemm_fp8 picks it

@@ -14,7 +14,12 @@
 //             gw = gy^T x                         rowwise: bf16 matrix cores
 // Every FP8 operand is produced directly in the layout its GEMM reads: no
 // transposed copies ("FP8 training on AMD GPUs with TorchTitan and TorchAO",
-// Level 1).
+// Level 1). In the rowwise recipe the weight operands are written k-packed
+// (1 KB chunks of 16 rows x 64 K, the layout the GEMM's LDS loads read as
+// whole cache lines) when the shapes allow it; the bytes are the same codes.
+// Accumulation follows "FP8 Training: Quantization, Autograd, Torchao",
+// section 5: both backward GEMMs use full precision; the forward takes the
+// caller's choice (the pages' recipe: fast accumulation).
 #include "../../include/fp8dyn.h"
 #include "internal.hpp"
 
@@ -83,6 +88,14 @@ fp8_status as_status(hipError_t e) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Shapes whose rowwise weight operands go k-packed: the forward's w [N][K]
+// (fp8_quant_row_kpacked + fp8_scaled_mm_kpacked), the backward's w^T [K][N]
+// (fp8_quant_col_kpacked + fp8_scaled_mm_kpacked, contraction over N).
+bool fwd_kpacked(int64_t N, int64_t K) {
+  return K > 0 && N % 16 == 0 && K % 128 == 0 && K <= 16384 && N * K < ((int64_t)1 << 31);
+}
+bool bwd_kpacked(int64_t N, int64_t K) { return N % 128 == 0 && K % 16 == 0 && N * K < ((int64_t)1 << 30); }
+
 }  // namespace
 
 extern "C" {
@@ -96,7 +109,8 @@ size_t fp8_linear_ws_bytes(int64_t M, int64_t N, int64_t K, fp8_recipe recipe) {
 }
 
 fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, fp8_recipe recipe,
-                          double eps, fp8_out out_type, void* y, void* ws, size_t ws_bytes, void* stream) {
+                          double eps, fp8_out out_type, int use_fast_accum, void* y, void* ws, size_t ws_bytes,
+                          void* stream) {
   if (recipe != FP8_RECIPE_TENSORWISE && recipe != FP8_RECIPE_ROWWISE_BF16_WGRAD) return FP8_ERR_INVALID_ARGUMENT;
   if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;
   if (M == 0 || N == 0) return FP8_OK;
@@ -120,13 +134,21 @@ fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64
     if ((st = fp8_quant_row(x, 1, M, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, stream)) !=
         FP8_OK)
       return st;
+    if (fwd_kpacked(N, K)) {
+      if ((st = fp8_quant_row_kpacked(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw,
+                                      stream)) != FP8_OK)
+        return st;
+      return fp8_scaled_mm_kpacked((const uint8_t*)L.qx, FP8_E4M3_NATIVE, (const uint8_t*)L.qw, FP8_E4M3_NATIVE,
+                                   FP8_SCALE_ROW, (const float*)L.ix, (const float*)L.iw, M, N, K, out_type, y,
+                                   use_fast_accum, stream);
+    }
     if ((st = fp8_quant_row(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw, stream)) !=
         FP8_OK)
       return st;
   }
   return fp8_scaled_mm((const uint8_t*)L.qx, FP8_E4M3_NATIVE, (const uint8_t*)L.qw, FP8_E4M3_NATIVE,
                        tw ? FP8_SCALE_TENSOR : FP8_SCALE_ROW, (const float*)L.ix, (const float*)L.iw, M, N, K, out_type,
-                       y, 1, stream);
+                       y, use_fast_accum, stream);
 }
 
 fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
@@ -174,8 +196,20 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
     if ((st = fp8_quant_row(gy, 1, M, N, FP8_E5M2_NATIVE, eps, (uint8_t*)L.qg, (float*)L.sg, (float*)L.ig, stream)) !=
         FP8_OK)
       return st;
+    const size_t colws = quant_col_ws_bytes(1, N, K) > 0 ? quant_col_ws_bytes(1, N, K) : 256;
+    if (bwd_kpacked(N, K)) {
+      // w^T k-packed as the grad-input GEMM's B operand
+      if ((st = fp8_quant_col_kpacked(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc,
+                                      L.wscol, colws, stream)) != FP8_OK)
+        return st;
+      if ((st = fp8_scaled_mm_kpacked((const uint8_t*)L.qg, FP8_E5M2_NATIVE, (const uint8_t*)L.qwt, FP8_E4M3_NATIVE,
+                                      FP8_SCALE_ROW, (const float*)L.ig, (const float*)L.iwc, M, K, N, FP8_OUT_BF16,
+                                      gx, 0, stream)) != FP8_OK)
+        return st;
+      return fp8_wgrad_bf16(gy, x, M, N, K, gw, stream);
+    }
     if ((st = fp8_quant_col(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc, L.wscol,
-                            quant_col_ws_bytes(1, N, K) > 0 ? quant_col_ws_bytes(1, N, K) : 256, stream)) != FP8_OK)
+                            colws, stream)) != FP8_OK)
       return st;
   }
   // grad-input: [M][N] x ([K][N])^T -> [M][K]

@@ -30,8 +30,9 @@
  *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
  *  - stream is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on it and returns; results are valid once the stream has
- *    been synchronized. No call synchronizes the device or reads device
- *    data back to the host.
+ *    been synchronized. No call reads device data back to the host, and no
+ *    call synchronizes the device except the one-time probe (fp8_probe) that
+ *    the first *_NATIVE format resolution on a device runs.
  *  - Every argument is validated on the host before anything is launched; on
  *    any error nothing is launched and the status says why. Launch failures return
  *    FP8_ERR_DEVICE; faults inside a kernel surface at the caller's next
@@ -116,7 +117,10 @@ typedef enum {
 /* Measures, on `device`, which e4m3 and e5m2 variants the hardware FP8
  * converts and FP8 matrix-core instructions use (a wrong max silently
  * corrupts results [P-AMD "AMD FP8 format in TorchAO"]). Runs two tiny
- * kernels and synchronizes once; the answer is cached per device.
+ * kernels and synchronizes once; the answer is cached per device. The first
+ * call on a device that resolves a *_NATIVE format (any quantization or GEMM
+ * call) runs this probe and so synchronizes that device once; later calls
+ * read the cache.
  * Returns FP8_ERR_UNSUPPORTED if the device is not gfx950 or the converts and
  * the matrix cores disagree. Output pointers are host pointers, may be NULL. */
 FP8DYN_API fp8_status fp8_probe(int device, fp8_format* e4m3_native, fp8_format* e5m2_native);
@@ -274,15 +278,24 @@ FP8DYN_API fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t row
                                    uint8_t* e8m0, void* stream);
 
 /* ---- GEMMs [P-TAO section 4; P-AMD "Scaling FP8 to MoE Architectures"] ----
- * out[m][n] = a_inv * b_inv * sum_k dec(a[m][k]) * dec(b[n][k]), fp32
- * accumulation on the matrix cores, scales applied in fp32, stored as bf16
- * (round to nearest even) or fp32.
+ * out[m][n] = a_inv * b_inv * sum_k dec(a[m][k]) * dec(b[n][k]) on the matrix
+ * cores, scales applied in fp32, stored as bf16 (round to nearest even) or
+ * fp32.
  * a: [M][K] row-major codes; b: [N][K] row-major codes, i.e. the column-major
  * K x N operand (a Linear weight as stored). fa in {e4m3, e5m2} native
- * variants, fb the e4m3 native variant. K % 16 == 0 (K % 128 == 0 for
- * BLOCK128, K % 32 == 0 for MX32), N % 16 == 0.
- * use_fast_accum is accepted and has no effect: the matrix cores accumulate
- * in fp32 either way [P-TAO section 5]. Scaling: TENSOR or ROW. */
+ * variants; fb must be the e4m3 native variant (an e5m2 B returns
+ * FP8_ERR_UNSUPPORTED). K % 16 == 0 (K % 128 == 0 for BLOCK128, K % 32 == 0
+ * for MX32).
+ * use_fast_accum [P-TAO section 5: fast accumulation in the forward, full
+ * precision in both backward GEMMs]:
+ *  - nonzero: the FP8 matrix-core instructions. Measured on MI355X, each
+ *    one aligns its products to the largest of them and keeps about 12 bits
+ *    below it (error up to ~2^-12 of the instruction's largest product,
+ *    independent of the accumulator); full FP8 rate.
+ *  - 0: full precision. The codes are decoded to bf16 (every e4m3 and e5m2
+ *    value is a bf16 value) and summed by the BF16 matrix-core instructions,
+ *    which accumulate at fp32 precision; the BF16 rate, half the FP8 one.
+ * fp8_scaled_mm scaling: TENSOR or ROW. */
 FP8DYN_API fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                     fp8_scaling scaling, const float* a_inv, const float* b_inv,
                                     int64_t M, int64_t N, int64_t K, fp8_out out_type, void* out,
@@ -292,11 +305,11 @@ FP8DYN_API fp8_status fp8_scaled_mm(const uint8_t* a, fp8_format fa, const uint8
  * 64 K, as fp8_quant_row_kpacked writes a weight and fp8_quant_col_kpacked a
  * transposed one): the same result. Scaling TENSOR or ROW. N % 16 == 0 and
  * K % 128 == 0 (else FP8_ERR_ALIGNMENT); N * K < 2^31 and 16-byte aligned a,
- * b (else FP8_ERR_UNSUPPORTED). No use_fast_accum argument. */
+ * b (else FP8_ERR_UNSUPPORTED). use_fast_accum as for fp8_scaled_mm. */
 FP8DYN_API fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                             fp8_scaling scaling, const float* a_inv, const float* b_inv,
                                             int64_t M, int64_t N, int64_t K, fp8_out out_type, void* out,
-                                            void* stream);
+                                            int use_fast_accum, void* stream);
 
 /* MoE grouped GEMM in one launch: rows [offsets[e], offsets[e+1]) of a use
  * expert e's b[e] ([E][N][K]) and scales. offsets: DEVICE int32 [E+1] with
@@ -304,11 +317,15 @@ FP8DYN_API fp8_status fp8_scaled_mm_kpacked(const uint8_t* a, fp8_format fa, con
  * fp8_validate_offsets on a host copy to check). Empty experts are skipped.
  * Scaling: ROW (a_inv [Mtot] float, b_inv [E][N] float), BLOCK128
  * (a_inv [Mtot][K/128], b_inv [E][N/128][K/128] float; N % 128 == 0) or MX32
- * (E8M0 bytes a [Mtot][K/32], b [E][N][K/32]). */
+ * (E8M0 bytes a [Mtot][K/32], b [E][N][K/32]). use_fast_accum as for
+ * fp8_scaled_mm; with MX32 and use_fast_accum == 0 the E8M0 scales are
+ * folded into the bf16 decode (exact while the scaled codes stay in bf16's
+ * range). */
 FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                      fp8_scaling scaling, const void* a_scale, const void* b_scale,
                                      const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N,
-                                     int64_t K, fp8_out out_type, void* out, void* stream);
+                                     int64_t K, fp8_out out_type, void* out, int use_fast_accum,
+                                     void* stream);
 
 /* fp8_grouped_mm with a pair-interleaved as fp8_quant_row_kpaired writes it
  * and b k-packed as fp8_quant_row_kpacked writes it (each expert's [N][K]
@@ -319,16 +336,21 @@ FP8DYN_API fp8_status fp8_grouped_mm(const uint8_t* a, fp8_format fa, const uint
  * Scaling ROW or MX32 (scales as for fp8_grouped_mm, row-major); BLOCK128
  * and TENSOR return FP8_ERR_UNSUPPORTED. N % 16 == 0, K % 128 == 0 and
  * Mtot % 2 == 0 (else FP8_ERR_ALIGNMENT); N * K < 2^31, K < 2^22 and
- * 16-byte aligned a, b (else FP8_ERR_UNSUPPORTED). */
+ * 16-byte aligned a, b (else FP8_ERR_UNSUPPORTED). use_fast_accum as for
+ * fp8_scaled_mm; full precision (0) with ROW scaling only, else
+ * FP8_ERR_UNSUPPORTED. */
 FP8DYN_API fp8_status fp8_grouped_mm_kpacked(const uint8_t* a, fp8_format fa, const uint8_t* b, fp8_format fb,
                                              fp8_scaling scaling, const void* a_scale, const void* b_scale,
                                              const int32_t* offsets, int32_t E, int64_t Mtot, int64_t N,
-                                             int64_t K, fp8_out out_type, void* out, void* stream);
+                                             int64_t K, fp8_out out_type, void* out, int use_fast_accum,
+                                             void* stream);
 
 /* BF16 weight-gradient GEMM [P-AMD Figure 1 caption: the weight-update GEMM
  * stays in BF16]: gw[n][k] = sum_m gy[m][n] * x[m][k], fp32 accumulation,
  * bf16 out. gy [M][N], x [M][K], gw [N][K], all bf16 row-major; no
- * transposed copies are made. N % 16 == 0, K % 16 == 0, M % 16 == 0. */
+ * transposed copies are made. N % 8 == 0 and K % 8 == 0 (else
+ * FP8_ERR_ALIGNMENT); any M >= 0 (M = 0 writes zeros); gy and x 16-byte
+ * aligned, gw 4-byte aligned. */
 FP8DYN_API fp8_status fp8_wgrad_bf16(const uint16_t* gy, const uint16_t* x, int64_t M, int64_t N,
                                      int64_t K, uint16_t* gw, void* stream);
 
@@ -352,11 +374,16 @@ FP8DYN_API fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t*
 
 /* ---- one Linear layer [P-TAO section 6; P-AMD "AMD FP8 format in TorchAO"] ---
  * Forward y = x w^T: x [M][K], w [N][K] bf16; quantize both (TENSORWISE: one
- * scale each; ROWWISE: per row of x and of w, e4m3), then the scaled GEMM;
- * y [M][N] bf16 or fp32. ws: fp8_linear_ws_bytes(M, N, K, recipe) bytes. */
+ * scale each; ROWWISE: per row of x and of w, e4m3), then the scaled GEMM
+ * with the accumulation use_fast_accum selects (as for fp8_scaled_mm; the
+ * pages' recipe runs the forward with fast accumulation [P-TAO section 5]);
+ * y [M][N] bf16 or fp32. ROWWISE
+ * with N % 16 == 0, K % 128 == 0 and K <= 16384 writes w k-packed
+ * (fp8_quant_row_kpacked, fp8_scaled_mm_kpacked). ws:
+ * fp8_linear_ws_bytes(M, N, K, recipe) bytes. */
 FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                      int64_t K, fp8_recipe recipe, double eps, fp8_out out_type,
-                                     void* y, void* ws, size_t ws_bytes, void* stream);
+                                     int use_fast_accum, void* y, void* ws, size_t ws_bytes, void* stream);
 /* Backward ["FP8 Training: Quantization, Autograd, Torchao" section 4: the
  * grad-input and grad-weight GEMMs]: gy [M][N], x [M][K], w [N][K] bf16.
  * gx [M][K] bf16 = FP8 GEMM of gy (e5m2) and w (e4m3, written transposed
@@ -367,7 +394,11 @@ FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64
  *    scale per tensor); needs M % 16 == 0 (else FP8_ERR_ALIGNMENT) and
  *    M*N, M*K, N*K < 2^30 (else FP8_ERR_UNSUPPORTED);
  *  - ROWWISE_BF16_WGRAD: the BF16 GEMM gy^T x ["FP8 training on AMD GPUs
- *    with TorchTitan and TorchAO" Figure 1 caption]. */
+ *    with TorchTitan and TorchAO" Figure 1 caption]; with N % 128 == 0 and
+ *    K % 16 == 0 w^T is written k-packed (fp8_quant_col_kpacked) for the
+ *    grad-input GEMM.
+ * Both FP8 GEMMs of the backward use full-precision accumulation [P-TAO
+ * section 5]. */
 FP8DYN_API fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w,
                                      int64_t M, int64_t N, int64_t K, fp8_recipe recipe, double eps,
                                      uint16_t* gx, uint16_t* gw, void* ws, size_t ws_bytes,

@@ -96,21 +96,35 @@ def norm_err(y, r) -> float:
     return float(np.abs(y - r).max() / peak) if peak > 0 else float(np.abs(y - r).max())
 
 
-def check_gemm(y, r, S, out_bf16: bool, label: str = ""):
-    """The GEMM acceptance test: normwise max relative error within 1e-2 (bf16 out) or
-    2e-3 (fp32 out), and every element within the componentwise accumulation bound.
+def check_gemm(y, r, S, out_bf16: bool, label: str = "", exact: bool = False):
+    """The GEMM acceptance test against the oracle's fp64 result r.
+
+    exact=True (full-precision accumulation, use_fast_accum off): the floored
+    elementwise error max|y - r| / max(|r|, 1e-3 max|r|) and the normwise error
+    max|y - r| / max|r| are both within 1e-2 (bf16 out) or 2e-3 (fp32 out).
+
+    exact=False (the FP8 matrix-core instructions): the normwise error within the same
+    tolerance, and every element within the componentwise bound of the hardware's
+    per-instruction product alignment (C_ACC above). The floored elementwise error is
+    printed: on outputs near the floor that alignment exceeds it.
     Returns (normwise error, worst componentwise ratio, floored elementwise error)."""
     y = np.asarray(y, np.float64)
     r = np.asarray(r, np.float64)
     S = np.asarray(S, np.float64)
     assert np.all(np.isfinite(y)), f"{label}: non-finite output"
+    tol = TOL_BF16 if out_bf16 else TOL_F32
     ne = norm_err(y, r)
     bound = C_ACC * S + (C_OUT_BF16 if out_bf16 else C_OUT_F32) * np.abs(r) + 1e-30
     ratio = float(np.max(np.abs(y - r) / bound)) if r.size else 0.0
     fe = rel_err(y, r)
-    print(f"{label}: normwise {ne:.3e}  componentwise/bound {ratio:.3f}  floored-elementwise {fe:.3e}", flush=True)
-    assert ne <= (TOL_BF16 if out_bf16 else TOL_F32), (label, ne)
-    assert ratio <= 1.0, (label, ratio)
+    mode = "exact" if exact else "fast"
+    print(f"{label} [{mode}]: normwise {ne:.3e}  componentwise/bound {ratio:.3f}  floored-elementwise {fe:.3e}",
+          flush=True)
+    assert ne <= tol, (label, mode, ne)
+    if exact:
+        assert fe <= tol, (label, mode, fe)
+    else:
+        assert ratio <= 1.0, (label, mode, ratio)
     return ne, ratio, fe
 
 gpu = pytest.mark.gpu

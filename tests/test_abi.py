@@ -83,10 +83,10 @@ def test_host_validation_without_gpu(f):
     assert lib.fp8_scaled_mm(*args, f.SCALE_ROW, FAKE, FAKE, 16, 16, 40, f.OUT_BF16, FAKE, 1, None) == f.ERR_ALIGNMENT
     assert lib.fp8_scaled_mm(*args, 7, FAKE, FAKE, 16, 16, 64, f.OUT_BF16, FAKE, 1, None) == f.ERR_UNSUPPORTED
     assert lib.fp8_scaled_mm(*args, f.SCALE_ROW, FAKE, FAKE, 16, 16, 64, 9, FAKE, 1, None) == f.ERR_INVALID_ARGUMENT
-    assert lib.fp8_grouped_mm(*args, f.SCALE_BLOCK128, FAKE, FAKE, FAKE, 2, 16, 128, 64, f.OUT_BF16, FAKE, None) == f.ERR_ALIGNMENT
-    assert lib.fp8_grouped_mm(*args, f.SCALE_MX32, FAKE, FAKE, FAKE, 2, 16, 128, 48, f.OUT_BF16, FAKE, None) == f.ERR_ALIGNMENT
-    assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 0, 16, 128, 64, f.OUT_BF16, FAKE, None) == f.ERR_INVALID_ARGUMENT
-    assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, None, 2, 16, 128, 64, f.OUT_BF16, FAKE, None) == f.ERR_INVALID_ARGUMENT
+    assert lib.fp8_grouped_mm(*args, f.SCALE_BLOCK128, FAKE, FAKE, FAKE, 2, 16, 128, 64, f.OUT_BF16, FAKE, 1, None) == f.ERR_ALIGNMENT
+    assert lib.fp8_grouped_mm(*args, f.SCALE_MX32, FAKE, FAKE, FAKE, 2, 16, 128, 48, f.OUT_BF16, FAKE, 1, None) == f.ERR_ALIGNMENT
+    assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 0, 16, 128, 64, f.OUT_BF16, FAKE, 1, None) == f.ERR_INVALID_ARGUMENT
+    assert lib.fp8_grouped_mm(*args, f.SCALE_ROW, FAKE, FAKE, None, 2, 16, 128, 64, f.OUT_BF16, FAKE, 1, None) == f.ERR_INVALID_ARGUMENT
     # k-packed rowwise codes: rows % 16, cols % 64, at most 16384 columns
     kp = (f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None)
     assert lib.fp8_quant_row_kpacked(FAKE, 1, 8, 64, *kp) == f.ERR_ALIGNMENT
@@ -94,15 +94,15 @@ def test_host_validation_without_gpu(f):
     assert lib.fp8_quant_row_kpacked(FAKE, 1, 16, 16448, *kp) == f.ERR_UNSUPPORTED
     # k-packed grouped GEMM: ROW or MX32 only, N % 16, K % 128, N * K < 2^31
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_BLOCK128, FAKE, FAKE, FAKE, 2, 16, 128, 128, f.OUT_BF16, FAKE,
-                                      None) == f.ERR_UNSUPPORTED
+                                      1, None) == f.ERR_UNSUPPORTED
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 40, 128, f.OUT_BF16, FAKE,
-                                      None) == f.ERR_ALIGNMENT
+                                      1, None) == f.ERR_ALIGNMENT
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 64, 64, f.OUT_BF16, FAKE,
-                                      None) == f.ERR_ALIGNMENT
+                                      1, None) == f.ERR_ALIGNMENT
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 65536, 32768, f.OUT_BF16, FAKE,
-                                      None) == f.ERR_UNSUPPORTED
+                                      1, None) == f.ERR_UNSUPPORTED
     assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 17, 64, 128, f.OUT_BF16, FAKE,
-                                      None) == f.ERR_ALIGNMENT
+                                      1, None) == f.ERR_ALIGNMENT
     # pair-interleaved rowwise codes: rows % 2, cols % 64
     assert lib.fp8_quant_row_kpaired(FAKE, 1, 3, 64, *kp) == f.ERR_ALIGNMENT
     assert lib.fp8_quant_row_kpaired(FAKE, 1, 2, 96, *kp) == f.ERR_ALIGNMENT
@@ -115,17 +115,33 @@ def test_host_validation_without_gpu(f):
                                      None) == f.ERR_WORKSPACE
     # k-packed dense GEMM: TENSOR or ROW, N % 16, K % 128
     assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_BLOCK128, FAKE, FAKE, 16, 16, 128, f.OUT_BF16, FAKE,
-                                     None) == f.ERR_UNSUPPORTED
+                                     1, None) == f.ERR_UNSUPPORTED
     assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, 16, 24, 128, f.OUT_BF16, FAKE,
-                                     None) == f.ERR_ALIGNMENT
+                                     1, None) == f.ERR_ALIGNMENT
     assert lib.fp8_scaled_mm_kpacked(*args, f.SCALE_ROW, FAKE, FAKE, 16, 16, 64, f.OUT_BF16, FAKE,
-                                     None) == f.ERR_ALIGNMENT
+                                     1, None) == f.ERR_ALIGNMENT
     # linear: workspace too small
     need = lib.fp8_linear_ws_bytes(64, 64, 64, f.RECIPE_ROWWISE_BF16_WGRAD)
     assert need > 64 * 64 * 2
-    assert lib.fp8_linear_fwd(FAKE, FAKE, 64, 64, 64, f.RECIPE_ROWWISE_BF16_WGRAD, 1e-12, f.OUT_BF16, FAKE, FAKE,
+    assert lib.fp8_linear_fwd(FAKE, FAKE, 64, 64, 64, f.RECIPE_ROWWISE_BF16_WGRAD, 1e-12, f.OUT_BF16, 1, FAKE, FAKE,
                               need - 1, None) == f.ERR_WORKSPACE
     assert lib.fp8_wgrad_bf16(FAKE, FAKE, 16, 12, 16, FAKE, None) == f.ERR_ALIGNMENT
+    assert lib.fp8_wgrad_bf16(FAKE, FAKE, 16, 16, 12, FAKE, None) == f.ERR_ALIGNMENT
+    assert lib.fp8_wgrad_bf16(FAKE + 8, FAKE, 16, 16, 16, FAKE, None) == f.ERR_ALIGNMENT
+    # B must be an e4m3 variant: every e5m2 request is refused before any device work
+    for fb in (f.E5M2, f.E5M2FNUZ, f.E5M2_NATIVE):
+        ab = (FAKE, f.E4M3_NATIVE, FAKE, fb)
+        assert lib.fp8_scaled_mm(*ab, f.SCALE_ROW, FAKE, FAKE, 16, 16, 64, f.OUT_BF16, FAKE, 1, None) == \
+            f.ERR_UNSUPPORTED
+        assert lib.fp8_grouped_mm(*ab, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 16, 128, f.OUT_BF16, FAKE, 0, None) == \
+            f.ERR_UNSUPPORTED
+        assert lib.fp8_scaled_mm_kpacked(*ab, f.SCALE_ROW, FAKE, FAKE, 16, 16, 128, f.OUT_BF16, FAKE, 1, None) == \
+            f.ERR_UNSUPPORTED
+        assert lib.fp8_grouped_mm_kpacked(*ab, f.SCALE_ROW, FAKE, FAKE, FAKE, 2, 16, 16, 128, f.OUT_BF16, FAKE, 1,
+                                          None) == f.ERR_UNSUPPORTED
+    # full-precision accumulation on the packed grouped GEMM: ROW scaling only
+    assert lib.fp8_grouped_mm_kpacked(*args, f.SCALE_MX32, FAKE, FAKE, FAKE, 2, 16, 16, 128, f.OUT_BF16, FAKE, 0,
+                                      None) == f.ERR_UNSUPPORTED
 
 
 def test_workspace_sizes(f):

@@ -44,10 +44,37 @@ def _host(out):
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def test_matrix_core_decodes_every_code(f):
+@pytest.mark.parametrize("fast", [True, False])
+def test_code_pair_product_table(f, fast):
+    """The exhaustive code-pair table through the matrix cores: row a of A holds code a
+    at all 128 K positions, row b of B code b, so out[a][b] = 128 dec(a) dec(b), exactly
+    (equal products need no alignment; the value fits fp32), for every pair of finite
+    codes: A in e4m3 and in e5m2, B in e4m3. Both accumulation modes."""
+    import torch
+    e4, e5 = _names(f)
+    tb = oracle.decode(e4, np.arange(256))
+    fb = np.isfinite(tb)
+    b = np.repeat(np.where(fb, np.arange(256), 0).astype(np.uint8)[:, None], 128, axis=1)
+    one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    for fa, name in ((f.E4M3_NATIVE, e4), (f.E5M2_NATIVE, e5)):
+        ta = oracle.decode(name, np.arange(256))
+        fa_ok = np.isfinite(ta)
+        a = np.repeat(np.where(fa_ok, np.arange(256), 0).astype(np.uint8)[:, None], 128, axis=1)
+        out = _out((256, 256), True)
+        f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
+                        use_fast_accum=fast)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        want = 128.0 * np.outer(np.where(fa_ok, ta, 0.0), np.where(fb, tb, 0.0))
+        assert np.array_equal(got, want), (name, fast, int(np.sum(got != want)))
+
+
+@pytest.mark.parametrize("fast", [True, False])
+def test_matrix_core_decodes_every_code(f, fast):
     """A has code c at k = 0 of row c (zeros elsewhere); B row 0 holds the code of 1.0.
     out[c][0] must be exactly the oracle's value of code c, for all finite codes, both
-    formats on the A side and the e4m3 format on the B side."""
+    formats on the A side and the e4m3 format on the B side; both accumulation modes
+    (the full-precision one decodes the codes to bf16 with gfx950's converts)."""
     import torch
     e4, e5 = _names(f)
     one_b = oracle.encode(e4, [1.0])[0]
@@ -61,7 +88,8 @@ def test_matrix_core_decodes_every_code(f):
         b[0, 0] = one_b
         out = _out((256, 16), True)
         one = torch.ones(1, dtype=torch.float32, device="cuda:0")
-        f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out)
+        f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
+                        use_fast_accum=fast)
         torch.cuda.synchronize()
         got = out.cpu().numpy()[:, 0].astype(np.float64)
         assert np.array_equal(got[fin], tab[fin]), name
@@ -75,7 +103,8 @@ def test_matrix_core_decodes_every_code(f):
     a[0, 0] = one_b
     out = _out((16, 256), True)
     one = torch.ones(1, dtype=torch.float32, device="cuda:0")
-    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out)
+    f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
+                    use_fast_accum=fast)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy()[0].astype(np.float64)[fin], tab[fin])
 
@@ -100,7 +129,8 @@ def test_small_integer_products_are_exact(f):
                                    (300, 520, 1152), (64, 64, 128), (200, 136, 256), (2100, 8200, 128)])
 @pytest.mark.parametrize("scaling", ["tensor", "row"])
 @pytest.mark.parametrize("out_f32", [True, False])
-def test_scaled_mm(f, M, N, K, scaling, out_f32):
+@pytest.mark.parametrize("fast", [True, False])
+def test_scaled_mm(f, M, N, K, scaling, out_f32, fast):
     import torch
     e4, _ = _names(f)
     rng = np.random.default_rng(M * 7 + N)
@@ -113,12 +143,12 @@ def test_scaled_mm(f, M, N, K, scaling, out_f32):
         sk = f.SCALE_ROW
     out = _out((M, N), out_f32)
     f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, sk, to_dev(sa), to_dev(sb),
-                    f.OUT_F32 if out_f32 else f.OUT_BF16, out)
+                    f.OUT_F32 if out_f32 else f.OUT_BF16, out, use_fast_accum=fast)
     torch.cuda.synchronize()
     osk = oracle.SCALE_TENSOR if scaling == "tensor" else oracle.SCALE_ROW
     ref = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb)
     S = oracle.scaled_mm(a, e4, b, e4, osk, sa, sb, absolute=True)
-    check_gemm(_host(out), ref, S, not out_f32, f"scaled_mm {M}x{N}x{K} {scaling}")
+    check_gemm(_host(out), ref, S, not out_f32, f"scaled_mm {M}x{N}x{K} {scaling}", exact=not fast)
 
 
 def test_scaled_mm_e5m2_a(f):
@@ -167,7 +197,8 @@ def _offsets(counts):
 @pytest.mark.parametrize("counts,N,K", [([37, 0, 300, 1, 0, 513], 272, 384), ([0, 0, 64], 128, 128),
                                          ([256], 256, 256), ([5] * 40, 64, 512), ([300, 5, 0, 129], 320, 640),
                                          ([17], 64, 128), ([600, 0, 3], 512, 1152)])
-def test_grouped_row(f, counts, N, K):
+@pytest.mark.parametrize("fast", [True, False])
+def test_grouped_row(f, counts, N, K, fast):
     import torch
     e4, _ = _names(f)
     rng = np.random.default_rng(sum(counts) + N)
@@ -178,19 +209,20 @@ def test_grouped_row(f, counts, N, K):
     sb = rng.uniform(0.1, 2, (E, N)).astype(np.float32)
     out = torch.full((Mt, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_ROW, to_dev(sa), to_dev(sb),
-                     to_dev(off), f.OUT_BF16, out)
+                     to_dev(off), f.OUT_BF16, out, use_fast_accum=fast)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_ROW, sa, sb, off)
     S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_ROW, sa, sb, off, absolute=True)
     got = _host(out)
     assert not np.any(np.isnan(got)), "rows left unwritten"
-    check_gemm(got, ref, S, True, f"grouped row {counts}")
+    check_gemm(got, ref, S, True, f"grouped row {counts}", exact=not fast)
 
 
 @pytest.mark.parametrize("counts,N,K,out_f32", [([100, 0, 200, 7], 256, 384, False), ([512, 512], 128, 256, False),
                                                  ([64], 128, 128, False), ([300, 5, 0, 129], 384, 640, True),
                                                  ([4096, 4096], 2304, 128, False)])
-def test_grouped_block(f, counts, N, K, out_f32):
+@pytest.mark.parametrize("fast", [True, False])
+def test_grouped_block(f, counts, N, K, out_f32, fast):
     """One K block (no prefetch), an odd number of K blocks, a partial B tile and fp32
     output, and more tiles than workgroups (each walks several, reusing its LDS slots)."""
     import torch
@@ -203,11 +235,11 @@ def test_grouped_block(f, counts, N, K, out_f32):
     sb = rng.uniform(0.01, 4, (E, N // 128, K // 128)).astype(np.float32)
     out = _out((Mt, N), out_f32)
     f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_BLOCK128, to_dev(sa), to_dev(sb),
-                     to_dev(off), f.OUT_F32 if out_f32 else f.OUT_BF16, out)
+                     to_dev(off), f.OUT_F32 if out_f32 else f.OUT_BF16, out, use_fast_accum=fast)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off)
     S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off, absolute=True)
-    check_gemm(_host(out), ref, S, not out_f32, f"grouped block {counts} K={K}")
+    check_gemm(_host(out), ref, S, not out_f32, f"grouped block {counts} K={K}", exact=not fast)
 
 
 @pytest.mark.parametrize("counts,N,K,shift", [([100, 0, 200, 7], 256, 384, 0), ([512, 512], 128, 256, 0),
@@ -216,7 +248,8 @@ def test_grouped_block(f, counts, N, K, out_f32):
                                                ([300, 5, 0, 129], 320, 1024, 0), ([64], 192, 512, 0),
                                                ([600, 0, 3], 512, 2048, 0), ([300, 5, 0, 129], 320, 1024, 4),
                                                ([1536, 1536], 6144, 512, 0)])
-def test_grouped_mx(f, counts, N, K, shift):
+@pytest.mark.parametrize("fast", [True, False])
+def test_grouped_mx(f, counts, N, K, shift, fast):
     """K % 512 == 0 with 16-byte aligned scales takes the kernel's 16-bytes-per-row
     scale loads; other K, or scales at a 4-byte offset (shift), the dword loads."""
     import torch
@@ -236,11 +269,11 @@ def test_grouped_mx(f, counts, N, K, shift):
         v.copy_(to_dev(x).reshape(-1))
         return v
     f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_MX32, shifted(sa), shifted(sb),
-                     to_dev(off), f.OUT_BF16, out)
+                     to_dev(off), f.OUT_BF16, out, use_fast_accum=fast)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_MX32, sa, sb, off)
     S = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_MX32, sa, sb, off, absolute=True)
-    check_gemm(_host(out), ref, S, True, f"grouped mx {counts}")
+    check_gemm(_host(out), ref, S, True, f"grouped mx {counts}", exact=not fast)
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 264, 136), (1000, 512, 256), (7, 16, 8), (128, 264, 136),

@@ -30,8 +30,10 @@ def _ws(f, M, N, K, recipe):
     return torch.empty(f.fp8_linear_ws_bytes(M, N, K, recipe), dtype=torch.uint8, device="cuda:0")
 
 
-def test_linear_tensorwise_forward_fp32(f):
-    """256 x 512 input, 512 x 512 weight, one scale each, fp32 out."""
+@pytest.mark.parametrize("fast", [True, False])
+def test_linear_tensorwise_forward_fp32(f, fast):
+    """256 x 512 input, 512 x 512 weight, one scale each, fp32 out; both accumulation
+    modes (full precision meets the floored elementwise 2e-3 fp32 bar)."""
     import torch
     e4, _ = _names(f)
     w = synth.linear_tensorwise()
@@ -39,21 +41,24 @@ def test_linear_tensorwise_forward_fp32(f):
     M, K, N = x.shape[0], x.shape[1], wt.shape[0]
     y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
     f.fp8_linear_fwd(to_dev_bf16(x), to_dev_bf16(wt), f.RECIPE_TENSORWISE, EPS, f.OUT_F32, y,
-                     _ws(f, M, N, K, f.RECIPE_TENSORWISE))
+                     _ws(f, M, N, K, f.RECIPE_TENSORWISE), use_fast_accum=fast)
     torch.cuda.synchronize()
     qx, _, ix = oracle.quant_tensor(x, e4, EPS)
     qw, _, iw = oracle.quant_tensor(wt, e4, EPS)
     ref = oracle.scaled_mm(qx, e4, qw, e4, oracle.SCALE_TENSOR, ix, iw)
     S = oracle.scaled_mm(qx, e4, qw, e4, oracle.SCALE_TENSOR, ix, iw, absolute=True)
-    check_gemm(y.cpu().numpy(), ref, S, False, "tensorwise linear fwd (fp32 out)")
+    check_gemm(y.cpu().numpy(), ref, S, False, "tensorwise linear fwd (fp32 out)", exact=not fast)
 
 
 @pytest.mark.parametrize("recipe", ["rowwise", "tensorwise"])
-def test_linear_small_fwd_bwd(f, recipe):
+@pytest.mark.parametrize("K,N", [(384, 272), (256, 384)])
+def test_linear_small_fwd_bwd(f, recipe, K, N):
+    """(384, 272): the rowwise forward's weight k-packed, its backward's row-major;
+    (256, 384): both k-packed (N % 128 == 0)."""
     import torch
     e4, e5 = _names(f)
     # rowwise takes any M; the all-FP8 tensorwise backward needs M % 16 == 0
-    M, K, N = (200 if recipe == "rowwise" else 208), 384, 272
+    M = 200 if recipe == "rowwise" else 208
     x = synth.normal_bf16((M, K), 801, 1.0)
     synth.add_outliers(x, 802, 0.01, 50.0)
     wt = synth.normal_bf16((N, K), 803, 0.02)
@@ -92,8 +97,11 @@ def test_linear_small_fwd_bwd(f, recipe):
         _, qgT, _, ig2, qxT, _, ix2 = oracle.quant_dual(gy, x, e5, e4, EPS)
         ref_gw = oracle.scaled_mm(qgT, e5, qxT, e4, sk, ig2, ix2)
         S_gw = oracle.scaled_mm(qgT, e5, qxT, e4, sk, ig2, ix2, absolute=True)
-    for name, got, ref, S in (("y", y, ref_y, S_y), ("gx", gx, ref_gx, S_gx), ("gw", gw, ref_gw, S_gw)):
-        check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}")
+    # the forward runs the fast accumulation; both backward GEMMs full precision (the
+    # BF16 grad-weight of the rowwise recipe sums at fp32 precision too)
+    for name, got, ref, S, ex in (("y", y, ref_y, S_y, False), ("gx", gx, ref_gx, S_gx, True),
+                                  ("gw", gw, ref_gw, S_gw, True)):
+        check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}", exact=ex)
 
 
 def test_linear_tensorwise_bwd_needs_m_multiple_of_16(f):

@@ -1,7 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
 times: every quantized byte and scale against the oracle (bit-exact), GEMM outputs on
-sampled positions the oracle computes one by one (every expert's first and last row,
-the tile corners, plus seeded random positions)."""
+sampled positions the oracle computes one by one. The samples cover every 256 x 256
+output tile of every expert (two random positions and two corners per tile) plus
+seeded random positions. Each FP8 GEMM runs in both accumulation modes: the full
+precision one is held to the floored elementwise bar, the fast one to the hardware's
+componentwise bound (check_gemm)."""
 import numpy as np
 import pytest
 
@@ -26,19 +29,23 @@ def _names(f):
     return name[e4], name[e5]
 
 
-def _samples(M, N, seed, n=2048, offsets=None):
+def _samples(M, N, seed, n=2048, offsets=None, tile=256):
+    """Output positions to check: in every tile x tile output tile of every expert (the
+    kernels' tiles start at each expert's first row), two seeded random positions and
+    its first and last corner; then n seeded random positions over the whole output."""
     rng = np.random.default_rng(seed)
-    rows = list(rng.integers(0, M, n))
-    cols = list(rng.integers(0, N, n))
-    edge_r = [0, M - 1]
-    if offsets is not None:
-        for e in range(len(offsets) - 1):
-            if offsets[e + 1] > offsets[e]:
-                edge_r += [int(offsets[e]), int(offsets[e + 1]) - 1]
-    for r in edge_r:
-        for c in (0, N - 1, N // 2):
-            rows.append(r)
-            cols.append(c)
+    off = np.asarray(offsets if offsets is not None else [0, M], np.int64)
+    rows, cols = [], []
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        for m0 in range(lo, hi, tile):
+            m1 = min(m0 + tile, hi)
+            for n0 in range(0, N, tile):
+                n1 = min(n0 + tile, N)
+                rows += list(rng.integers(m0, m1, 2)) + [m0, m1 - 1]
+                cols += list(rng.integers(n0, n1, 2)) + [n0, n1 - 1]
+    rows += list(rng.integers(0, M, n))
+    cols += list(rng.integers(0, N, n))
     return np.array(rows, np.int64), np.array(cols, np.int64)
 
 
@@ -109,8 +116,17 @@ def test_linear_rowwise_llama3_8b_mlp(f):
     assert torch.equal(iwp, iw) and torch.equal(iwcp, iwc)
     assert torch.equal(pair[1].view(torch.int16), pair[0].view(torch.int16)), "k-packed forward differs"
     assert torch.equal(gpair[1].view(torch.int16), gpair[0].view(torch.int16)), "k-packed grad-input differs"
-    del qwp, qwtp, pair, gpair
-    _log("linear_rowwise k-packed weights and GEMMs bit-identical")
+    # full precision: the same bits from the k-packed and the row-major weights too
+    y_ex = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0") for _ in range(2)]
+    f.fp8_scaled_mm(qx, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ix, iw, f.OUT_BF16, y_ex[0],
+                    use_fast_accum=False)
+    f.fp8_scaled_mm_kpacked(qx, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, ix, iwp, f.OUT_BF16, y_ex[1], N,
+                            use_fast_accum=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ex[1].view(torch.int16), y_ex[0].view(torch.int16)), "k-packed exact forward differs"
+    y_exact, gx_fast, y_fast_rm = y_ex[0], gpair[0], pair[0]
+    del qwp, qwtp, pair, gpair, y_ex
+    _log("linear_rowwise k-packed weights and GEMMs bit-identical (both accumulation modes)")
 
     rc = f.RECIPE_ROWWISE_BF16_WGRAD
     lws = torch.empty(f.fp8_linear_ws_bytes(M, N, K, rc), dtype=torch.uint8, device="cuda:0")
@@ -120,18 +136,23 @@ def test_linear_rowwise_llama3_8b_mlp(f):
     f.fp8_linear_fwd(xd, wd, rc, EPS, f.OUT_BF16, y, lws)
     f.fp8_linear_bwd(gd, xd, wd, rc, EPS, gx, gw, lws)
     torch.cuda.synchronize()
+    # the Linear call's forward is the fast accumulation (k-packed weight): the same
+    # bits as the row-major fast GEMM above
+    assert torch.equal(y.view(torch.int16), y_fast_rm.view(torch.int16)), "fp8_linear_fwd differs"
     r, c = _samples(M, N, 1)
     ref = oracle.scaled_mm_sample(r_qx, e4, r_qw, e4, oracle.SCALE_ROW, r_ix, r_iw, r, c)
     S = oracle.scaled_mm_sample(r_qx, e4, r_qw, e4, oracle.SCALE_ROW, r_ix, r_iw, r, c, absolute=True)
     check_gemm(_gather(y, r, c), ref, S, True, "linear_rowwise forward (sampled)")
+    check_gemm(_gather(y_exact, r, c), ref, S, True, "linear_rowwise forward (sampled)", exact=True)
     r, c = _samples(M, K, 2)
     ref = oracle.scaled_mm_sample(r_qg, e5, r_qwt, e4, oracle.SCALE_ROW, r_ig, r_iwc, r, c)
     S = oracle.scaled_mm_sample(r_qg, e5, r_qwt, e4, oracle.SCALE_ROW, r_ig, r_iwc, r, c, absolute=True)
-    check_gemm(_gather(gx, r, c), ref, S, True, "linear_rowwise grad-input (sampled)")
+    check_gemm(_gather(gx, r, c), ref, S, True, "linear_rowwise grad-input (sampled)", exact=True)
+    check_gemm(_gather(gx_fast, r, c), ref, S, True, "linear_rowwise grad-input (sampled)")
     r, c = _samples(N, K, 3)
     ref = oracle.wgrad_bf16_sample(gy, x, r, c)
     S = oracle.wgrad_bf16_sample(gy, x, r, c, absolute=True)
-    check_gemm(_gather(gw, r, c), ref, S, True, "linear_rowwise grad-weight bf16 (sampled)")
+    check_gemm(_gather(gw, r, c), ref, S, True, "linear_rowwise grad-weight bf16 (sampled)", exact=True)
 
 
 def test_fused_rmsnorm_quant_llama3_8b_activation(f):
@@ -191,11 +212,11 @@ def test_linear_tensorwise_all_fp8_backward_llama3_8b_mlp(f):
     r, c = _samples(M, K, 4)
     ref = oracle.scaled_mm_sample(r_gq, e5, r_qwt, e4, oracle.SCALE_TENSOR, r_gi, r_iw, r, c)
     S = oracle.scaled_mm_sample(r_gq, e5, r_qwt, e4, oracle.SCALE_TENSOR, r_gi, r_iw, r, c, absolute=True)
-    check_gemm(_gather(gx, r, c), ref, S, True, "tensorwise grad-input (sampled)")
+    check_gemm(_gather(gx, r, c), ref, S, True, "tensorwise grad-input (sampled)", exact=True)
     r, c = _samples(N, K, 5)
     ref = oracle.scaled_mm_sample(r_gqT, e5, r_xqT, e4, oracle.SCALE_TENSOR, r_gi, r_xi, r, c)
     S = oracle.scaled_mm_sample(r_gqT, e5, r_xqT, e4, oracle.SCALE_TENSOR, r_gi, r_xi, r, c, absolute=True)
-    check_gemm(_gather(gw, r, c), ref, S, True, "tensorwise FP8 grad-weight (sampled)")
+    check_gemm(_gather(gw, r, c), ref, S, True, "tensorwise FP8 grad-weight (sampled)", exact=True)
 
 
 def test_expert_colwise(f):
@@ -256,6 +277,14 @@ def test_moe_grouped_forward(f):
     del ad, wd
     assert torch.equal(outp.view(torch.int16), out.view(torch.int16)), "k-packed GEMM differs from row-major"
     assert torch.equal(iwp, iw) and torch.equal(swp, sw) and torch.equal(iap, ia) and torch.equal(sap, sa)
+    # full precision, row-major and packed: the same bits
+    out_x = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_ROW, ia, iw, to_dev(off), f.OUT_BF16, out_x,
+                     use_fast_accum=False)
+    f.fp8_grouped_mm_kpacked(qap, f.E4M3_NATIVE, qwp, f.E4M3_NATIVE, f.SCALE_ROW, iap, iwp, to_dev(off), f.OUT_BF16,
+                             outp, N, use_fast_accum=False)
+    torch.cuda.synchronize()
+    assert torch.equal(outp.view(torch.int16), out_x.view(torch.int16)), "k-packed exact GEMM differs"
     del outp
     r_qa, _, r_ia = oracle.quant_row(a, e4, EPS)
     assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
@@ -270,6 +299,7 @@ def test_moe_grouped_forward(f):
     ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c)
     S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_ROW, r_ia, r_iw, off, r, c, absolute=True)
     check_gemm(_gather(out, r, c), ref, S, True, "moe_grouped gemm (sampled)")
+    check_gemm(_gather(out_x, r, c), ref, S, True, "moe_grouped gemm (sampled)", exact=True)
 
 
 def test_moe_backward(f):
@@ -296,7 +326,10 @@ def test_moe_backward(f):
     iT = torch.empty_like(sT)
     f.fp8_quant_col(wd, f.E4M3_NATIVE, EPS, qT, sT, iT, None)
     gx = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda:0")
-    f.fp8_grouped_mm(qg, f.E5M2_NATIVE, qT, f.E4M3_NATIVE, f.SCALE_ROW, ig, iT, offd, f.OUT_BF16, gx)
+    gx_fast = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_grouped_mm(qg, f.E5M2_NATIVE, qT, f.E4M3_NATIVE, f.SCALE_ROW, ig, iT, offd, f.OUT_BF16, gx,
+                     use_fast_accum=False)
+    f.fp8_grouped_mm(qg, f.E5M2_NATIVE, qT, f.E4M3_NATIVE, f.SCALE_ROW, ig, iT, offd, f.OUT_BF16, gx_fast)
     gw = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_wgrad_bf16(gd, ad, offd, gw)
     torch.cuda.synchronize()
@@ -309,20 +342,20 @@ def test_moe_backward(f):
     r, c = _samples(Mt, K, 6, offsets=off)
     ref = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c)
     S = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c, absolute=True)
-    check_gemm(_gather(gx, r, c), ref, S, True, "moe grouped grad-input (sampled)")
-    rng = np.random.default_rng(7)
+    check_gemm(_gather(gx, r, c), ref, S, True, "moe grouped grad-input (sampled)", exact=True)
+    check_gemm(_gather(gx_fast, r, c), ref, S, True, "moe grouped grad-input (sampled)")
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             assert torch.count_nonzero(gw[e]).item() == 0, f"empty expert {e}"
             continue
-        ns = np.concatenate([rng.integers(0, N, 96), [0, N - 1]])
-        ks = np.concatenate([rng.integers(0, K, 96), [K - 1, 0]])
+        # every 256 x 256 tile of the expert's [N][K] gradient, and 64 random positions
+        ns, ks = _samples(N, K, 700 + e, n=64)
         gs, xs = np.ascontiguousarray(go[lo:hi]), np.ascontiguousarray(a[lo:hi])
         ref = oracle.wgrad_bf16_sample(gs, xs, ns, ks)
         S = oracle.wgrad_bf16_sample(gs, xs, ns, ks, absolute=True)
         got = gw[e][torch.from_numpy(ns).cuda(), torch.from_numpy(ks).cuda()].float().cpu().numpy()
-        check_gemm(got.astype(np.float64), ref, S, True, f"moe grouped grad-weight expert {e} (sampled)")
+        check_gemm(got.astype(np.float64), ref, S, True, f"moe grouped grad-weight expert {e} (sampled)", exact=True)
 
 
 def test_moe_block_and_mx(f):
@@ -345,7 +378,10 @@ def test_moe_block_and_mx(f):
     iw = torch.empty_like(sw)
     f.fp8_quant_block(wd, 128, 128, f.E4M3_NATIVE, EPS, qw, sw, iw)
     out = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
+    out_x = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_BLOCK128, ia, iw, offd, f.OUT_BF16, out)
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_BLOCK128, ia, iw, offd, f.OUT_BF16, out_x,
+                     use_fast_accum=False)
     torch.cuda.synchronize()
     r_qa, _, r_ia = oracle.quant_block(a, 1, 128, e4, EPS)
     assert np.array_equal(u8(qa), r_qa) and np.array_equal(ia.cpu().numpy(), r_ia)
@@ -355,6 +391,7 @@ def test_moe_block_and_mx(f):
     ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_BLOCK128, r_ia, r_iw, off, r, c)
     S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_BLOCK128, r_ia, r_iw, off, r, c, absolute=True)
     check_gemm(_gather(out, r, c), ref, S, True, "moe blockwise gemm (sampled)")
+    check_gemm(_gather(out_x, r, c), ref, S, True, "moe blockwise gemm (sampled)", exact=True)
     del r_qw
     # MX
     ea = torch.empty((Mt, K // 32), dtype=torch.uint8, device="cuda:0")
@@ -362,6 +399,8 @@ def test_moe_block_and_mx(f):
     ew = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda:0")
     f.fp8_quant_mx(wd, f.E4M3_NATIVE, f.MX_POW2_FLOOR, EPS, qw, ew)
     f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_MX32, ea, ew, offd, f.OUT_BF16, out)
+    f.fp8_grouped_mm(qa, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_MX32, ea, ew, offd, f.OUT_BF16, out_x,
+                     use_fast_accum=False)
     torch.cuda.synchronize()
     r_qa, r_ea = oracle.quant_mx(a, e4, oracle.MX_POW2_FLOOR, EPS)
     assert np.array_equal(u8(qa), r_qa) and np.array_equal(u8(ea), r_ea)
@@ -370,3 +409,4 @@ def test_moe_block_and_mx(f):
     ref = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_MX32, r_ea, r_ew, off, r, c)
     S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_MX32, r_ea, r_ew, off, r, c, absolute=True)
     check_gemm(_gather(out, r, c), ref, S, True, "moe MX gemm (sampled)")
+    check_gemm(_gather(out_x, r, c), ref, S, True, "moe MX gemm (sampled)", exact=True)
