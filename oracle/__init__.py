@@ -65,6 +65,7 @@ def _load():
         "orc_quant_tensor": (None, [P, I64, I, D, P, P, P, P]),
         "orc_quant_row": (None, [P, I64, I64, I64, I, D, P, P, P, I]),
         "orc_norm_row": (None, [P, P, P, I64, I64, I, D, P]),
+        "orc_norm_stats": (None, [P, I64, I64, P, P]),
         "orc_norm_quant_row": (None, [P, P, P, I64, I64, I, D, I, D, P, P, P, P]),
         "orc_quant_col": (None, [P, I64, I64, I64, I, D, P, P, P, I]),
         "orc_quant_block": (None, [P, I64, I64, I64, I64, I64, I, D, P, P, P, I]),
@@ -173,6 +174,17 @@ def norm_row(x, gamma, beta=None, layer=False, norm_eps=1e-6):
     y = np.empty((rows, cols), np.uint16)
     _load().orc_norm_row(_p(x), _p(g), _p(b), rows, cols, int(bool(layer)), float(norm_eps), _p(y))
     return y
+
+
+def norm_stats(x):
+    """(s1, s2) per row of x [rows][cols] bf16 bits: the exact sums of x and x^2,
+    each rounded once to fp64 (norm.c, step 1)."""
+    x = _u16(x)
+    rows, cols = x.shape
+    s1 = np.empty(rows, np.float64)
+    s2 = np.empty(rows, np.float64)
+    _load().orc_norm_stats(_p(x), rows, cols, _p(s1), _p(s2))
+    return s1, s2
 
 
 def norm_quant_row(x, gamma, beta=None, layer=False, norm_eps=1e-6, fmt="e4m3fn", eps=1e-12):

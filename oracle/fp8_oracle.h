@@ -100,6 +100,9 @@ void orc_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
  * activation); q/scale/inv as orc_quant_row of y. */
 void orc_norm_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
                   int64_t cols, int layer, double norm_eps, uint16_t* y);
+/* The row sums the normalization starts from: s1[r] = sum x, s2[r] = sum x^2,
+ * each the exact sum rounded once to fp64. */
+void orc_norm_stats(const uint16_t* x, int64_t rows, int64_t cols, double* s1, double* s2);
 void orc_norm_quant_row(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows,
                         int64_t cols, int layer, double norm_eps, int fmt, double eps, uint16_t* y,
                         uint8_t* q, float* scale, float* inv);
