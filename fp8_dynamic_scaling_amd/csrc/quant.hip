@@ -1044,16 +1044,91 @@ hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps,
 // write and the next layer's amax pass become one memory pass). One
 // 256-thread workgroup per row; the row stays in registers from the load to
 // the FP8 store, so x is read once and y (bf16) is written only if asked.
-//  1. s1 = sum x, s2 = sum x^2 in fp64 (every bf16 value and square is exact
-//     in fp64, so while the row's sums fit in 53 bits they are exact in any
-//     order; s2 accumulates with fused multiply-adds, which round like the
-//     separate add because the product is exact);
+//  1. s1 = sum x, s2 = sum x^2: the exact sums rounded once to fp64. The row
+//     is summed in fp64 (s2 with fused multiply-adds: x * x is exact). That
+//     is exact in any order when every term is a multiple of one unit u and
+//     the sum of the |terms| stays below 2^53 u: each partial sum is then an
+//     fp64 value. With u = 2^(2 qmin) for the squares (x = M 2^q, M < 256,
+//     qmin the row's smallest q) the computed s2 < 2^52 u proves it for s2,
+//     and for s1 too (sum |x| <= sqrt(n s2) < 2^(33 + qmin) for n <= 2^14).
+//     A row that fails the test sums again exactly: integer terms
+//     M 2^(q + 133) and M^2 2^(2 q + 266) added with LDS atomics into limbs of
+//     32 bits held in 64-bit words, then rounded once to fp64;
 //  2. mean, mean square, var (LayerNorm) and rstd = 1 / sqrt(var + norm_eps):
 //     fp64 IEEE operations (no contraction);
 //  3. y = ((x - mean32) * rstd32) * gamma + beta (LayerNorm) or
 //     (x * rstd32) * gamma (RMSNorm), fp32 IEEE operations, stored as bf16
 //     (RNE);
 //  4. amax of the bf16 row, scale, clamp and cast as in k_quant_row.
+constexpr int kS1Limbs = 10;  // sum x in units of 2^-133: below 2^275 for 2^14 terms
+constexpr int kS2Limbs = 18;  // sum x^2 in units of 2^-266: below 2^536
+
+// Exact row sums (the slow path of step 1): limbs L[0..n) hold 32-bit digits
+// in 64-bit words; called by one lane after all the atomics landed. Carries
+// go up (arithmetic shifts keep the sign in the top word), a negative total
+// is negated, and the magnitude is rounded to the nearest fp64, ties to even.
+__device__ __noinline__ double limbs_to_double(long long* L, int n, int unit_exp) {
+  for (int i = 0; i < n - 1; ++i) {
+    const long long c = L[i] >> 32;
+    L[i] -= c * 4294967296LL;
+    L[i + 1] += c;
+  }
+  const bool neg = L[n - 1] < 0;
+  if (neg) {
+    for (int i = 0; i < n; ++i) L[i] = -L[i];
+    for (int i = 0; i < n - 1; ++i) {
+      const long long c = L[i] >> 32;
+      L[i] -= c * 4294967296LL;
+      L[i + 1] += c;
+    }
+  }
+  int h = n - 1;
+  while (h >= 0 && L[h] == 0) --h;
+  if (h < 0) return 0.0;
+  const uint32_t top = (uint32_t)L[h];
+  const int lead = 32 * h + 31 - __clz(top);
+  // bits [32 (h - 1), 32 h + 32) of the magnitude, and the next digit below
+  const uint64_t hi = ((uint64_t)top << 32) | (h >= 1 ? (uint64_t)(uint32_t)L[h - 1] : 0);
+  const uint32_t lo = h >= 2 ? (uint32_t)L[h - 2] : 0u;
+  const int sh = 63 - (lead - 32 * (h - 1));  // brings the leading one to bit 63
+  const uint64_t w = sh ? (hi << sh) | ((uint64_t)lo >> (32 - sh)) : hi;
+  bool sticky = (w & 0x3ffu) != 0 || (sh ? (uint32_t)(lo << sh) != 0u : lo != 0u);
+  for (int i = h - 3; i >= 0 && !sticky; --i) sticky = L[i] != 0;
+  uint64_t sig = w >> 11;
+  const bool round = (w >> 10) & 1u;
+  int e = lead - 52 + unit_exp;
+  if (round && (sticky || (sig & 1u))) {
+    sig += 1;
+    if (sig == (1ull << 53)) {
+      sig >>= 1;
+      e += 1;
+    }
+  }
+  const double v = ldexp((double)sig, e);
+  return neg ? -v : v;
+}
+
+// Adds one bf16 value (and its square) as integers to the limbs.
+template <bool LAYER>
+__device__ __forceinline__ void exact_add(uint32_t b, long long* L1, long long* L2) {
+  const uint32_t v = b & 0x7fffu;
+  if (v == 0) return;
+  const uint32_t E = v >> 7;
+  const uint64_t M = E ? 128u + (v & 0x7fu) : (v & 0x7fu);
+  const int sh = (E ? (int)E : 1) - 1;  // q + 133
+  if constexpr (LAYER) {
+    const uint64_t t = M << (sh & 31);
+    const long long lo = (long long)(t & 0xffffffffu), hi = (long long)(t >> 32);
+    const bool ng = (b & 0x8000u) != 0;
+    atomicAdd(reinterpret_cast<unsigned long long*>(&L1[sh >> 5]), (unsigned long long)(ng ? -lo : lo));
+    if (hi) atomicAdd(reinterpret_cast<unsigned long long*>(&L1[(sh >> 5) + 1]), (unsigned long long)(ng ? -hi : hi));
+  }
+  const int s2 = 2 * sh;
+  const uint64_t t = (M * M) << (s2 & 31);
+  atomicAdd(reinterpret_cast<unsigned long long*>(&L2[s2 >> 5]), (unsigned long long)(t & 0xffffffffu));
+  if (t >> 32) atomicAdd(reinterpret_cast<unsigned long long*>(&L2[(s2 >> 5) + 1]), (unsigned long long)(t >> 32));
+}
+
 template <int TPR, int J, bool E5, bool LAYER>
 __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ gamma,
@@ -1062,17 +1137,23 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
                                                         uint8_t* __restrict__ q, float* __restrict__ scale,
                                                         float* __restrict__ inv, double fmax, double eps) {
   // TPR threads per row: 64 (one wavefront per row, 4 rows per workgroup, no
-  // LDS and no barrier) for rows up to 4096 elements, else 256
+  // barrier; LDS only in the exact-sum path) for rows up to 4096 elements,
+  // else 256
   static_assert(TPR == 64 || TPR == 256, "threads per row");
   __shared__ double red_d[2][4];
+  __shared__ uint32_t red_e[4];
   __shared__ float red[4];
+  __shared__ long long s_limbs[TPR == 64 ? 4 : 1][kS1Limbs + kS2Limbs];
+  __shared__ double s_exact[TPR == 64 ? 4 : 1][2];
   const int tid = threadIdx.x;
   const int t = TPR == 64 ? (tid & 63) : tid;
+  const int slot = TPR == 64 ? (tid >> 6) : 0;
   const int64_t row = TPR == 64 ? (int64_t)blockIdx.x * 4 + (tid >> 6) : (int64_t)blockIdx.x;
   if (TPR == 64 && row >= rows) return;
   const uint16_t* xr = x + row * cols;
   uint4 v[J];
   double s1 = 0.0, s2 = 0.0;
+  uint32_t emin = 0x7f80u;  // smallest exponent field of a nonzero value (the field of v - 1: never larger)
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int64_t c = 8 * (t + TPR * j);
@@ -1088,22 +1169,56 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
       // x * x is exact in fp64, so the fused multiply-add rounds exactly as
       // s2 + x * x does, with one fp64 operation instead of two
       s2 = __fma_rn(hi, hi, __fma_rn(lo, lo, s2));
+      const uint32_t a = w[k] & 0x7fffu, b = (w[k] >> 16) & 0x7fffu;
+      emin = min(emin, min((a - 1u) & 0x7f80u, (b - 1u) & 0x7f80u));
     }
   }
-  // row sums (fp64): the wavefront, then (256 threads per row) the 4 waves
+  // row sums (fp64) and the smallest exponent: the wavefront, then (256
+  // threads per row) the 4 waves
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     if constexpr (LAYER) s1 = __dadd_rn(s1, __shfl_xor(s1, o, 64));
     s2 = __dadd_rn(s2, __shfl_xor(s2, o, 64));
+    emin = min(emin, (uint32_t)__shfl_xor((int)emin, o, 64));
   }
   if constexpr (TPR == 256) {
     if ((tid & 63) == 0) {
       red_d[0][tid >> 6] = s1;
       red_d[1][tid >> 6] = s2;
+      red_e[tid >> 6] = emin;
     }
     __syncthreads();
     s1 = __dadd_rn(__dadd_rn(red_d[0][0], red_d[0][1]), __dadd_rn(red_d[0][2], red_d[0][3]));
     s2 = __dadd_rn(__dadd_rn(red_d[1][0], red_d[1][1]), __dadd_rn(red_d[1][2], red_d[1][3]));
+    emin = min(min(red_e[0], red_e[1]), min(red_e[2], red_e[3]));
+  }
+  // exactness test (row-uniform): s2 < 2^(2 qmin + 52), qmin = max(E, 1) - 134
+  const int emn = (int)(emin >> 7) > 1 ? (int)(emin >> 7) : 1;
+  if (!(s2 < ldexp(1.0, 2 * (emn - 134) + 52))) {
+    long long* L1 = s_limbs[slot];
+    long long* L2 = s_limbs[slot] + kS1Limbs;
+    if (t < kS1Limbs + kS2Limbs) s_limbs[slot][t] = 0;
+    if constexpr (TPR == 256) __syncthreads();
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        exact_add<LAYER>(w[k] & 0xffffu, L1, L2);
+        exact_add<LAYER>(w[k] >> 16, L1, L2);
+      }
+    }
+    if constexpr (TPR == 256) __syncthreads();
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t == 0) {
+      s_exact[slot][0] = LAYER ? limbs_to_double(L1, kS1Limbs, -133) : 0.0;
+      s_exact[slot][1] = limbs_to_double(L2, kS2Limbs, -266);
+    }
+    if constexpr (TPR == 256) __syncthreads();
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    s1 = s_exact[slot][0];
+    s2 = s_exact[slot][1];
   }
   const double n = (double)cols;
   const double mean = __ddiv_rn(s1, n), ms = __ddiv_rn(s2, n);

@@ -290,6 +290,66 @@ def test_norm_quant_row(f, shape, kind):
         assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
 
 
+def _bits(values):
+    f32 = np.asarray(values, np.float32)
+    b = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f32(b), f32)
+    return b
+
+
+def _hard_rows(cols, seed):
+    """Rows whose sums no fp64 accumulation gets right, so the kernel takes its exact
+    path: 2^60 + 2^-20 - 2^60 (the exact mean is 2^-20 / cols), squares just above an
+    fp64 tie (2^80 + 2^27 + 2^-40), subnormals beside 1.0, and rows of random sign,
+    mantissa and exponent over 2^-67 .. 2^63; plus an all-zero row."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    r = np.zeros(cols, np.float32)
+    r[[0, 5, 9]] = [2.0 ** 60, 2.0 ** -20, -(2.0 ** 60)]
+    rows.append(_bits(r))
+    r = np.zeros(cols, np.float32)
+    r[[1, 2, 3, cols - 1]] = [2.0 ** 40, 2.0 ** 13, 2.0 ** 13, 2.0 ** -20]
+    rows.append(_bits(r))
+    r = np.ones(cols, np.float32)
+    r[::7] = 2.0 ** -133
+    r[3::11] = -(2.0 ** -126)
+    rows.append(_bits(r))
+    for _ in range(3):
+        e = rng.integers(60, 191, cols)
+        rows.append(((rng.integers(0, 2, cols) << 15) | (e << 7) | rng.integers(0, 128, cols)).astype(np.uint16))
+    rows.append(np.zeros(cols, np.uint16))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("cols", [1016, 4096, 7168])
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_quant_row_exact_sums(f, cols, kind):
+    """Rows whose statistics need the exact sums (the kernel's LDS integer path),
+    mixed with ordinary rows (the fp64 path): y, codes and scales bit-exact against
+    the oracle, whose sums are exact by construction. One wavefront per row (1016,
+    4096 columns) and one workgroup per row (7168)."""
+    import torch
+    layer = kind == "layer"
+    x = np.concatenate([_x((5, cols), 850 + cols), _hard_rows(cols, 860 + cols), _x((3, cols), 870 + cols)])
+    rows = x.shape[0]
+    g, b = _gamma(cols, 880 + cols, layer)
+    fmt, name = _natives(f)[0]
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda:0")
+    q, full = empty_u8((rows, cols), 256)
+    s = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+    i = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+    f.fp8_norm_quant_row(to_dev_bf16(x), to_dev_bf16(g), None if b is None else to_dev_bf16(b),
+                         f.NORM_LAYER if layer else f.NORM_RMS, 1e-5, fmt, EPS, y, q, s, i)
+    torch.cuda.synchronize()
+    check_guard(full, 256)
+    ry, rq, rs, ri = oracle.norm_quant_row(x, g, b, layer, 1e-5, name, EPS)
+    gy = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.nonzero(np.any(gy != ry, axis=1))[0]
+    assert bad.size == 0, (kind, cols, bad)
+    assert np.array_equal(u8(q), rq), (kind, cols)
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+
+
 def test_norm_quant_row_partial_outputs_and_errors(f):
     """y only, q only; bad shapes and arguments are refused."""
     import torch
