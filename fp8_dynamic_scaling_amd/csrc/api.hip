@@ -368,6 +368,8 @@ fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t rows, int64
 fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
                         fp8_mx_mode mode, double eps, uint8_t* q, uint8_t* e8m0, void* stream) {
   if (mode != FP8_MX_POW2_FLOOR && mode != FP8_MX_OCP) return FP8_ERR_INVALID_ARGUMENT;
+  // the E8M0 range: with eps >= 2^-100 every group's exponent lies in [-120, 115]
+  if (!(eps >= 0x1p-100)) return FP8_ERR_INVALID_ARGUMENT;
   fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, e8m0);
   if (st != FP8_OK || batch * rows * cols == 0) return st;
   if (cols % 32 != 0) return FP8_ERR_ALIGNMENT;

@@ -272,7 +272,9 @@ FP8DYN_API fp8_status fp8_quant_block(const uint16_t* x, int64_t batch, int64_t 
 /* MXFP8: 32 consecutive elements along cols share one E8M0 power-of-two
  * scale [P-AMD "AMD FP8 format in TorchAO", MXFP8; "Summary and Next Steps"].
  * e8m0[g] = 127 + log2(dequantize factor); q = encode(clamp(x * 2^k)).
- * cols % 32 == 0. x [batch][rows][cols] -> q same, e8m0 [batch][rows][cols/32]. */
+ * cols % 32 == 0. x [batch][rows][cols] -> q same, e8m0 [batch][rows][cols/32].
+ * eps >= 2^-100 (else FP8_ERR_INVALID_ARGUMENT): then every group's exponent,
+ * an all-zero group's included, fits E8M0 (bytes 12 .. 247). */
 FP8DYN_API fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
                                    fp8_format fmt, fp8_mx_mode mode, double eps, uint8_t* q,
                                    uint8_t* e8m0, void* stream);

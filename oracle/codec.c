@@ -133,7 +133,8 @@ double orc_scale_from_amax(int fmt, float amax, double eps, float* scale, float*
  *   mode 1: the OCP MX rule, dequantization exponent
  *           floor(log2(max(amax, eps))) - floor(log2(fmax)), values above
  *           fmax saturate.
- * E8M0 holds the dequantization exponent plus 127. */
+ * E8M0 holds the dequantization exponent plus 127. Callers keep eps >= 2^-100,
+ * so that the exponent of an all-zero group fits E8M0. */
 uint8_t orc_mx_scale_from_amax(int fmt, int mode, float amax, double eps, float* scale, float* inv) {
     int ex, kq; /* kq: quantize exponent, scale = 2^kq */
     if (mode == ORC_MX_POW2_FLOOR) {

@@ -72,8 +72,11 @@ def test_host_validation_without_gpu(f):
     assert lib.fp8_quant_col(None, 1, 0, 8, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.ERR_INVALID_ARGUMENT
     assert lib.fp8_quant_row(None, 1, 4, 0, f.E4M3_NATIVE, 1e-12, None, None, None, None) == f.ERR_INVALID_ARGUMENT
     assert lib.fp8_quant_tensor(None, 0, f.E4M3_NATIVE, 1e-12, None, None, None, None, 0, None) == f.ERR_INVALID_ARGUMENT
-    # MX needs cols % 32 == 0
+    # MX needs cols % 32 == 0, and eps >= 2^-100 (the E8M0 range)
     assert lib.fp8_quant_mx(FAKE, 1, 4, 48, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
+    for mode in (f.MX_POW2_FLOOR, f.MX_OCP):
+        assert lib.fp8_quant_mx(FAKE, 1, 4, 64, f.E4M3_NATIVE, mode, 2.0 ** -101, FAKE, FAKE, None) == \
+            f.ERR_INVALID_ARGUMENT
     # block geometry
     assert lib.fp8_quant_block(FAKE, 1, 4, 8, 2, 128, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None) == f.ERR_INVALID_ARGUMENT
     # tensorwise needs a workspace

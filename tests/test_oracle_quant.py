@@ -181,3 +181,20 @@ def test_thread_count_does_not_change_results():
         b = f(x, "e4m3fn", EPS, threads=8)
         for u, v in zip(a, b):
             assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mx_exponent_range_at_the_smallest_eps(fmt, mode):
+    """With eps = 2^-100, the smallest the library accepts, an all-zero group's E8M0
+    byte is 127 - floor(log2(fmax / eps)) (mode 0) or 127 + floor(log2 eps) -
+    floor(log2 fmax) (mode 1), inside [1, 254]; the largest bf16 amax stays inside too."""
+    import math
+    fmax = oracle.fp8_max(fmt)
+    x = np.zeros((1, 32), np.uint16)
+    _, e = oracle.quant_mx(x, fmt, mode, 2.0 ** -100)
+    want = 127 - math.floor(math.log2(fmax) + 100) if mode == 0 else 127 - 100 - math.floor(math.log2(fmax))
+    assert int(e[0, 0]) == want and 1 <= want <= 254
+    big = np.full((1, 32), 0x7F7F, np.uint16)  # largest finite bf16, about 2^128
+    _, e = oracle.quant_mx(big, fmt, mode, 2.0 ** -100)
+    assert 1 <= int(e[0, 0]) <= 254
