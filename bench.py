@@ -21,12 +21,16 @@ already resident in HBM:
                      grad-weight GEMM over the same offsets
   moe_block_mx       1x128 / 128x128 blockwise and MX quant, 16 experts, K 5120, N 8192,
                      and the blockwise and MX grouped GEMMs
-Every launch is bracketed by HIP events on the stream it runs on. The JSON line
-reports the fused-quantization throughput (algorithmic bytes of all quantization
-calls / their summed event time, 3 B per element + 8 B per fp32 scale group or 1 B
-per E8M0 group) as `value`, the grouped-GEMM throughput (2*M*N*K / event time) of
-the moe_grouped GEMM as `gemm_value`, per-call figures under `rows`, the roofline of
-the dominant kernel and the oracle's CPU throughput on a bounded sample.
+Every launch is bracketed by HIP events on the stream it runs on. The steps run
+twice: back to back (warm; the wall-clock timed region of ms_per_step) and with a
+512 MiB write before each call, outside its events (cold: nothing left in the L2 or
+the Infinity Cache). The JSON line reports, from the cold pass, the fused-quantization
+throughput (algorithmic bytes of all quantization calls / their summed event time,
+3 B per element + 8 B per fp32 scale group or 1 B per E8M0 group) as `value`, the
+grouped-GEMM throughput (2*M*N*K / event time) of the moe_grouped GEMM as
+`gemm_value`, per-call avg/median/p10/p90 (cold and warm) under `rows`, the roofline
+of the dominant kernel, the shader and memory clocks sampled during the run, and the
+oracle's CPU throughput on a bounded sample.
 """
 from __future__ import annotations
 
@@ -62,9 +66,15 @@ class Step:
     def add(self, name, kind, work, fn):
         self.calls.append((name, kind, float(work), fn))
 
-    def run(self, stream, record=None):
+    def run(self, stream, record=None, flush=None):
+        """One pass over the calls. record: per-call lists receiving (start, end) events.
+        flush: a device buffer written in full before each call, outside its events,
+        so that the call finds neither its inputs nor its outputs in the L2 or the
+        256 MB Infinity Cache (the cold measurement)."""
         torch = self.torch
         for i, (name, kind, work, fn) in enumerate(self.calls):
+            if flush is not None:
+                flush.fill_(i & 0x7f)
             if record is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -144,6 +154,20 @@ def build_step(f, torch, dev, wls, dev_of):
            lambda: f.fp8_scaled_mm_kpacked(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2, K))
     st.add("linear_rowwise.wgrad_bf16", "gemm16", 2.0 * M * N * K,
            lambda: f.fp8_wgrad_bf16(g2, x2, gw2))
+    # the grad-input GEMM at full precision (codes decoded to bf16, BF16 matrix
+    # cores), as fp8_linear_bwd runs it; and the two whole Linear calls, each the
+    # sum of its launches above (forward: quant_row_x + quant_row_w + gemm_fwd;
+    # backward: quant_row_gy_e5m2 + quant_col_w + gemm_dgrad_exact + wgrad_bf16)
+    gx2x = torch.empty((M, K), **bf)
+    st.add("linear_rowwise.gemm_dgrad_exact", "gemm8x_next", 2.0 * M * N * K,
+           lambda: f.fp8_scaled_mm_kpacked(qg, E5, qwt, E4, f.SCALE_ROW, ig, iwc, f.OUT_BF16, gx2x, K,
+                                           use_fast_accum=False))
+    lws_r = torch.empty(f.fp8_linear_ws_bytes(M, N, K, f.RECIPE_ROWWISE_BF16_WGRAD), **u8)
+    y2l, gx2l, gw2l = torch.empty((M, N), **bf), torch.empty((M, K), **bf), torch.empty((N, K), **bf)
+    st.add("linear_rowwise.linear_fwd", "latency", 2.0 * M * N * K,
+           lambda: f.fp8_linear_fwd(x2, wt2, f.RECIPE_ROWWISE_BF16_WGRAD, EPS, f.OUT_BF16, y2l, lws_r))
+    st.add("linear_rowwise.linear_bwd", "latency", 4.0 * M * N * K,
+           lambda: f.fp8_linear_bwd(g2, x2, wt2, f.RECIPE_ROWWISE_BF16_WGRAD, EPS, gx2l, gw2l, lws_r))
 
     # ---- the norm that produces X, fused with its rowwise quantization,
     # against the unfused pair (outside the aggregates) ----
@@ -177,6 +201,8 @@ def build_step(f, torch, dev, wls, dev_of):
            2 * (M * N + M * K) + 2 * M * N + M * K + 16,
            lambda: f.fp8_quant_dual(g2, x2, E5, E4, EPS, gqb, gqTb, dsc[0], dsc[1], xqTb, dsc[2], dsc[3], dws))
     st.add("linear_tensorwise_fp8_bwd.gemm_wgrad_fp8", "gemm8_next", 2.0 * M * N * K,
+           lambda: f.fp8_scaled_mm(gqTb, E5, xqTb, E4, f.SCALE_TENSOR, dsc[1], dsc[3], f.OUT_BF16, gwf))
+    st.add("linear_tensorwise_fp8_bwd.gemm_wgrad_fp8_exact", "gemm8x_next", 2.0 * M * N * K,
            lambda: f.fp8_scaled_mm(gqTb, E5, xqTb, E4, f.SCALE_TENSOR, dsc[1], dsc[3], f.OUT_BF16, gwf,
                                    use_fast_accum=False))
     st.add("linear_tensorwise_fp8_bwd.linear_bwd", "latency", 4.0 * M * N * K,
@@ -227,6 +253,9 @@ def build_step(f, torch, dev, wls, dev_of):
            lambda: f.fp8_quant_row(go4, E5, EPS, qgo4, sgo4, igo4))
     st.add("moe_backward.grouped_dgrad", "gemm8_next", 2.0 * Mt * N4 * K4,
            lambda: f.fp8_grouped_mm(qgo4, E5, qt3, E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16, gx4))
+    st.add("moe_backward.grouped_dgrad_exact", "gemm8x_next", 2.0 * Mt * N4 * K4,
+           lambda: f.fp8_grouped_mm(qgo4, E5, qt3, E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16, gx4,
+                                    use_fast_accum=False))
     st.add("moe_backward.grouped_wgrad_bf16", "gemm16_next", 2.0 * Mt * N4 * K4,
            lambda: f.fp8_grouped_wgrad_bf16(go4, a4, off4, gw4))
 
@@ -405,22 +434,45 @@ def main():
         st.run(stream)
     torch.cuda.synchronize()
     log("warmup done")
-    rec = [[] for _ in st.calls]
+    clocks = ClockSampler()
+    clocks.start()
+    # warm: the steps back to back, as a training step runs them (the timed region)
+    warm = [[] for _ in st.calls]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        st.run(stream, rec)
+        st.run(stream, warm)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
+    log(f"warm steps done ({ms_per_step:.2f} ms per step)")
+    # cold: the same steps with a 512 MiB write before every call (outside its
+    # events), twice the 256 MB Infinity Cache, so no call reads data an earlier
+    # call left in the caches; the reported figures are these
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = [[] for _ in st.calls]
+    for _ in range(args.steps):
+        st.run(stream, cold, flush=flush)
+    torch.cuda.synchronize()
+    del flush
+    clocks.stop()
+    log("cold steps done")
+
+    def times(rec_i):
+        return np.array([e0.elapsed_time(e1) for e0, e1 in rec_i]) * 1e-3  # seconds
 
     rows = {}
     q_bytes = q_time = 0.0
     dom = None
     for i, (name, kind, work, _) in enumerate(st.calls):
-        ts = np.array([e0.elapsed_time(e1) for e0, e1 in rec[i]]) * 1e-3  # seconds
+        ts, tw = times(cold[i]), times(warm[i])
         avg = float(ts.mean())
-        r = {"avg_us": round(avg * 1e6, 2), "median_us": round(float(np.median(ts)) * 1e6, 2)}
+        r = {"avg_us": round(avg * 1e6, 2), "median_us": round(float(np.median(ts)) * 1e6, 2),
+             "p10_us": round(float(np.percentile(ts, 10)) * 1e6, 2),
+             "p90_us": round(float(np.percentile(ts, 90)) * 1e6, 2),
+             "warm_avg_us": round(float(tw.mean()) * 1e6, 2),
+             "warm_p10_us": round(float(np.percentile(tw, 10)) * 1e6, 2),
+             "warm_p90_us": round(float(np.percentile(tw, 90)) * 1e6, 2)}
         if kind == "quant":
             r.update(gbs=round(work / avg / 1e9, 1), frac_hbm=round(work / avg / 1e9 / HBM_PEAK_GBS, 4),
                      bytes=int(work))
@@ -429,10 +481,11 @@ def main():
         elif kind == "quant_next":
             r.update(gbs=round(work / avg / 1e9, 1), frac_hbm=round(work / avg / 1e9 / HBM_PEAK_GBS, 4),
                      bytes=int(work))
-        elif kind in ("gemm8", "gemm16", "gemm8_next", "gemm16_next"):
-            peak = BF16_PEAK_TFLOPS if kind.startswith("gemm16") else FP8_PEAK_TFLOPS
+        elif kind in ("gemm8", "gemm16", "gemm8_next", "gemm16_next", "gemm8x_next"):
+            # full-precision FP8 GEMMs (gemm8x) run on the BF16 matrix cores
+            peak = BF16_PEAK_TFLOPS if kind.startswith(("gemm16", "gemm8x")) else FP8_PEAK_TFLOPS
             r.update(tflops=round(work / avg / 1e12, 1), frac_mfma=round(work / avg / 1e12 / peak, 4),
-                     flops=work)
+                     flops=work, peak_tflops=peak)
         rows[name] = r
         if kind in ("quant", "gemm8", "gemm16") and (dom is None or avg > dom[2]):
             dom = (name, kind, avg, work)
@@ -471,12 +524,98 @@ def main():
                                "traffic": traffic}
         out["roofline"]["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         out["roofline"]["sources"] = sources_digest(kind)
+    out["timing"] = ("per row: HIP events on the launch stream; avg/median/p10/p90 with a 512 MiB write "
+                     "between calls (cold; value, gemm_value and roofline use these), warm_* back to back")
+    out["clocks"] = clocks.summary()
     out["rows"] = rows
     out["inputs_sha256"] = input_digests(wls)
     if not args.no_cpu_baseline and "moe_grouped" in wls:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(wls, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+class ClockSampler:
+    """Samples the GPU's shader and memory clocks while the timed steps run: the
+    current DPM level of card*/device/pp_dpm_sclk and pp_dpm_mclk (the line marked
+    '*'), or rocm-smi's JSON where sysfs does not show them."""
+
+    def __init__(self, period_s=0.02):
+        import glob
+        import threading
+        self.period = period_s
+        self.samples = {"sclk": [], "mclk": []}
+        self.files = {}
+        for k in ("sclk", "mclk"):
+            fs = sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{k}"))
+            if fs:
+                self.files[k] = fs
+        self.source = "sysfs pp_dpm_*" if self.files else "rocm-smi --showclocks"
+        if not self.files:
+            self.period = 0.25
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._loop, daemon=True)
+
+    @staticmethod
+    def _mhz(text):
+        import re
+        m = re.search(r"(\d+)\s*[Mm][Hh]z", text)
+        return int(m.group(1)) if m else None
+
+    def _read(self):
+        if self.files:
+            for k, fs in self.files.items():
+                for fn in fs:
+                    try:
+                        with open(fn) as fh:
+                            for line in fh:
+                                if "*" in line:
+                                    v = self._mhz(line)
+                                    if v:
+                                        self.samples[k].append(v)
+                    except OSError:
+                        pass
+            return
+        import subprocess
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=5)
+            d = json.loads(r.stdout) if r.returncode == 0 else {}
+        except (OSError, ValueError, subprocess.TimeoutExpired):
+            return
+        for card in d.values():
+            if not isinstance(card, dict):
+                continue
+            for key, val in card.items():
+                kl = key.lower()
+                v = self._mhz(str(val)) if isinstance(val, str) else None
+                if v and kl.startswith("sclk"):
+                    self.samples["sclk"].append(v)
+                elif v and kl.startswith("mclk"):
+                    self.samples["mclk"].append(v)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            self._read()
+            self._stop.wait(self.period)
+
+    def start(self):
+        self._t.start()
+
+    def stop(self):
+        self._stop.set()
+        self._t.join(timeout=10)
+
+    def summary(self):
+        import numpy as np
+        out = {"source": self.source}
+        for k, v in self.samples.items():
+            if v:
+                a = np.array(v)
+                out[k + "_mhz"] = {"min": int(a.min()), "median": int(np.median(a)), "max": int(a.max()),
+                                   "samples": int(a.size)}
+            else:
+                out[k + "_mhz"] = None
+        return out
 
 
 def build_step_subset(f, torch, dev, wls, dev_of):

@@ -26,6 +26,11 @@ COMMON = [
 ]
 
 
+# Sources whose arithmetic is defined operation by operation (the quantizers and
+# the fused normalization): no multiply-add contraction, so a * b + c rounds twice.
+NO_CONTRACT = {"quant.hip": ["-ffp-contract=off"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
@@ -37,7 +42,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + COMMON + NO_CONTRACT.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -1044,18 +1044,25 @@ hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps,
 // write and the next layer's amax pass become one memory pass). One
 // 256-thread workgroup per row; the row stays in registers from the load to
 // the FP8 store, so x is read once and y (bf16) is written only if asked.
-//  1. s1 = sum x, s2 = sum x^2: the exact sums rounded once to fp64. The row
-//     is summed in fp64 (s2 with fused multiply-adds: x * x is exact). That
-//     is exact in any order when every term is a multiple of one unit u and
-//     the sum of the |terms| stays below 2^53 u: each partial sum is then an
-//     fp64 value. With u = 2^(2 qmin) for the squares (x = M 2^q, M < 256,
-//     qmin the row's smallest q) the computed s2 < 2^52 u proves it for s2,
-//     and for s1 too (sum |x| <= sqrt(n s2) < 2^(33 + qmin) for n <= 2^14).
-//     A row that fails the test sums again exactly: integer terms
-//     M 2^(q + 133) and M^2 2^(2 q + 266) added with LDS atomics into limbs of
-//     32 bits held in 64-bit words, then rounded once to fp64;
+//  1. s1 = sum x, s2 = sum x^2: the exact sums rounded once to fp64. Only
+//     mean32 and rstd32 (step 2) reach the output, so the kernel sums the row
+//     in fp64 (s2 with fused multiply-adds: x * x is exact) and bounds the
+//     error: no term passes more than 72 additions (64 in a lane, 6 shuffle
+//     levels, 2 across waves), so |error| <= 72 * 2^-53 * sum|terms|, below
+//     2^-46 s2 for s2 and 2^-45 sqrt(n s2) for s1 (sum|x| <= sqrt(n s2)).
+//     (LayerNorm: 0 when s1 is proven exact, below). Step 2 is monotone in
+//     s2 (and in s1, in mean^2), so running it at both ends of those
+//     intervals brackets the exact result: when both ends give the same
+//     mean32 and rstd32, so does the exact sum. A row where they differ (a
+//     rounding boundary inside the interval, about 2^-20 of random rows, or
+//     sums that cancel) is summed again exactly: integer terms
+//     M 2^(q + 133) and M^2 2^(2 q + 266) of x = +-M 2^q added with LDS atomics
+//     into limbs of 32 bits held in 64-bit words, then rounded once to fp64;
 //  2. mean, mean square, var (LayerNorm) and rstd = 1 / sqrt(var + norm_eps):
-//     fp64 IEEE operations (no contraction);
+//     fp64 IEEE operations (no contraction: this file is built with
+//     -ffp-contract=off, because hip's __fmul_rn / __fadd_rn are plain
+//     operators that the compiler would otherwise fuse, and a fused
+//     t * gamma + beta rounds once where the definition rounds twice);
 //  3. y = ((x - mean32) * rstd32) * gamma + beta (LayerNorm) or
 //     (x * rstd32) * gamma (RMSNorm), fp32 IEEE operations, stored as bf16
 //     (RNE);
@@ -1153,7 +1160,9 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
   const uint16_t* xr = x + row * cols;
   uint4 v[J];
   double s1 = 0.0, s2 = 0.0;
-  uint32_t emin = 0x7f80u;  // smallest exponent field of a nonzero value (the field of v - 1: never larger)
+  // LayerNorm: the smallest exponent field over the row's nonzero values (the
+  // field of v - 1, never above the value's own) for the exactness test of s1
+  uint32_t emin = 0x7f80u;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int64_t c = 8 * (t + TPR * j);
@@ -1169,17 +1178,20 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
       // x * x is exact in fp64, so the fused multiply-add rounds exactly as
       // s2 + x * x does, with one fp64 operation instead of two
       s2 = __fma_rn(hi, hi, __fma_rn(lo, lo, s2));
-      const uint32_t a = w[k] & 0x7fffu, b = (w[k] >> 16) & 0x7fffu;
-      emin = min(emin, min((a - 1u) & 0x7f80u, (b - 1u) & 0x7f80u));
+      if constexpr (LAYER) {
+        const uint32_t a = w[k] & 0x7fffu, b = (w[k] >> 16) & 0x7fffu;
+        emin = min(emin, min((a - 1u) & 0x7f80u, (b - 1u) & 0x7f80u));
+      }
     }
   }
-  // row sums (fp64) and the smallest exponent: the wavefront, then (256
-  // threads per row) the 4 waves
+  // row sums (fp64): the wavefront, then (256 threads per row) the 4 waves
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    if constexpr (LAYER) s1 = __dadd_rn(s1, __shfl_xor(s1, o, 64));
+    if constexpr (LAYER) {
+      s1 = __dadd_rn(s1, __shfl_xor(s1, o, 64));
+      emin = min(emin, (uint32_t)__shfl_xor((int)emin, o, 64));
+    }
     s2 = __dadd_rn(s2, __shfl_xor(s2, o, 64));
-    emin = min(emin, (uint32_t)__shfl_xor((int)emin, o, 64));
   }
   if constexpr (TPR == 256) {
     if ((tid & 63) == 0) {
@@ -1192,9 +1204,42 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
     s2 = __dadd_rn(__dadd_rn(red_d[1][0], red_d[1][1]), __dadd_rn(red_d[1][2], red_d[1][3]));
     emin = min(min(red_e[0], red_e[1]), min(red_e[2], red_e[3]));
   }
-  // exactness test (row-uniform): s2 < 2^(2 qmin + 52), qmin = max(E, 1) - 134
-  const int emn = (int)(emin >> 7) > 1 ? (int)(emin >> 7) : 1;
-  if (!(s2 < ldexp(1.0, 2 * (emn - 134) + 52))) {
+  const double n = (double)cols;
+  float mean32 = 0.0f, rstd32;
+  // step 2 at the ends of the error intervals (row-uniform decision)
+  bool settled;
+  {
+    const double e2 = __dmul_rn(s2, 0x1p-46);
+    const double ms_lo = __ddiv_rn(__dsub_rn(s2, e2), n), ms_hi = __ddiv_rn(__dadd_rn(s2, e2), n);
+    double v_lo = ms_lo, v_hi = ms_hi;
+    if constexpr (LAYER) {
+      // sum|x| <= sqrt(n s2); every term is a multiple of 2^qmin, qmin =
+      // max(E, 1) - 134 over the nonzero values, so s1 is exact when that
+      // bound stays below 2^(qmin + 53). The mean is then exact too whenever n
+      // is a power of two, and often sits on an fp32 rounding midpoint, where
+      // any interval around it would leave the rounding open
+      const double bnd = __dmul_rn(__dsqrt_rn(__dmul_rn(n, __dadd_rn(s2, e2))), 1.0 + 0x1p-40);
+      const int qmin = ((int)(emin >> 7) > 1 ? (int)(emin >> 7) : 1) - 134;
+      const double e1 = bnd < ldexp(1.0, qmin + 53) ? 0.0 : __dmul_rn(bnd, 0x1p-45);
+      const double m_lo = __ddiv_rn(__dsub_rn(s1, e1), n), m_hi = __ddiv_rn(__dadd_rn(s1, e1), n);
+      const float m32 = __double2float_rn(m_lo);
+      // the range of |mean| over the interval, then of var = ms - mean^2
+      const double f_lo = fabs(m_lo), f_hi = fabs(m_hi);
+      const double a_lo = m_lo <= 0.0 && m_hi >= 0.0 ? 0.0 : (f_lo < f_hi ? f_lo : f_hi);
+      const double a_hi = f_lo > f_hi ? f_lo : f_hi;
+      v_lo = __dsub_rn(ms_lo, __dmul_rn(a_hi, a_hi));
+      v_hi = __dsub_rn(ms_hi, __dmul_rn(a_lo, a_lo));
+      settled = m32 == __double2float_rn(m_hi);
+      mean32 = m32;
+    } else {
+      settled = true;
+    }
+    const float r_small = __double2float_rn(__ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(v_hi, norm_eps))));
+    const float r_large = __double2float_rn(__ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(v_lo, norm_eps))));
+    settled = settled && r_small == r_large;  // false for NaN (var + norm_eps < 0)
+    rstd32 = r_small;
+  }
+  if (!settled) {
     long long* L1 = s_limbs[slot];
     long long* L2 = s_limbs[slot] + kS1Limbs;
     if (t < kS1Limbs + kS2Limbs) s_limbs[slot][t] = 0;
@@ -1219,12 +1264,12 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
     else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     s1 = s_exact[slot][0];
     s2 = s_exact[slot][1];
+    const double mean = __ddiv_rn(s1, n), ms = __ddiv_rn(s2, n);
+    const double var = LAYER ? __dsub_rn(ms, __dmul_rn(mean, mean)) : ms;
+    const double rstd = __ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(var, norm_eps)));
+    mean32 = __double2float_rn(mean);
+    rstd32 = __double2float_rn(rstd);
   }
-  const double n = (double)cols;
-  const double mean = __ddiv_rn(s1, n), ms = __ddiv_rn(s2, n);
-  const double var = LAYER ? __dsub_rn(ms, __dmul_rn(mean, mean)) : ms;
-  const double rstd = __ddiv_rn(1.0, __dsqrt_rn(__dadd_rn(var, norm_eps)));
-  const float mean32 = __double2float_rn(mean), rstd32 = __double2float_rn(rstd);
   // normalize, keep as bf16 in registers (and store to y)
   float m = 0.0f;
 #pragma unroll

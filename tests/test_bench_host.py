@@ -77,3 +77,16 @@ def test_sources_digest_follows_the_kernel_files():
         with open(os.path.join(ROOT, "fp8_dynamic_scaling_amd", "csrc", fn), "rb") as fh:
             h.update(fh.read())
     assert bench.sources_digest("quant") == h.hexdigest()[:16]
+
+
+def test_clock_sampler_parses_dpm_levels():
+    """The current DPM level line ('*') of pp_dpm_sclk / pp_dpm_mclk, and rocm-smi's
+    '(2100Mhz)' strings, give MHz; no samples give None."""
+    assert bench.ClockSampler._mhz("2: 2400Mhz *") == 2400
+    assert bench.ClockSampler._mhz("(1900Mhz)") == 1900
+    assert bench.ClockSampler._mhz("level 3") is None
+    c = bench.ClockSampler()
+    c.samples = {"sclk": [2000, 2100, 2400], "mclk": []}
+    s = c.summary()
+    assert s["sclk_mhz"] == {"min": 2000, "median": 2100, "max": 2400, "samples": 3}
+    assert s["mclk_mhz"] is None

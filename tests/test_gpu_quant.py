@@ -297,13 +297,36 @@ def _bits(values):
     return b
 
 
+def _rstd_boundary_row(cols, norm_eps):
+    """A row whose RMSNorm rstd lies within 2^-60 of an fp32 rounding midpoint (3/4 +
+    2^-25): bf16 values chosen greedily so their squares sum to cols * (1/m^2 - eps),
+    each the largest bf16 not above the square root of what is left."""
+    import math
+    from fractions import Fraction
+    m = Fraction(3, 4) + Fraction(1, 2 ** 25)
+    r = cols * (1 / (m * m) - Fraction(norm_eps))
+    vals = []
+    for _ in range(12):
+        if r <= 0:
+            break
+        x = float((np.float32(math.sqrt(float(r))).view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32))
+        if x == 0.0:
+            break
+        vals.append(x)
+        r -= Fraction(x) ** 2
+    row = np.zeros(cols, np.float32)
+    row[:len(vals)] = vals
+    return _bits(row)
+
+
 def _hard_rows(cols, seed):
-    """Rows whose sums no fp64 accumulation gets right, so the kernel takes its exact
-    path: 2^60 + 2^-20 - 2^60 (the exact mean is 2^-20 / cols), squares just above an
-    fp64 tie (2^80 + 2^27 + 2^-40), subnormals beside 1.0, and rows of random sign,
-    mantissa and exponent over 2^-67 .. 2^63; plus an all-zero row."""
+    """Rows the kernel's fp64 sums cannot settle, so it takes its exact path:
+    2^60 + 2^-20 - 2^60 (the exact mean is 2^-20 / cols), squares just above an fp64
+    tie (2^80 + 2^27 + 2^-40), subnormals beside 1.0, rows of random sign, mantissa
+    and exponent over 2^-67 .. 2^63, and a row whose RMSNorm rstd sits on an fp32
+    rounding midpoint; plus an all-zero row."""
     rng = np.random.default_rng(seed)
-    rows = []
+    rows = [_rstd_boundary_row(cols, 1e-5)]
     r = np.zeros(cols, np.float32)
     r[[0, 5, 9]] = [2.0 ** 60, 2.0 ** -20, -(2.0 ** 60)]
     rows.append(_bits(r))

@@ -106,3 +106,27 @@ def test_no_mfma_destination_overlaps_its_sources(src, tmp_path):
     assert not bad, bad[:5]
     raw = mfma_raw_hazards(asm)
     assert not raw, raw[:5]
+
+
+def test_norm_kernels_fuse_no_fp32_multiply_add(tmp_path):
+    """The fused normalization's fp32 steps round one by one, as the definition's
+    (x - mean) * rstd * gamma + beta does: built with the library's flags for its file,
+    no k_norm_quant_row instantiation may contain an fp32 fma (hip's __fmul_rn and
+    __fadd_rn are plain operators that contraction would fuse)."""
+    src = "quant.hip"
+    path = os.path.join(hb.HERE, "csrc", src)
+    out = tmp_path / (src + ".s")
+    cmd = [hb.HIPCC] + hb.COMMON + hb.NO_CONTRACT.get(src, []) + ["--cuda-device-only", "-S", path, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    cur, seen, bad = None, 0, []
+    for line in out.read_text().splitlines():
+        m = re.match(r"^(_Z\S*k_norm_quant_row\S*):", line)
+        if m:
+            cur, seen = m.group(1), seen + 1
+            continue
+        if cur and line.strip().startswith(".Lfunc_end"):
+            cur = None
+        if cur and re.search(r"\bv_(pk_)?fmac?_f32\b", line):
+            bad.append((cur, line.strip()))
+    assert seen >= 4 and not bad, bad[:3]
