@@ -219,11 +219,13 @@ __global__ __launch_bounds__(256, 4) void k_quant_col(const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l8 = tid & 7, rg = tid >> 3;
+  // strip fastest: the workgroups of one row chunk run side by side and
+  // together read whole rows, rather than 128-byte pieces of rows far apart
   int64_t blk = blockIdx.x;
-  const int64_t rc = blk % rchunks;
-  blk /= rchunks;
   const int64_t strip = blk % strips;
-  const int64_t b = blk / strips;
+  blk /= strips;
+  const int64_t rc = blk % rchunks;
+  const int64_t b = blk / rchunks;
   const int64_t c0 = strip * 64 + l8 * 8;
   const bool cok = c0 < C;
   const int64_t r_beg = rc * rows_per_blk;
