@@ -11,9 +11,9 @@
 // Design:
 //  - Tensorwise, rowwise and MX scales: k_gemm_fp8_pp, an 8-wave ping-pong
 //    kernel (the header comment there has the details).
-//  - 128-blockwise scales: k_gemm_fp8_block, 8 waves of 128 x 64 with
-//    v_mfma_scale_f32_16x16x128_f8f6f4: each 128-deep product goes into a
-//    zeroed accumulator and is added to the fp32 result scaled by
+//  - 128-blockwise scales: k_gemm_fp8_block, the same ping-pong over 128-deep
+//    K blocks with v_mfma_scale_f32_16x16x128_f8f6f4: each 128-deep product
+//    goes into a zeroed accumulator and is added to the fp32 result scaled by
 //    inv_a[m][kb] * inv_b[nb][kb].
 //  - Both: 256 x 256 output tiles walked persistently (one workgroup per CU,
 //    XCD-aware order; see gemm_common.hpp); operands go from HBM straight into
@@ -419,27 +419,68 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
 }
 
 
-template <bool AE5, bool BE5, bool OF32>
+// ---------------------------------------------------------------------------
+// Kernel for 128-blockwise scales. Every 128-deep partial product carries its
+// own scale inv_a[m][kb] * inv_b[nb][kb], so partial sums cannot stay in the
+// matrix-core accumulator: each 128-deep product of a 32 x 32 block is two
+// v_mfma_scale_f32_32x32x64_f8f6f4 into a fresh register, and an fp32 FMA
+// per output adds it, scaled, into the result.
+//  - Transposed products: the instruction's rows are B rows (n), its columns
+//    A rows (m), so a lane holds one m and 16 n of each block. The A-block
+//    scale is then one value per lane and block, and the B-block scale one
+//    per wave (its 64 columns lie in one 128-column block): a single factor
+//    per lane scales a whole product. Measured on MI355X, this instruction
+//    sustains about 94% of the nominal FP8 rate back to back; the 16 x 16 x
+//    128 one, about 75%.
+//  - 256 x 256 tile, 8 waves of 128 m x 64 n, two per SIMD, both computing:
+//    while one wave runs the FMAs of a product or waits on LDS, the other
+//    keeps the matrix core busy. (A ping-pong split, one wave computing while
+//    the other reads, measured slower here: the FMAs then stall the only
+//    wave that could feed the matrix core, and every phase boundary idles
+//    it.) Per K block a wave runs 8 products (4 row blocks x 2 column
+//    blocks); the FMAs of product n follow the first instruction of product
+//    n + 1, and each row block's A fragments are read while the previous row
+//    block's products run.
+//  - LDS: a ring of two 128-deep K blocks, each 256 rows of A then 256 rows
+//    of B, 128 bytes per row, so every DMA lane group fetches whole cache
+//    lines; 16-byte chunks XOR-swizzled by (row / 2) % 8: two rows share a
+//    line of the 64 four-byte banks, and a 16-lane group of a 16-byte read
+//    (16 consecutive rows) then hits 16 distinct bank quads. Lane l's 32-byte
+//    operand for K half kh of a block is chunks 4 kh + g and 4 kh + 2 + g of
+//    row l % 32, g = l / 32 (the instruction's measured operand layout).
+//  - Two barriers per K block kb. After the first (kb has landed, every wave
+//    is done with kb - 1), waves 0-3 load A of kb + 1 into kb - 1's slot.
+//    After the second (every wave holds its B fragments of kb), waves 4-7
+//    load B of kb + 2 into the B half of kb's slot: B, mostly fetched from
+//    HBM (a B tile serves few row tiles), gets about 1.75 K blocks to land,
+//    A (row tiles are shared by the whole tile row, mostly L2 hits) one.
+//  - Scales (SC4: K % 512 == 0 and 16-byte aligned scale arrays): one
+//    16-byte load per row brings the A-block scales of four K blocks, and one
+//    per column block those of B. Otherwise one 4-byte load per row per K
+//    block; that form touches a cache line per lane for 4 bytes.
+template <bool AE5, bool BE5, bool OF32, bool SC4>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 128;
-  constexpr int NW = 8, WN = 4;
-  constexpr int TM = 128, TN = 64, MI = TM / 16, NI = TN / 16;
-  constexpr int SA_BYTES = BM * BK, STAGE = (BM + BN) * BK;
-  constexpr int D = STAGE / 1024 / NW;  // wave-wide 1 KB loads per wave per stage
+  constexpr int TM = 128, TN = 64;
+  constexpr int SA_BYTES = BM * BK, STAGE = 2 * SA_BYTES;
+  constexpr int D = SA_BYTES / 1024 / 4;  // wave-wide 1 KB loads per wave per K block
+  typedef float v16f __attribute__((ext_vector_type(16)));
   static_assert(D == 8, "stage split");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) float s_sa[2][BM];
-  // each wave's B-block scale of the stage (64 copies: one wave-wide DMA)
-  __shared__ __attribute__((aligned(16))) float s_sb[2][NW][64];
+  // A-block scales of four K blocks: SC4 [slot][row][kb % 4], else
+  // [slot][kb % 4][row]; slot (kb / 4) % 2
+  __shared__ __attribute__((aligned(16))) float s_sa[2][4 * BM];
+  // B-block scales of four K blocks per 64-column block: [slot][wn][kb % 4]
+  __shared__ __attribute__((aligned(16))) float s_sb[2][4][4];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int64_t s_pref[kMaxExperts + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int grp = wave >> 2, wn = wave & 3;
+  const int lrow = lane & 31, g = lane >> 5;
   const int64_t N = p.N, K = p.K;
   const int64_t nt = (N + BN - 1) / BN;
   const int64_t nk = K / BK;
@@ -450,26 +491,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
   int64_t t_begin, t_end, t_step;
   xcd_range(total, t_begin, t_end, t_step);
 
-  // wave w loads 1 KB pieces 8w .. 8w + 7 of a stage: 0-31 are A (8 rows of
-  // 128 bytes each), 32-63 are B; lane -> row lane / 8, chunk lane % 8
-  const bool loads_a = wave < 4;
-  const int q0 = (wave & 3) * D;
-  const int ld_row = lane >> 3, ld_pch = lane & 7;
-
-  // fragment read offsets within a stage (16-row block i of A, j of B)
-  uint32_t fa_lo[MI], fa_hi[MI], fb_lo[NI], fb_hi[NI];
+  // fragment byte offsets within a slot, lane part: row lrow, chunk
+  // (4 kh + 2 s + g) ^ ((row / 2) % 8) for K half kh, low (s = 0) or high 16
+  // bytes; row block i of A starts 16384 grp + 4096 i further, column block
+  // j of B SA_BYTES + 8192 wn + 4096 j further
+  uint32_t fo[2][2];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int r = wm * TM + 16 * i + lr;
-    fa_lo[i] = (uint32_t)(r * BK + 16 * (lg ^ (r & 7)));
-    fa_hi[i] = (uint32_t)(r * BK + 16 * ((lg + 4) ^ (r & 7)));
-  }
+  for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int r = wn * TN + 16 * j + lr;
-    fb_lo[j] = (uint32_t)(SA_BYTES + r * BK + 16 * (lg ^ (r & 7)));
-    fb_hi[j] = (uint32_t)(SA_BYTES + r * BK + 16 * ((lg + 4) ^ (r & 7)));
-  }
+    for (int s = 0; s < 2; ++s)
+      fo[kh][s] = (uint32_t)(lrow * BK) + 16u * ((uint32_t)(4 * kh + 2 * s + g) ^ (uint32_t)((lrow >> 1) & 7));
+  const uint32_t a_part = (uint32_t)(grp * TM * BK);
+  const uint32_t b_part = (uint32_t)(SA_BYTES + wn * TN * BK);
 
   for (int64_t t = t_begin; t < t_end; t += t_step) {
     TileInfo ti;
@@ -481,160 +514,216 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
     const int32_t K32 = (int32_t)K;
     const int32_t a_rows = (int32_t)(ti.m_end - ti.m0);
     const int32_t b_rows = (int32_t)(N - ti.n0 < BN ? N - ti.n0 : BN);
-    const uint8_t* base = loads_a ? p.a + ti.m0 * K : p.b + ((int64_t)ti.e * N + ti.n0) * K;
-    const int32_t rows = loads_a ? a_rows : b_rows;
-    uint32_t off[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int r = 8 * (q0 + d) + ld_row;
-      const int c = ld_pch ^ (r & 7);
-      const int32_t rr = r < rows ? r : rows - 1;  // rows past the expert / N load a valid row
-      off[d] = (uint32_t)(rr * K32 + 16 * c);
-    }
-    const uint32_t opnd_lds = loads_a ? 0u : (uint32_t)SA_BYTES;
-    // A-block scales: wave w (and its twin w + 4, same bytes) loads rows
-    // 64 (w % 4) .. + 63 of inv_a[m][kb]
-    const float* sa_base = reinterpret_cast<const float*>(p.sa) + ti.m0 * nk;
-    int32_t sr = 64 * (wave & 3) + lane;
-    sr = sr < a_rows ? sr : a_rows - 1;
-    const uint32_t sa_off = (uint32_t)(sr * (int32_t)nk) * 4u;
-    // this wave's B-block scales: inv_b[e][nb][kb], nb of its 64 columns
-    const int64_t nb = (ti.n0 + wn * TN) / 128;
-    const float* sb_row = reinterpret_cast<const float*>(p.sb) + ((int64_t)ti.e * nbt + (nb < nbt ? nb : nbt - 1)) * nk;
-    const uint8_t* sb_bytes = reinterpret_cast<const uint8_t*>(sb_row);
+    // waves 0-3 load A rows 64 wn .. 64 wn + 63 of the tile, waves 4-7 those
+    // B rows; rows past the expert (or N) load a valid row, never stored
+    const uint8_t* base = grp == 0 ? p.a + ti.m0 * K : p.b + ((int64_t)ti.e * N + ti.n0) * K;
+    const int32_t rows = grp == 0 ? a_rows : b_rows;
+    const uint32_t part = (grp == 0 ? 0u : (uint32_t)SA_BYTES) + (uint32_t)(wn * D * 1024);
+    // scales: waves 0-3 those of A rows 64 wn + lane, waves 4-7 (one lane)
+    // those of B column block (n0 + 64 wn) / 128
+    const uint8_t* sa_bytes = reinterpret_cast<const uint8_t*>(reinterpret_cast<const float*>(p.sa) + ti.m0 * nk);
+    int64_t nb = (ti.n0 + wn * TN) / 128;
+    nb = nb < nbt ? nb : nbt - 1;
+    const uint8_t* sb_bytes =
+        reinterpret_cast<const uint8_t*>(reinterpret_cast<const float*>(p.sb) + ((int64_t)ti.e * nbt + nb) * nk);
 
-    // this wave's operand pieces of stage k (A for waves 0-3, B for 4-7)
-    auto issue_ops = [&](int64_t k) {
-      const uint32_t slot = lds0 + (uint32_t)((k & 1) * STAGE) + opnd_lds + (uint32_t)(q0 * 1024);
-      const uint8_t* bk = base + k * BK;
+    // K block kb starts a scale load: SC4 one in four, else every one
+    auto has_scale = [&](int64_t kb) { return SC4 ? (kb & 3) == 0 : true; };
+    // the offsets are formed per call from opaque inputs: held across the
+    // K loop they would take 16 registers the loop does not have
+    auto issue_ops = [&](int64_t kb) {
+      const uint32_t slot = lds0 + (uint32_t)((kb & 1) * STAGE) + part;
+      const uint8_t* bk = base + kb * BK;
+      // lane: row 8 d + lane / 8 of the wave's 64, LDS chunk lane % 8, which
+      // holds chunk (lane % 8) ^ ((row / 2) % 8) of the row; (8 d + lane / 8)
+      // / 2 % 8 is lane / 16 + 4 (d % 2)
+      uint32_t l = (uint32_t)lane;
+      asm volatile("" : "+v"(l));
+      const int32_t r0 = 64 * wn + (int32_t)(l >> 3);
+      const uint32_t cb0 = 16u * ((l & 7u) ^ (l >> 4));
+      const uint32_t cb1 = 16u * ((l & 7u) ^ ((l >> 4) + 4u));
 #pragma unroll
-      for (int d = 0; d < D; ++d) dma16(bk, off[d], slot + (uint32_t)(d * 1024));
-    };
-    // the A-block scales and this wave's B-block scale of stage k
-    auto issue_scales = [&](int64_t k) {
-      const uint32_t sl = lds_addr(&s_sa[k & 1][64 * (wave & 3)]);
-      asm volatile("global_load_lds_dword %0, %1" ::"v"(sa_off + (uint32_t)(4 * k)),
-                   "s"(reinterpret_cast<const uint8_t*>(sa_base)), "{m0}"(sl)
-                   : "memory");
-      // the B-block scale through LDS as well: a plain global load here would
-      // be waited for with a vmcnt that also covers the DMA just issued
-      const uint32_t bl = lds_addr(&s_sb[k & 1][wave][0]);
-      asm volatile("global_load_lds_dword %0, %1" ::"v"((uint32_t)(4 * k)), "s"(sb_bytes), "{m0}"(bl) : "memory");
-    };
-
-    v4f acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-    // A of stage k + 1 is loaded when stage k begins, into the slot of stage
-    // k - 1. B of stage k + 2 is loaded as soon as every wave holds its B
-    // fragments of stage k, into that stage's B half: the B operand, mostly
-    // fetched from HBM (each B tile serves few row tiles), gets one and a half
-    // stages to land, A (shared by the tile row, mostly L2 hits) one.
-    issue_ops(0);
-    issue_scales(0);
-    if (!loads_a && nk > 1) issue_ops(1);
-    for (int64_t k = 0; k < nk; ++k) {
-      // stage k landed everywhere and every wave is done with stage k - 1
-      if (loads_a || k + 1 >= nk) wait_vm_lgkm_and_barrier<0>();
-      else wait_vm_lgkm_and_barrier<D>();  // B of stage k + 1 may stay in flight
-      if (k + 1 < nk) {
-        if (loads_a) issue_ops(k + 1);
-        issue_scales(k + 1);
+      for (int d = 0; d < D; ++d) {
+        const int32_t r = r0 + 8 * d;
+        const int32_t rr = r < rows ? r : rows - 1;
+        dma16(bk, (uint32_t)rr * (uint32_t)K32 + ((d & 1) ? cb1 : cb0), slot + (uint32_t)(d * 1024));
       }
-      const float sbk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_sb[k & 1][wave][0])));
-      const uint8_t* st = lds + (k & 1) * STAGE;
-      v8i bf[NI];
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(st + fb_lo[j]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(st + fb_hi[j]);
-        bf[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto issue_sa = [&](int64_t kb) {
+      uint32_t l = (uint32_t)lane;
+      asm volatile("" : "+v"(l));
+      int32_t sr = 64 * wn + (int32_t)l;
+      sr = sr < a_rows ? sr : a_rows - 1;
+      const uint32_t o = (uint32_t)(sr * (int32_t)nk + (int32_t)kb) * 4u;
+      if constexpr (SC4) {
+        const uint32_t l = lds_addr(&s_sa[(kb >> 2) & 1][4 * 64 * wn]);
+        asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(o), "s"(sa_bytes), "{m0}"(l) : "memory");
+      } else {
+        const uint32_t l = lds_addr(&s_sa[(kb >> 2) & 1][(kb & 3) * BM + 64 * wn]);
+        asm volatile("global_load_lds_dword %0, %1" ::"v"(o), "s"(sa_bytes), "{m0}"(l) : "memory");
       }
-      // every wave holds its B fragments: the B half of this slot is free
-      wait_lgkm_and_barrier();
-      if (!loads_a && k + 2 < nk) issue_ops(k + 2);
-      // software pipeline over the row blocks: the products of block i issue
-      // while the FMAs that scale block i - 1 into the result run on the VALU,
-      // and block i + 1's fragment is read meanwhile
-      auto ld_a = [&](int i, v8i& af, float4& sv) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(st + fa_lo[i]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(st + fa_hi[i]);
-        af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        // rows 16 i + 4 g + r (r < 4) of this lane's output block
-        sv = *reinterpret_cast<const float4*>(&s_sa[k & 1][wm * TM + 16 * i + 4 * lg]);
-      };
-      v8i af_c, af_n;
-      float4 sv_c, sv_n;
-      v4f pr_p[NI];
-      float fp[4];
-      ld_a(0, af_c, sv_c);
-      // the FMAs that scale the previous block's products into the result
-      auto fma_prev = [&](int i, int j) {
-        acc[i][j][0] += pr_p[j][0] * fp[0];
-        acc[i][j][1] += pr_p[j][1] * fp[1];
-        acc[i][j][2] += pr_p[j][2] * fp[2];
-        acc[i][j][3] += pr_p[j][3] * fp[3];
-      };
-#pragma unroll
-      for (int i = 0; i <= MI; ++i) {
-        v4f pr_c[NI];
-        if (i < MI) {
-          if (i + 1 < MI) ld_a(i + 1, af_n, sv_n);
-          // product j, then (fixed order) the FMAs of product j of block i - 1
-#pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-            __builtin_amdgcn_sched_barrier(0);
-            pr_c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_c, bf[j], z, AE5 ? 1 : 0, BE5 ? 1 : 0, 0,
-                                                                       127, 0, 127);
-            if (i > 0) fma_prev(i - 1, j);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          // sources stay live until every product exists (the statement
-          // takes both), so the compiler cannot hand their registers to a
-          // destination (not allowed for this MFMA)
-          asm volatile("" ::"v"(af_c), "v"(bf[0]), "v"(bf[1]), "v"(bf[2]), "v"(bf[3]), "v"(pr_c[0]),
-                       "v"(pr_c[1]), "v"(pr_c[2]), "v"(pr_c[3]));
-#pragma unroll
-          for (int j = 0; j < NI; ++j) pr_p[j] = pr_c[j];
-          fp[0] = sv_c.x * sbk;
-          fp[1] = sv_c.y * sbk;
-          fp[2] = sv_c.z * sbk;
-          fp[3] = sv_c.w * sbk;
-          af_c = af_n;
-          sv_c = sv_n;
+    };
+    auto issue_sb = [&](int64_t kb) {
+      const uint32_t o = (uint32_t)(4 * kb);
+      if (lane == 0) {
+        if constexpr (SC4) {
+          const uint32_t l = lds_addr(&s_sb[(kb >> 2) & 1][wn][0]);
+          asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(o), "s"(sb_bytes), "{m0}"(l) : "memory");
         } else {
-#pragma unroll
-          for (int j = 0; j < NI; ++j) fma_prev(MI - 1, j);
+          const uint32_t l = lds_addr(&s_sb[(kb >> 2) & 1][wn][kb & 3]);
+          asm volatile("global_load_lds_dword %0, %1" ::"v"(o), "s"(sb_bytes), "{m0}"(l) : "memory");
         }
       }
-    }
-    // every wave is done reading the last stage before the next tile's loads
-    // refill its slot
-    wait_vm_lgkm_and_barrier<0>();
+    };
 
-    // ---- epilogue: lane l holds rows 16 i + 4 g + r, column 16 j + l % 16 ----
-    __builtin_amdgcn_s_waitcnt(0);
+    auto frag = [&](uint32_t o0, uint32_t o1) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(lds + o0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(lds + o1);
+      return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    v16f acc[4][2];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t n = ti.n0 + wn * TN + 16 * j + lr;
-      if (n >= N) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = ti.m0 + wm * TM + 16 * i + 4 * lg + r;
-          if (m >= ti.m_end) continue;
-          if constexpr (OF32)
-            reinterpret_cast<float*>(p.out)[m * N + n] = acc[i][j][r];
-          else
-            reinterpret_cast<uint16_t*>(p.out)[m * N + n] = f32_to_bf16_rne(acc[i][j][r]);
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // prologue: K block 0 (both operands) and B of K block 1
+    issue_ops(0);
+    if (grp == 0) {
+      issue_sa(0);
+    } else {
+      issue_sb(0);
+      if (nk > 1) {
+        issue_ops(1);
+        if (has_scale(1)) issue_sb(1);
+      }
+    }
+    for (int64_t kb = 0; kb < nk; ++kb) {
+      // K block kb has landed (each wave waits for its own loads of kb, the
+      // barrier for everyone's); every wave is done with kb - 1
+      if (grp == 0 || kb + 1 >= nk) {
+        wait_vm_lgkm_and_barrier<0>();
+      } else if (has_scale(kb + 1)) {
+        // B of kb + 1 (issued in the prologue or after the second barrier of
+        // kb - 1) may stay in flight
+        wait_vm_lgkm_and_barrier<D + 1>();
+      } else {
+        wait_vm_lgkm_and_barrier<D>();
+      }
+      if (grp == 0 && kb + 1 < nk) {
+        issue_ops(kb + 1);
+        if (has_scale(kb + 1)) issue_sa(kb + 1);
+      }
+      uint32_t so = (uint32_t)((kb & 1) * STAGE);
+      asm volatile("" : "+s"(so));
+      const int q = (int)(kb & 3);
+      const float* ss = &s_sa[(kb >> 2) & 1][0];
+      v8i fb[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          fb[j][kh] = frag(so + b_part + fo[kh][0] + 4096 * j, so + b_part + fo[kh][1] + 4096 * j);
+      const float sbk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_sb[(kb >> 2) & 1][wn][q])));
+      // A fragments and factor of row block i, double-buffered
+      v8i fa[2][2];
+      float f[2];
+      auto read_a = [&](int i) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          fa[i & 1][kh] = frag(so + a_part + fo[kh][0] + 4096 * i, so + a_part + fo[kh][1] + 4096 * i);
+        const int m = grp * TM + 32 * i + lrow;
+        f[i & 1] = SC4 ? ss[4 * m + q] : ss[q * BM + m];
+      };
+      read_a(0);
+
+      // product n = (row block n / 2, column block n % 2): two instructions
+      // (K halves) into P[n % 2]; the FMAs of product n - 1 run between them
+      const v16f z = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      v16f P[2];
+      auto scale_add = [&](int n) {
+        const int i = n >> 1, j = n & 1;
+        const float fs = f[i & 1] * sbk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(P[n & 1][e], fs, acc[i][j][e]);
+      };
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int i = n >> 1, j = n & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        P[n & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[i & 1][0], z, BE5 ? 1 : 0,
+                                                                   AE5 ? 1 : 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n > 0) scale_add(n - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        P[n & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[i & 1][1], P[n & 1], BE5 ? 1 : 0,
+                                                                   AE5 ? 1 : 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+        // row block i's A fragments stay live up to its last instruction (no
+        // product may take their registers); i + 1's are read while i runs
+        if (j == 1) asm volatile("" ::"v"(fa[i & 1][0]), "v"(fa[i & 1][1]));
+        if (j == 0 && i + 1 < 4) read_a(i + 1);
+        if (n == 1) {
+          // every wave holds its B fragments of kb (waited for before the
+          // first product): waves 4-7 refill the B half of kb's slot with
+          // kb + 2. The products issued so far keep the matrix core busy
+          // through the barrier.
+          asm volatile("" : "+v"(P[1]), "+v"(acc[0][0]));
+          asm volatile("s_barrier" ::: "memory");
+          if (grp == 1 && kb + 2 < nk) {
+            issue_ops(kb + 2);
+            if (has_scale(kb + 2)) issue_sb(kb + 2);
+          }
+        }
+      }
+      scale_add(7);
+      // the K block's results and B fragments are pinned before the next
+      // barrier: the products and FMAs have no side effects and would
+      // otherwise be sunk past it
+      asm volatile(""
+                   : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[2][0]),
+                     "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1])
+                   : "v"(fb[0][0]), "v"(fb[0][1]), "v"(fb[1][0]), "v"(fb[1][1]));
+    }
+
+    // ---- epilogue: element 4 q + u of block (i, j) is row m = 32 i + lrow,
+    // column n = 32 j + 8 q + 4 g + u of the wave's part; the four u are
+    // adjacent in memory ----
+    const int32_t m_lim = (int32_t)(ti.m_end - ti.m0);
+    const int32_t n_lim = (int32_t)(N - ti.n0);
+    int32_t N32 = (int32_t)N;
+    asm volatile("" : "+s"(N32));
+    const int64_t corner = ti.m0 * N + ti.n0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t ml = grp * TM + 32 * i + lrow;
+      if (ml >= m_lim) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t nl = wn * TN + 32 * j + 8 * q + 4 * g;
+          if (nl >= n_lim) continue;  // n_lim is a multiple of 128: the four are valid together
+          const uint32_t o = (uint32_t)(ml * N32 + nl);
+          const v16f& a = acc[i][j];
+          if constexpr (OF32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + corner + o) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          } else {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(a[4 * q]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 1]) << 16);
+            const uint32_t hi =
+                (uint32_t)f32_to_bf16_rne(a[4 * q + 2]) | ((uint32_t)f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + corner + o) = make_uint2(lo, hi);
+          }
         }
       }
     }
+    // every wave is done with the last K block's slot, and the next tile's
+    // loads count their own completions: stores complete first
+    wait_vm_lgkm_and_barrier<0>();
   }
 }
 
@@ -649,7 +738,12 @@ static hipError_t launch_fast_cfg(const GemmArgs& g) {
   if (grid >= kNumXcd) grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
   if constexpr (SK == kScaleBlock) {
-    hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+    // scales of four K blocks per 16-byte load
+    const bool sc4 = (g.K / 128) % 4 == 0 && ((uintptr_t)g.sa % 16) == 0 && ((uintptr_t)g.sb % 16) == 0;
+    if (sc4)
+      hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32, true>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
+    else
+      hipLaunchKernelGGL((k_gemm_fp8_block<AE5, BE5, OF32, false>), dim3((unsigned)grid), dim3(512), 0, g.stream, p);
   } else {
     if (g.offsets && g.b_kpacked)
       hipLaunchKernelGGL((k_gemm_fp8_pp<AE5, BE5, SK, OF32, true, true, EX>), dim3((unsigned)grid), dim3(512), 0,
@@ -699,7 +793,9 @@ bool gemm_fp8_fast_eligible(const GemmArgs& g) {
   if (g.K % 128 != 0 || g.K == 0) return false;
   if (g.K > (1 << 23)) return false;  // 32-bit in-tile offsets: 256 rows * K < 2^31
   if (!al(g.a, 16) || !al(g.b, 16)) return false;
-  if (g.scale_kind == kScaleMX && (!al(g.sa, 4) || !al(g.sb, 4))) return false;
+  if ((g.scale_kind == kScaleMX || g.scale_kind == kScaleBlock) && (!al(g.sa, 4) || !al(g.sb, 4))) return false;
+  // the blockwise kernel stores 4 adjacent outputs per lane (8 or 16 bytes)
+  if (g.scale_kind == kScaleBlock && !al(g.out, 16)) return false;
   return true;
 }
 

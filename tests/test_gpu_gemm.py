@@ -218,13 +218,23 @@ def test_grouped_row(f, counts, N, K, fast):
     check_gemm(got, ref, S, True, f"grouped row {counts}", exact=not fast)
 
 
-@pytest.mark.parametrize("counts,N,K,out_f32", [([100, 0, 200, 7], 256, 384, False), ([512, 512], 128, 256, False),
-                                                 ([64], 128, 128, False), ([300, 5, 0, 129], 384, 640, True),
-                                                 ([4096, 4096], 2304, 128, False)])
+@pytest.mark.parametrize("counts,N,K,out_f32,shift", [([100, 0, 200, 7], 256, 384, False, 0),
+                                                       ([512, 512], 128, 256, False, 0),
+                                                       ([64], 128, 128, False, 0),
+                                                       ([300, 5, 0, 129], 384, 640, True, 0),
+                                                       ([4096, 4096], 2304, 128, False, 0),
+                                                       ([64], 256, 512, False, 0),
+                                                       ([300, 5, 0, 129], 384, 1024, False, 0),
+                                                       ([600, 0, 3], 512, 2048, True, 0),
+                                                       ([1000, 24], 640, 1536, False, 0),
+                                                       ([300, 5, 0, 129], 384, 1024, False, 4),
+                                                       ([600, 0, 3], 512, 1152, False, 0)])
 @pytest.mark.parametrize("fast", [True, False])
-def test_grouped_block(f, counts, N, K, out_f32, fast):
+def test_grouped_block(f, counts, N, K, out_f32, shift, fast):
     """One K block (no prefetch), an odd number of K blocks, a partial B tile and fp32
-    output, and more tiles than workgroups (each walks several, reusing its LDS slots)."""
+    output, and more tiles than workgroups (each walks several, reusing its LDS slots).
+    K % 512 == 0 with 16-byte aligned scales takes the kernel's loads of four K blocks'
+    scales at a time; other K, or scales at a 4-byte offset (shift), one K block's."""
     import torch
     e4, _ = _names(f)
     rng = np.random.default_rng(11)
@@ -234,7 +244,14 @@ def test_grouped_block(f, counts, N, K, out_f32, fast):
     sa = rng.uniform(0.01, 4, (Mt, K // 128)).astype(np.float32)
     sb = rng.uniform(0.01, 4, (E, N // 128, K // 128)).astype(np.float32)
     out = _out((Mt, N), out_f32)
-    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_BLOCK128, to_dev(sa), to_dev(sb),
+
+    def shifted(x):
+        # the same floats at a device address `shift` bytes past a 256-byte boundary
+        buf = torch.zeros(x.size + 64, dtype=torch.float32, device="cuda:0")
+        v = buf[shift // 4:shift // 4 + x.size]
+        v.copy_(torch.from_numpy(x.reshape(-1)).to("cuda:0"))
+        return v
+    f.fp8_grouped_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_BLOCK128, shifted(sa), shifted(sb),
                      to_dev(off), f.OUT_F32 if out_f32 else f.OUT_BF16, out, use_fast_accum=fast)
     torch.cuda.synchronize()
     ref = oracle.grouped_mm(a, e4, b, e4, oracle.SCALE_BLOCK128, sa, sb, off)
