@@ -144,7 +144,7 @@ def test_quant_then_gemm_kpacked(f):
 
 
 @pytest.mark.parametrize("shape", [(128, 64), (2, 256, 48), (2048, 144), (4096, 128), (2112, 64),
-                                   (1024, 2112, 64)])
+                                   (1024, 2112, 64), (14336, 128), (3, 8192, 80), (16448, 64)])
 def test_quant_col_kpacked(f, shape):
     """The three column paths: up to 2048 rows in registers, the split form (column amax
     over row chunks, then the cast) and the fused two-read form (many strips)."""

@@ -133,8 +133,12 @@ def _run_col(f, fmt, name, x, guard=256):
 
 @pytest.mark.parametrize("shape", [(16, 8), (2048, 64), (2048, 72), (48, 200), (100, 24), (4096, 128),
                                    (3, 48, 40), (2, 2064, 64), (1024, 2064, 8), (64, 64, 512), (70, 32, 520),
-                                   (9, 2048, 3648), (40, 2000, 840)])
+                                   (9, 2048, 3648), (40, 2000, 840),
+                                   (14336, 256), (16384, 200), (3, 8192, 136), (5008, 72), (16400, 72)])
 def test_quant_col(f, shape):
+    """Up to 2048 rows: one workgroup per strip in registers. More rows: the split
+    form (amax pass over row chunks, then the cast pass), with ragged last strips,
+    batches and row counts that are not a multiple of the 1024-row chunk."""
     x = _x(shape, 300 + shape[-1], spread=False)
     for fmt, name in _natives(f):
         print("col", shape, name, flush=True)
