@@ -283,12 +283,15 @@ def build_step(f, torch, dev, wls, dev_of):
            lambda: f.fp8_quant_block(we5, 128, 128, E4, EPS, qw5, sw5, iw5))
     st.add("moe_block_mx.grouped_gemm_block", "gemm8", 2.0 * M5 * N5 * K5,
            lambda: f.fp8_grouped_mm(qa5, E4, qw5, E4, f.SCALE_BLOCK128, ia5, iw5, off5, f.OUT_BF16, out5))
+    # MX codes written in the k-packed grouped GEMM's operand layouts by the
+    # quantizers themselves (A pair-interleaved, W k-packed), as for moe_grouped
     st.add("moe_block_mx.quant_mx_a", "quant", 3 * M5 * K5 + M5 * (K5 // 32),
-           lambda: f.fp8_quant_mx(a5, E4, f.MX_POW2_FLOOR, EPS, qa5m, ea5))
+           lambda: f.fp8_quant_mx_kpaired(a5, E4, f.MX_POW2_FLOOR, EPS, qa5m, ea5))
     st.add("moe_block_mx.quant_mx_w", "quant", 3 * E5n * N5 * K5 + E5n * N5 * (K5 // 32),
-           lambda: f.fp8_quant_mx(we5, E4, f.MX_POW2_FLOOR, EPS, qw5m, ew5))
+           lambda: f.fp8_quant_mx_kpacked(we5, E4, f.MX_POW2_FLOOR, EPS, qw5m, ew5))
     st.add("moe_block_mx.grouped_gemm_mx", "gemm8", 2.0 * M5 * N5 * K5,
-           lambda: f.fp8_grouped_mm(qa5m, E4, qw5m, E4, f.SCALE_MX32, ea5, ew5, off5, f.OUT_BF16, out5m))
+           lambda: f.fp8_grouped_mm_kpacked(qa5m, E4, qw5m.reshape(E5n, -1), E4, f.SCALE_MX32, ea5, ew5, off5,
+                                            f.OUT_BF16, out5m, N5))
     return st
 
 

@@ -27,7 +27,7 @@ EXPORTS = [
     "fp8_quant_tensor", "fp8_quant_tensor_ws_bytes", "fp8_quant_row", "fp8_quant_row_kpacked", "fp8_quant_row_kpaired", "fp8_quant_col",
     "fp8_quant_col_kpacked",
     "fp8_quant_col_ws_bytes", "fp8_quant_col_noalloc", "fp8_quant_dual", "fp8_quant_dual_ws_bytes", "fp8_norm_quant_row",
-    "fp8_quant_block", "fp8_quant_mx",
+    "fp8_quant_block", "fp8_quant_mx", "fp8_quant_mx_kpacked", "fp8_quant_mx_kpaired",
     "fp8_scaled_mm", "fp8_scaled_mm_kpacked",
     "fp8_grouped_mm", "fp8_grouped_mm_kpacked", "fp8_wgrad_bf16", "fp8_grouped_wgrad_bf16", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_linear_ws_bytes", "fp8_validate_offsets",
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
         "fp8_quant_dual_ws_bytes": (SZ, []),
         "fp8_quant_block": (I, [P, I64, I64, I64, I, I, I, D, P, P, P, P]),
         "fp8_quant_mx": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
+        "fp8_quant_mx_kpacked": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
+        "fp8_quant_mx_kpaired": (I, [P, I64, I64, I64, I, I, D, P, P, P]),
         "fp8_scaled_mm": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
         "fp8_scaled_mm_kpacked": (I, [P, I, P, I, I, P, P, I64, I64, I64, I, P, I, P]),
         "fp8_grouped_mm": (I, [P, I, P, I, I, P, P, P, I32, I64, I64, I64, I, P, I, P]),
@@ -324,6 +326,27 @@ def fp8_quant_mx(x, fmt, mode, eps, q, e8m0, stream=None):
     _arg(fn, "e8m0", e8m0, b * r * (c // 32), 1)
     _check(fn, load().fp8_quant_mx(
         _ptr(x), b, r, c, int(fmt), int(mode), float(eps), _ptr(q), _ptr(e8m0), _stream(stream)))
+
+
+def _quant_mx_packed(fn, x, fmt, mode, eps, q, e8m0, stream):
+    b, r, c = _brc(x)
+    _arg(fn, "x", x, 2 * b * r * c, 2)
+    _arg(fn, "q", q, b * r * c, 1)
+    _arg(fn, "e8m0", e8m0, b * r * (c // 32), 1)
+    _check(fn, getattr(load(), fn)(
+        _ptr(x), b, r, c, int(fmt), int(mode), float(eps), _ptr(q), _ptr(e8m0), _stream(stream)))
+
+
+def fp8_quant_mx_kpacked(x, fmt, mode, eps, q, e8m0, stream=None):
+    """fp8_quant_mx with the codes k-packed (1 KB chunks of 16 rows x 64 columns per
+    batch slice: fp8_grouped_mm_kpacked's B); q is any uint8 tensor of x.numel() bytes."""
+    _quant_mx_packed("fp8_quant_mx_kpacked", x, fmt, mode, eps, q, e8m0, stream)
+
+
+def fp8_quant_mx_kpaired(x, fmt, mode, eps, q, e8m0, stream=None):
+    """fp8_quant_mx with the codes pair-interleaved (rows 2i, 2i + 1 sharing each
+    128-byte line of a 64-column block: fp8_grouped_mm_kpacked's A)."""
+    _quant_mx_packed("fp8_quant_mx_kpaired", x, fmt, mode, eps, q, e8m0, stream)
 
 
 # ---- GEMMs ----------------------------------------------------------------------

@@ -380,6 +380,33 @@ fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t rows, int64_t 
   return dev_err(launch_quant_mx(a, e8m0, (int)mode));
 }
 
+// fp8_quant_mx with packed codes (group_rows 16: k-packed, 2: pair-interleaved)
+static fp8_status quant_mx_packed(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                  fp8_mx_mode mode, double eps, uint8_t* q, uint8_t* e8m0, void* stream,
+                                  int group_rows) {
+  if (mode != FP8_MX_POW2_FLOOR && mode != FP8_MX_OCP) return FP8_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0x1p-100)) return FP8_ERR_INVALID_ARGUMENT;
+  fp8_status st = check_quant_common(x, batch, rows, cols, eps, q, e8m0);
+  if (st != FP8_OK || batch * rows * cols == 0) return st;
+  if (rows % group_rows != 0 || cols % 64 != 0) return FP8_ERR_ALIGNMENT;
+  if (((uintptr_t)x & 15) != 0 || ((uintptr_t)q & 15) != 0) return FP8_ERR_ALIGNMENT;
+  bool e5;
+  double fm;
+  if ((st = resolve(fmt, &e5, &fm)) != FP8_OK) return st;
+  QuantArgs a{x, batch, rows, cols, e5, fm, eps, q, nullptr, nullptr, (hipStream_t)stream};
+  return dev_err(launch_quant_mx_packed(a, e8m0, (int)mode, group_rows));
+}
+
+fp8_status fp8_quant_mx_kpacked(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                fp8_mx_mode mode, double eps, uint8_t* q, uint8_t* e8m0, void* stream) {
+  return quant_mx_packed(x, batch, rows, cols, fmt, mode, eps, q, e8m0, stream, 16);
+}
+
+fp8_status fp8_quant_mx_kpaired(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, fp8_format fmt,
+                                fp8_mx_mode mode, double eps, uint8_t* q, uint8_t* e8m0, void* stream) {
+  return quant_mx_packed(x, batch, rows, cols, fmt, mode, eps, q, e8m0, stream, 2);
+}
+
 static fp8_status check_gemm(const void* a, const void* b, const void* sa, const void* sb, int64_t M, int64_t N,
                              int64_t K, fp8_scaling scaling, fp8_out out_type, const void* out) {
   if (M < 0 || N < 0 || K < 0) return FP8_ERR_INVALID_ARGUMENT;

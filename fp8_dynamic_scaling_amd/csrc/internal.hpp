@@ -72,6 +72,7 @@ struct TJobSpec {
 hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps, uint32_t* amax_words,
                                        hipStream_t stream);
 hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode);
+hipError_t launch_quant_mx_packed(const QuantArgs& a, uint8_t* e8m0, int mode, int group_rows);
 
 // Probe kernels: results[0..3] = fp8 codes of 1.0 (e4m3, e5m2) and of the
 // formats' maxima; results[4..5] = matrix-core dot products of 128 copies of

@@ -1421,4 +1421,71 @@ hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode) {
   return a.e5 ? launch_mx_t<true>(a, e8m0, mode) : launch_mx_t<false>(a, e8m0, mode);
 }
 
+// MX groups as k_quant_group1d<E5, 32, true>, codes written in the packed
+// layouts of the grouped GEMM's operands: GR = 16 k-packed (1 KB chunks of
+// 16 rows x 64 columns), GR = 2 pair-interleaved (128-byte chunks of 2 rows
+// x 64 columns); code (r, c) at ((r / GR) * (cols / 64) + c / 64) * 64 GR +
+// (r % GR) * 64 + c % 64. A tile is GR rows x 2048 / GR columns, 8 columns
+// per lane (a 32-column group is 4 neighbouring lanes), so a workgroup
+// writes whole chunks: both halves of every 128-byte line come from one CU
+// and meet in its L2 (with row-major work each half line would be written
+// from another XCD). A workgroup takes U column-adjacent tiles per
+// iteration, loads first, so it reads U * 4096 / GR contiguous bytes of each
+// of its rows.
+template <bool E5, int GR, int U>
+__global__ __launch_bounds__(256) void k_quant_mx_packed(const uint16_t* __restrict__ x, int64_t nrows, int64_t cols,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ e8m0,
+                                                         double fmax, double eps, int mx_mode) {
+  constexpr int TC = 2048 / GR, LPR = TC / 8;
+  const int lane_row = threadIdx.x / LPR, c8 = threadIdx.x % LPR;
+  const int64_t ntc = (cols + TC - 1) / TC;
+  const int64_t total = nrows / GR * ntc;
+  const int64_t cb = cols / 64, g32 = cols / 32;
+  const float fm = (float)fmax;
+  for (int64_t t0 = (int64_t)blockIdx.x * U; t0 < total; t0 += (int64_t)gridDim.x * U) {
+    uint4 v[U];
+    int64_t r[U], c[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u;
+      const int64_t band = t / ntc, tc = t % ntc;
+      r[u] = band * GR + lane_row;
+      c[u] = tc * TC + 8 * c8;
+      ok[u] = t < total && c[u] < cols;
+      v[u] = ok[u] ? ld_nt16(x + r[u] * cols + c[u]) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float m = amax8(v[u], 0.0f);
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const int k = mx_exponent(m, fmax, eps, mx_mode);
+      if (ok[u]) {
+        if ((c8 & 3) == 0) e8m0[r[u] * g32 + c[u] / 32] = (uint8_t)(127 - k);
+        const int64_t o = ((r[u] / GR) * cb + c[u] / 64) * (64 * GR) + (r[u] % GR) * 64 + c[u] % 64;
+        *reinterpret_cast<uint2*>(q + o) = quant8<E5>(v[u], exp2i(k), fm);
+      }
+    }
+  }
+}
+
+template <bool E5, int GR>
+static hipError_t launch_mx_packed_t(const QuantArgs& a, uint8_t* e8m0, int mode) {
+  const int64_t R = a.batch * a.rows, C = a.cols;
+  if (R == 0 || C == 0) return hipSuccess;
+  constexpr int U = 4;
+  const int64_t tiles = R / GR * ((C + 2048 / GR - 1) / (2048 / GR));
+  int64_t blocks = (tiles + U - 1) / U;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((k_quant_mx_packed<E5, GR, U>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, R, C, a.q,
+                     e8m0, a.fmax, a.eps, mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_packed(const QuantArgs& a, uint8_t* e8m0, int mode, int group_rows) {
+  if (group_rows == 2) return a.e5 ? launch_mx_packed_t<true, 2>(a, e8m0, mode) : launch_mx_packed_t<false, 2>(a, e8m0, mode);
+  return a.e5 ? launch_mx_packed_t<true, 16>(a, e8m0, mode) : launch_mx_packed_t<false, 16>(a, e8m0, mode);
+}
+
 }  // namespace fp8dyn

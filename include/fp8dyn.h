@@ -279,6 +279,22 @@ FP8DYN_API fp8_status fp8_quant_mx(const uint16_t* x, int64_t batch, int64_t row
                                    fp8_format fmt, fp8_mx_mode mode, double eps, uint8_t* q,
                                    uint8_t* e8m0, void* stream);
 
+/* MXFP8 as fp8_quant_mx (same codes, same E8M0 bytes, e8m0 row-major), with
+ * the codes written in the packed layouts of fp8_grouped_mm_kpacked's
+ * operands: _kpacked, its B, code (r, c) of each batch slice at byte
+ * ((r / 16) * (cols / 64) + c / 64) * 1024 + (r % 16) * 64 + c % 64 (as
+ * fp8_quant_row_kpacked), rows % 16 == 0; _kpaired, its A, at
+ * ((r / 2) * (cols / 64) + c / 64) * 128 + (r % 2) * 64 + c % 64 (as
+ * fp8_quant_row_kpaired), rows % 2 == 0. Both need cols % 64 == 0 and
+ * 16-byte aligned x and q (else FP8_ERR_ALIGNMENT); native formats only.
+ * q holds batch * rows * cols bytes. */
+FP8DYN_API fp8_status fp8_quant_mx_kpacked(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                           fp8_format fmt, fp8_mx_mode mode, double eps, uint8_t* q,
+                                           uint8_t* e8m0, void* stream);
+FP8DYN_API fp8_status fp8_quant_mx_kpaired(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                           fp8_format fmt, fp8_mx_mode mode, double eps, uint8_t* q,
+                                           uint8_t* e8m0, void* stream);
+
 /* ---- GEMMs [P-TAO section 4; P-AMD "Scaling FP8 to MoE Architectures"] ----
  * out[m][n] = a_inv * b_inv * sum_k dec(a[m][k]) * dec(b[n][k]) on the matrix
  * cores, scales applied in fp32, stored as bf16 (round to nearest even) or

@@ -77,6 +77,16 @@ def test_host_validation_without_gpu(f):
     for mode in (f.MX_POW2_FLOOR, f.MX_OCP):
         assert lib.fp8_quant_mx(FAKE, 1, 4, 64, f.E4M3_NATIVE, mode, 2.0 ** -101, FAKE, FAKE, None) == \
             f.ERR_INVALID_ARGUMENT
+    # packed MX: cols % 64, rows % 16 (k-packed) or % 2 (pair-interleaved), 16-byte
+    # aligned x and q, and the same eps bound
+    kp, kq = lib.fp8_quant_mx_kpacked, lib.fp8_quant_mx_kpaired
+    assert kp(FAKE, 1, 16, 96, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
+    assert kp(FAKE, 1, 8, 64, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
+    assert kq(FAKE, 1, 3, 64, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
+    assert kq(FAKE + 8, 1, 2, 64, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.ERR_ALIGNMENT
+    assert kp(FAKE, 1, 16, 64, f.E4M3_NATIVE, f.MX_OCP, 2.0 ** -101, FAKE, FAKE, None) == f.ERR_INVALID_ARGUMENT
+    assert kq(FAKE, 1, 2, 64, f.E4M3_NATIVE, 7, 1e-12, FAKE, FAKE, None) == f.ERR_INVALID_ARGUMENT
+    assert kp(FAKE, 0, 16, 64, f.E4M3_NATIVE, f.MX_POW2_FLOOR, 1e-12, FAKE, FAKE, None) == f.OK
     # block geometry
     assert lib.fp8_quant_block(FAKE, 1, 4, 8, 2, 128, f.E4M3_NATIVE, 1e-12, FAKE, FAKE, None, None) == f.ERR_INVALID_ARGUMENT
     # tensorwise needs a workspace

@@ -1,6 +1,7 @@
-"""GPU parity of the packed-operand paths: fp8_quant_row_kpacked / fp8_quant_col_kpacked
-write the oracle's codes (bit-exact) permuted into 1 KB chunks of 16 rows x 64 columns,
-fp8_quant_row_kpaired into pair-interleaved rows, and the k-packed GEMMs on those give
+"""GPU parity of the packed-operand paths: fp8_quant_row_kpacked / fp8_quant_col_kpacked /
+fp8_quant_mx_kpacked write the oracle's codes (bit-exact) permuted into 1 KB chunks of 16
+rows x 64 columns, fp8_quant_row_kpaired / fp8_quant_mx_kpaired into pair-interleaved
+rows, and the k-packed GEMMs on those give
 the oracle's products (to the GEMM bar of tests/gpu_util.check_gemm) and the same bits
 as the row-major GEMMs. The permutation (tests/gpu_util.kpack) is numpy reshapes of the layout
 the header states; nothing of it is shared with the library."""
@@ -50,6 +51,31 @@ def test_quant_row_kpacked(f, shape):
         rq, rs, ri = oracle.quant_row(x, name, EPS)
         assert np.array_equal(u8(q), kpack(rq))
         assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(i.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("g", [16, 2])
+@pytest.mark.parametrize("shape", [(16, 64), (48, 5120), (2, 32, 192), (3, 16, 1088), (64, 7168), (2, 96, 4160)])
+def test_quant_mx_packed(f, shape, g):
+    """Codes and E8M0 bytes of fp8_quant_mx, the codes permuted into the packed layout:
+    a column count that is not a multiple of a workgroup tile (128 or 1024 columns),
+    batches, an all-zero group and a large outlier, both rounding modes of the scale."""
+    import torch
+    x = synth.normal_bf16(shape, 930 + shape[-1] + g, 1.0)
+    x.reshape(-1, shape[-1])[3, 32:64] = 0   # an all-zero group (eps clamp)
+    x.reshape(-1, shape[-1])[5, 7] = 0x4700  # 32768.0
+    n = int(np.prod(shape))
+    fn = f.fp8_quant_mx_kpacked if g == 16 else f.fp8_quant_mx_kpaired
+    for mode in (f.MX_POW2_FLOOR, f.MX_OCP):
+        for fmt, name in _natives(f):
+            print("mx packed", g, shape, mode, name, flush=True)
+            q, full = empty_u8((n,), 256)
+            e = torch.empty(shape[:-1] + (shape[-1] // 32,), dtype=torch.uint8, device="cuda:0")
+            fn(to_dev_bf16(x), fmt, mode, EPS, q, e)
+            torch.cuda.synchronize()
+            check_guard(full, 256)
+            rq, re = oracle.quant_mx(x, name, mode, EPS)
+            assert np.array_equal(u8(q), kpack(rq, g))
+            assert np.array_equal(u8(e), re)
 
 
 def _offsets(counts):

@@ -410,3 +410,18 @@ def test_moe_block_and_mx(f):
     S = oracle.grouped_mm_sample(r_qa, e4, r_qw, e4, oracle.SCALE_MX32, r_ea, r_ew, off, r, c, absolute=True)
     check_gemm(_gather(out, r, c), ref, S, True, "moe MX gemm (sampled)")
     check_gemm(_gather(out_x, r, c), ref, S, True, "moe MX gemm (sampled)", exact=True)
+    # the packed path the benchmark times: the MX quantizers writing pair-interleaved A
+    # and k-packed W give the oracle's codes permuted and the same E8M0 bytes, and the
+    # k-packed grouped GEMM on them gives the row-major GEMM's bits
+    qap, qwp = torch.empty_like(qa), torch.empty_like(qw)
+    eap, ewp = torch.empty_like(ea), torch.empty_like(ew)
+    f.fp8_quant_mx_kpaired(ad, f.E4M3_NATIVE, f.MX_POW2_FLOOR, EPS, qap, eap)
+    f.fp8_quant_mx_kpacked(wd, f.E4M3_NATIVE, f.MX_POW2_FLOOR, EPS, qwp, ewp)
+    out_p = torch.empty_like(out)
+    f.fp8_grouped_mm_kpacked(qap, f.E4M3_NATIVE, qwp.reshape(E, -1), f.E4M3_NATIVE, f.SCALE_MX32, eap, ewp, offd,
+                             f.OUT_BF16, out_p, N)
+    torch.cuda.synchronize()
+    assert torch.equal(eap, ea) and torch.equal(ewp, ew)
+    assert np.array_equal(u8(qap).reshape(-1), kpack(r_qa, 2))
+    assert np.array_equal(u8(qwp).reshape(-1), kpack(r_qw, 16))
+    assert torch.equal(out_p.view(torch.int16), out.view(torch.int16))
