@@ -219,8 +219,10 @@ def build_step(f, torch, dev, wls, dev_of):
     E3, R3, C3 = we3.shape
     qt3 = torch.empty((E3, C3, R3), **u8)
     s3, i3 = torch.empty((E3, C3), **f32), torch.empty((E3, C3), **f32)
+    # the transposed codes k-packed (the MoE backward's grouped grad-input GEMM
+    # loads B from that layout in whole lines)
     st.add("expert_colwise.quant_col", "quant", 3 * E3 * R3 * C3 + 8 * E3 * C3,
-           lambda: f.fp8_quant_col(we3, E4, EPS, qt3, s3, i3, None))
+           lambda: f.fp8_quant_col_kpacked(we3, E4, EPS, qt3, s3, i3, None))
 
     # ---- moe_grouped ----
     w4 = wls["moe_grouped"]
@@ -254,13 +256,16 @@ def build_step(f, torch, dev, wls, dev_of):
     qgo4, sgo4, igo4 = torch.empty((Mt, N4), **u8), torch.empty(Mt, **f32), torch.empty(Mt, **f32)
     gx4 = torch.empty((Mt, K4), **bf)
     gw4 = torch.empty((E4n, N4, K4), **bf)
+    # grad_out pair-interleaved and the transposed weights k-packed: the k-packed
+    # grouped GEMM (same bits as the row-major one)
     st.add("moe_backward.quant_row_go_e5m2", "quant_next", 3 * Mt * N4 + 8 * Mt,
-           lambda: f.fp8_quant_row(go4, E5, EPS, qgo4, sgo4, igo4))
+           lambda: f.fp8_quant_row_kpaired(go4, E5, EPS, qgo4, sgo4, igo4))
     st.add("moe_backward.grouped_dgrad", "gemm8_next", 2.0 * Mt * N4 * K4,
-           lambda: f.fp8_grouped_mm(qgo4, E5, qt3, E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16, gx4))
+           lambda: f.fp8_grouped_mm_kpacked(qgo4, E5, qt3.reshape(E3, -1), E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16,
+                                            gx4, C3))
     st.add("moe_backward.grouped_dgrad_exact", "gemm8x_next", 2.0 * Mt * N4 * K4,
-           lambda: f.fp8_grouped_mm(qgo4, E5, qt3, E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16, gx4,
-                                    use_fast_accum=False))
+           lambda: f.fp8_grouped_mm_kpacked(qgo4, E5, qt3.reshape(E3, -1), E4, f.SCALE_ROW, igo4, i3, off4, f.OUT_BF16,
+                                            gx4, C3, use_fast_accum=False))
     st.add("moe_backward.grouped_wgrad_bf16", "gemm16_next", 2.0 * Mt * N4 * K4,
            lambda: f.fp8_grouped_wgrad_bf16(go4, a4, off4, gw4))
 

@@ -225,8 +225,11 @@ def test_scaled_mm_kpacked(f, M, N, K, scaling, out_f32):
     check_gemm(got, ref, S, not out_f32, f"scaled_mm kpacked {M}x{N}x{K} {scaling}")
 
 
-@pytest.mark.parametrize("shape", [(2, 64), (98, 7168), (2, 6, 192), (64, 16384), (3, 10, 4160)])
+@pytest.mark.parametrize("shape", [(2, 64), (98, 7168), (2, 6, 192), (64, 16384), (3, 10, 4160), (6, 2048),
+                                   (2, 10, 4096), (3, 4, 576)])
 def test_quant_row_kpaired(f, shape):
+    """A wavefront per row up to 4096 columns (a pair's two rows in one workgroup; 6 rows:
+    the last workgroup holds a single pair), a workgroup per row beyond."""
     import torch
     x = synth.normal_bf16(shape, 930 + shape[-1], 1.0)
     x.reshape(-1, shape[-1])[1] = 0

@@ -332,13 +332,30 @@ def test_moe_backward(f):
     f.fp8_grouped_mm(qg, f.E5M2_NATIVE, qT, f.E4M3_NATIVE, f.SCALE_ROW, ig, iT, offd, f.OUT_BF16, gx_fast)
     gw = torch.full((E, N, K), float("nan"), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_grouped_wgrad_bf16(gd, ad, offd, gw)
+    # the packed path the benchmark times: grad_out pair-interleaved, the transposed
+    # weights k-packed, the k-packed grouped GEMM giving the row-major GEMM's bits
+    qgp, qTp = torch.empty_like(qg), torch.empty_like(qT)
+    sgp, igp, sTp, iTp = torch.empty_like(sg), torch.empty_like(ig), torch.empty_like(sT), torch.empty_like(iT)
+    f.fp8_quant_row_kpaired(gd, f.E5M2_NATIVE, EPS, qgp, sgp, igp)
+    f.fp8_quant_col_kpacked(wd, f.E4M3_NATIVE, EPS, qTp, sTp, iTp, None)
+    gxp = torch.empty_like(gx)
+    gxp_fast = torch.empty_like(gx)
+    f.fp8_grouped_mm_kpacked(qgp, f.E5M2_NATIVE, qTp.reshape(E, -1), f.E4M3_NATIVE, f.SCALE_ROW, igp, iTp, offd,
+                             f.OUT_BF16, gxp, K, use_fast_accum=False)
+    f.fp8_grouped_mm_kpacked(qgp, f.E5M2_NATIVE, qTp.reshape(E, -1), f.E4M3_NATIVE, f.SCALE_ROW, igp, iTp, offd,
+                             f.OUT_BF16, gxp_fast, K)
     torch.cuda.synchronize()
+    assert torch.equal(igp, ig) and torch.equal(iTp, iT)
+    assert torch.equal(gxp.view(torch.int16), gx.view(torch.int16))
+    assert torch.equal(gxp_fast.view(torch.int16), gx_fast.view(torch.int16))
     del ad, wd, gd
     r_qg, _, r_ig = oracle.quant_row(go, e5, EPS)
     assert np.array_equal(u8(qg), r_qg) and np.array_equal(ig.cpu().numpy(), r_ig)
+    assert np.array_equal(u8(qgp).reshape(-1), kpack(r_qg, 2))
     r_qT, _, r_iT = oracle.quant_col(w, e4, EPS)
     assert np.array_equal(u8(qT), r_qT) and np.array_equal(iT.cpu().numpy(), r_iT)
-    _log("moe backward quantization bit-exact")
+    assert np.array_equal(u8(qTp).reshape(-1), kpack(r_qT, 16))
+    _log("moe backward quantization bit-exact (row-major and packed)")
     r, c = _samples(Mt, K, 6, offsets=off)
     ref = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c)
     S = oracle.grouped_mm_sample(r_qg, e5, r_qT, e4, oracle.SCALE_ROW, r_ig, r_iT, off, r, c, absolute=True)
