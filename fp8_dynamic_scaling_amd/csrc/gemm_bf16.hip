@@ -197,14 +197,21 @@ constexpr int64_t kTileCost = 4;
 // that loaded them zeroes those LDS rows after its own loads landed and before
 // the barrier that lets anyone read the stage. An empty expert gets a zero
 // gradient.
-template <bool GR>
+// Dense form: tiles [t_lo, t_lo + t_cnt) of the grouped tile order. HALF:
+// work item u is the k half u % 2 (128 columns) of tile t_lo + u / 2; it loads
+// the whole tile's stages and runs half the products, each wave 128 x 64. A
+// launch of half tiles takes the tiles that would otherwise leave most of the
+// last round of workgroups idle (section on the launcher below).
+template <bool GR, bool HALF = false>
 __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restrict__ gy, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ offsets, int32_t E, int64_t M,
-                                                      int64_t N, int64_t K, uint16_t* __restrict__ gw) {
+                                                      int64_t N, int64_t K, uint16_t* __restrict__ gw, int64_t t_lo,
+                                                      int64_t t_cnt) {
+  static_assert(!(GR && HALF), "half tiles: dense form");
   constexpr int BN = 256, BK = 256, MS = 32, NS = 4;
   constexpr int ROWB = 512;                    // bytes per LDS row (256 values)
   constexpr int SG = MS * ROWB, STAGE = 2 * SG;  // gy part, whole stage
-  constexpr int NW = 4, WN = 2, TM = 128, TN = 128, MI = 4, NI = 4;
+  constexpr int NW = 4, WN = 2, TM = 128, TN = HALF ? 64 : 128, MI = 4, NI = TN / 32;
   constexpr int D = STAGE / 1024 / NW;  // wave-wide 1 KB loads per wave per stage
   static_assert(D == 8, "stage split");
 
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
       t_step = G;
     }
   } else {
-    xcd_range(tpe, t_begin, t_end, t_step);
+    xcd_range(HALF ? 2 * t_cnt : t_cnt, t_begin, t_end, t_step);
   }
 
   // loads: waves 0-1 take gy (16 pieces of 1 KB = 2 rows), waves 2-3 take x;
@@ -294,16 +301,31 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        fa[i][ks][h] = tr_off(wm * TM + 32 * i, ks, h);
-        fb[i][ks][h] = (uint32_t)SG + tr_off(wn * TN + 32 * i, ks, h);
-      }
+      for (int h = 0; h < 2; ++h) fa[i][ks][h] = tr_off(wm * TM + 32 * i, ks, h);
+  // this wave's first column within the loaded tile (HALF: set per item)
+  int cb = wn * TN;
+  auto set_fb = [&]() {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fb[j][ks][h] = (uint32_t)SG + tr_off(cb + 32 * j, ks, h);
+  };
+  if constexpr (!HALF) set_fb();
 
   for (int64_t t0 = t_begin; t0 < t_end; t0 += t_step) {
     // expert (grouped form), then grouped order over its tiles: 4 row tiles
     // (n), column tiles (k) fastest
     int64_t t = t0, m_beg = 0, m_end = M;
     int32_t e = 0;
+    if constexpr (HALF) {
+      t = t_lo + t0 / 2;
+      cb = (int)(t0 & 1) * 128 + wn * TN;
+      set_fb();
+    } else if constexpr (!GR) {
+      t = t_lo + t0;
+    }
     if constexpr (GR) {
       e = __builtin_amdgcn_readfirstlane((int32_t)(t0 / tpe));
       t = t0 - (int64_t)e * tpe;
@@ -398,10 +420,21 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
     auto read_mma = [&](int64_t s_next, WgFrags& nxt, const WgFrags& cur) {
       read(s_next, nxt);
       mma(cur);
+      if constexpr (HALF) {
+        // 24 LDS reads, 16 MFMAs
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        }
       }
     };
     auto steady = [&](int64_t s, WgFrags& cur, WgFrags& nxt) {
@@ -451,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
     const int lg = lane >> 5, lc = lane & 31;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int64_t k = k0 + wn * TN + 32 * j + lc;
+      const int64_t k = k0 + cb + 32 * j + lc;
       if (k >= K) continue;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -476,8 +509,21 @@ hipError_t launch_wgrad_bf16(const WgradArgs& w) {
     int64_t grid = cus < total ? cus : total;
     if (grid >= kNumXcd) grid -= grid % kNumXcd;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(k_wgrad_pipe<false>, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x,
-                       (const int32_t*)nullptr, 1, w.M, w.N, w.K, w.gw);
+    // Whole rounds of tiles, then the rest. When the rest would occupy at
+    // most half the workgroups for a whole extra round (896 tiles on 256 CUs:
+    // 128 left over), a second launch splits each leftover tile into its two
+    // 128-column halves, one per workgroup, and the extra round takes about
+    // half as long.
+    const int64_t full = (total / grid) * grid, rest = total - full;
+    const bool halves = full > 0 && rest > 0 && 2 * rest <= grid;
+    hipLaunchKernelGGL((k_wgrad_pipe<false, false>), dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x,
+                       (const int32_t*)nullptr, 1, w.M, w.N, w.K, w.gw, (int64_t)0, halves ? full : total);
+    if (halves) {
+      int64_t g2 = 2 * rest;
+      if (g2 >= kNumXcd) g2 -= g2 % kNumXcd;
+      hipLaunchKernelGGL((k_wgrad_pipe<false, true>), dim3((unsigned)g2), dim3(256), 0, w.stream, w.gy, w.x,
+                         (const int32_t*)nullptr, 1, w.M, w.N, w.K, w.gw, full, rest);
+    }
     return hipGetLastError();
   }
   int64_t grid = cus < total ? cus : total;
@@ -496,8 +542,8 @@ hipError_t launch_grouped_wgrad_bf16(const GroupedWgradArgs& w) {
   int64_t grid = cus < total ? cus : total;
   if (grid >= kNumXcd) grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_wgrad_pipe<true>, dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x, w.offsets, w.E,
-                     w.Mtot, w.N, w.K, w.gw);
+  hipLaunchKernelGGL((k_wgrad_pipe<true, false>), dim3((unsigned)grid), dim3(256), 0, w.stream, w.gy, w.x, w.offsets,
+                     w.E, w.Mtot, w.N, w.K, w.gw, (int64_t)0, total);
   return hipGetLastError();
 }
 

@@ -697,15 +697,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_block(GemmParams p) {
     int32_t N32 = (int32_t)N;
     asm volatile("" : "+s"(N32));
     const int64_t corner = ti.m0 * N + ti.n0;
+    // lane offsets formed here, per tile: hoisted out of the tile loop they
+    // would stay live through the K loop, be spilled, and each reload would
+    // wait behind every store issued before it
+    int32_t ml0 = grp * TM + lrow, nl0 = wn * TN + 4 * g;
+    asm volatile("" : "+v"(ml0), "+v"(nl0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int32_t ml = grp * TM + 32 * i + lrow;
+      const int32_t ml = ml0 + 32 * i;
       if (ml >= m_lim) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int32_t nl = wn * TN + 32 * j + 8 * q + 4 * g;
+          const int32_t nl = nl0 + 32 * j + 8 * q;
           if (nl >= n_lim) continue;  // n_lim is a multiple of 128: the four are valid together
           const uint32_t o = (uint32_t)(ml * N32 + nl);
           const v16f& a = acc[i][j];

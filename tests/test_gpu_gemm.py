@@ -307,6 +307,22 @@ def test_wgrad_bf16(f, M, N, K):
     check_gemm(_host(gw), ref, S, True, f"wgrad {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 16632, 904), (128, 22784, 1024)])
+def test_wgrad_bf16_leftover_half_tiles(f, M, N, K):
+    """More 256 x 256 tiles than workgroups with at most half a round left over
+    (260 tiles with ragged last row and column tiles, and 356 tiles, on 256 CUs):
+    the leftover tiles run as 128-column halves in a second launch."""
+    import torch
+    g = synth.normal_bf16((M, N), 720 + M, 1e-3)
+    x = synth.normal_bf16((M, K), 721 + M, 1.0)
+    gw = torch.full((N, K), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_wgrad_bf16(to_dev_bf16(g), to_dev_bf16(x), gw)
+    torch.cuda.synchronize()
+    ref = oracle.wgrad_bf16(g, x)
+    S = oracle.wgrad_bf16(g, x, absolute=True)
+    check_gemm(_host(gw), ref, S, True, f"wgrad halves {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("counts,N,K", [([37, 0, 300, 1, 0, 513], 264, 136), ([64], 256, 256), ([0, 0], 64, 64),
                                          ([5] * 40, 64, 512), ([600, 0, 3], 520, 264),
                                          ([32, 31, 33, 95, 96, 97, 128], 128, 136)])
