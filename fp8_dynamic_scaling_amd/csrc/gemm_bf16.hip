@@ -226,6 +226,8 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tn = (N + BN - 1) / BN, tk = (K + BK - 1) / BK;
   const uint32_t lds0 = lds_addr(lds);
+  // 8-byte output stores where gw allows (K % 8 == 0 keeps every row aligned)
+  const bool vec_out = ((uintptr_t)gw & 7) == 0;
   // The XCD-aware split of the tile list (xcd_range). Grouped: the tiles of
   // an expert differ in length (its rows), so the XCDs get contiguous ranges
   // of equal total cost (stages + kTileCost per tile) rather than of equal
@@ -408,6 +410,9 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // transposed products (x fragment first): register 4 q + t of lane l in
+    // block (i, j) is n = 32 i + l % 32, k = 32 j + 8 q + 4 (l / 32) + t, so a
+    // lane stores 4 adjacent outputs at once
     auto mma = [&](const WgFrags& f) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i][ks], f.b[j][ks], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j][ks], f.a[i][ks], acc[i][j], 0, 0, 0);
     };
     auto read_mma = [&](int64_t s_next, WgFrags& nxt, const WgFrags& cur) {
       read(s_next, nxt);
@@ -479,20 +484,45 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
       mma(f1);
     }
 
-    // ---- epilogue: register r of lane l in block (i, j) holds row (n)
-    // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column (k) 32 j + l % 32 ----
-    const int lg = lane >> 5, lc = lane & 31;
+    // ---- epilogue: block (i, j), register 4 q + t of lane l: n = 32 i + l % 32,
+    // k = 32 j + 8 q + 4 (l / 32) + t of the wave's part; K % 8 == 0, so a
+    // lane's 4 columns are all inside K or all past it ----
+    int32_t nl0 = wm * TM + (lane & 31), kl0 = cb + 4 * (lane >> 5);
+    asm volatile("" : "+v"(nl0), "+v"(kl0));
+    uint16_t* const gwe = gw + (int64_t)e * N * K;
+    if (vec_out) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t k = k0 + cb + 32 * j + lc;
-      if (k >= K) continue;
+      for (int i = 0; i < MI; ++i) {
+        const int64_t n = n0 + nl0 + 32 * i;
+        if (n >= N) continue;
+        uint16_t* const row = gwe + n * K + k0;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t n = n0 + wm * TM + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (n < N) gw[((int64_t)e * N + n) * K + k] = f32_to_bf16_rne(acc[i][j][r]);
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int32_t kl = kl0 + 32 * j + 8 * q;
+            if (k0 + kl >= K) continue;
+            const v16f& a = acc[i][j];
+            const v2bf h01 = {(__bf16)a[4 * q], (__bf16)a[4 * q + 1]}, h23 = {(__bf16)a[4 * q + 2], (__bf16)a[4 * q + 3]};
+            *reinterpret_cast<uint2*>(row + kl) =
+                make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+          }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int64_t n = n0 + nl0 + 32 * i;
+        if (n >= N) continue;
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int32_t kl = kl0 + 32 * j + 8 * q;
+            if (k0 + kl >= K) continue;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) gwe[n * K + k0 + kl + t] = f32_to_bf16_rne(acc[i][j][4 * q + t]);
+          }
+      }
     }
   }
 }

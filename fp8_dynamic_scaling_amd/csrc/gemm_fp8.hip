@@ -329,9 +329,11 @@ static hipError_t launch_cfg(const GemmArgs& g) {
 
 template <bool AE5, bool BE5, int SK, bool OF32>
 static hipError_t launch_sk(const GemmArgs& g) {
-  // full precision: 64 x 64 per wave (the decoded operands need registers)
+  // 64 x 64 per wave: the accumulators, a blockwise step's partial product
+  // and the decoded operands of full precision all fit in registers (with
+  // 128 x 128 per wave they spilled)
   if (g.exact) return launch_cfg<128, 128, 2, 2, AE5, BE5, SK, OF32, true>(g);
-  return launch_cfg<256, 256, 2, 2, AE5, BE5, SK, OF32, false>(g);
+  return launch_cfg<128, 128, 2, 2, AE5, BE5, SK, OF32, false>(g);
 }
 
 template <bool AE5, bool BE5>
