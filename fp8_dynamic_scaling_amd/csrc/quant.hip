@@ -1389,6 +1389,17 @@ hipError_t launch_quant_tensor(const QuantArgs& a, void* ws) {
   return a.e5 ? launch_tensor_t<true>(a, (uint32_t*)ws) : launch_tensor_t<false>(a, (uint32_t*)ws);
 }
 
+// Grid of the looping 1-D quantizers: a grid of up to four resident rounds
+// (8 workgroups of 256 threads per CU) runs as one round of workgroups that
+// loop, which cut the 1 x 128 and MX activations of the Llama-4-style MoE
+// ([8192, 5120]) from 26.6 to 25.3 us and 28.8 to 26.8 us; larger grids keep one
+// workgroup per work item (capping the 16 x 8192 x 5120 MX weights at one round
+// measured 10% slower).
+static int64_t looping_grid(int64_t blocks) {
+  if (blocks > 2048 && blocks <= 8192) return 2048;
+  return blocks > 65536 ? 65536 : blocks;
+}
+
 template <bool E5>
 static hipError_t launch_block_t(const QuantArgs& a, int br, int bc) {
   const int64_t B = a.batch, R = a.rows, C = a.cols;
@@ -1398,8 +1409,7 @@ static hipError_t launch_block_t(const QuantArgs& a, int br, int bc) {
   if (vec && br == 1 && bc == 128) {
     const int64_t ngroups = B * R * nbc;
     const bool small = ngroups * 128 < ((int64_t)1 << 28);
-    int64_t blocks = (ngroups + 16 * (small ? 4 : 1) - 1) / (16 * (small ? 4 : 1));
-    if (blocks > 65536) blocks = 65536;
+    const int64_t blocks = looping_grid((ngroups + 16 * (small ? 4 : 1) - 1) / (16 * (small ? 4 : 1)));
     if (small)
       hipLaunchKernelGGL((k_quant_group1d<E5, 128, false, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
                          B * R, C, a.q, a.scale, a.inv, (uint8_t*)nullptr, a.fmax, a.eps, 0);
@@ -1431,8 +1441,7 @@ static hipError_t launch_mx_t(const QuantArgs& a, uint8_t* e8m0, int mode) {
   if (vec) {
     const int64_t ngroups = B * R * (C / 32);
     const bool small = ngroups * 32 < ((int64_t)1 << 28);
-    int64_t blocks = (ngroups + 64 * (small ? 4 : 1) - 1) / (64 * (small ? 4 : 1));
-    if (blocks > 65536) blocks = 65536;
+    const int64_t blocks = looping_grid((ngroups + 64 * (small ? 4 : 1) - 1) / (64 * (small ? 4 : 1)));
     if (small)
       hipLaunchKernelGGL((k_quant_group1d<E5, 32, true, 4>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x,
                          B * R, C, a.q, (float*)nullptr, (float*)nullptr, e8m0, a.fmax, a.eps, mode);
@@ -1507,8 +1516,7 @@ static hipError_t launch_mx_packed_t(const QuantArgs& a, uint8_t* e8m0, int mode
   if (R == 0 || C == 0) return hipSuccess;
   constexpr int U = 4;
   const int64_t tiles = R / GR * ((C + 2048 / GR - 1) / (2048 / GR));
-  int64_t blocks = (tiles + U - 1) / U;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t blocks = looping_grid((tiles + U - 1) / U);
   hipLaunchKernelGGL((k_quant_mx_packed<E5, GR, U>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.x, R, C, a.q,
                      e8m0, a.fmax, a.eps, mode);
   return hipGetLastError();
