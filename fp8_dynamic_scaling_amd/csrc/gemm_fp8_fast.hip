@@ -22,6 +22,8 @@
 //    under the row-XOR swizzle; rows past the end of an expert (or of N) load
 //    a valid clamped row and their outputs are never stored; K % 128 == 0
 //    means no K tail.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace fp8dyn {
@@ -58,8 +60,12 @@ namespace fp8dyn {
 //    E8M0 bytes for four stage pairs (512-deep K) come in one 16-byte load per
 //    lane with one stage in eight, into an LDS ring of two such blocks;
 //    otherwise a stage pair's bytes (one dword per row, 128-deep K) ride in a
-//    ring of 4 pairs with each even stage's loads. Each lane reads its byte
-//    straight into the MFMA's scale operand in the memory phase.
+//    ring of 4 pairs with each even stage's loads. In an even stage's memory
+//    phase each lane reads its rows' dwords of the pair (bytes: K blocks
+//    4 p .. 4 p + 3) and shifts them right by 8 g, so byte 0 is its K block
+//    of the even stage and byte 2 that of the odd one; the instruction's byte
+//    select picks it. A per-stage byte read and mask cost about a sixth of
+//    the MX GEMM's time on the Llama-4-style MoE shape.
 //  - EX (tensorwise and rowwise scales): full-precision accumulation. The
 //    compute phase decodes each pair of 32-byte fragments to bf16 and runs
 //    four v_mfma_f32_32x32x16_bf16 instead of one FP8 instruction: bytes
@@ -124,11 +130,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
 
   for (int64_t t = t_begin; t < t_end; t += t_step) {
     TileInfo ti;
+    // the column-tile count opaque per tile: the divisions below then form
+    // their reciprocal per tile instead of holding it in a register across the
+    // K loop (the MX form spilled it, and the reload waited for the previous
+    // tile's stores)
+    int64_t nt_t = nt;
+    asm volatile("" : "+s"(nt_t));
     if constexpr (GR) {
-      tile_of<BM, BN>(t, s_off, s_pref, p.E, nt, ti);
+      tile_of<BM, BN>(t, s_off, s_pref, p.E, nt_t, ti);
     } else {
       const int64_t mt = (p.M + BM - 1) / BM;
-      const int64_t g = t / (kGroupM * nt), rem = t % (kGroupM * nt);
+      const int64_t g = t / (kGroupM * nt_t), rem = t % (kGroupM * nt_t);
       const int64_t gm = (mt - g * kGroupM) < kGroupM ? (mt - g * kGroupM) : kGroupM;
       ti.e = 0;
       ti.m0 = (g * kGroupM + rem % gm) * BM;
@@ -216,7 +228,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     };
     v8i fa[MI], fb[NI];
     int sa[MI], sb[NI];
-    auto read = [&](int64_t s) {
+    // P: the stage's parity where MX reads scales (even stages only), else 0
+    auto read = [&](int64_t s, auto par) {
+      constexpr int P = decltype(par)::value;
       // slot offset opaque per call: the 12 addresses are formed per read, not
       // precomputed for all 4 slots (48 registers)
       uint32_t so = (uint32_t)((s & (NS - 1)) * STAGE);
@@ -233,23 +247,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
         const uint4 hi = *reinterpret_cast<const uint4*>(lds + so + fb_hi[j]);
         fb[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-      if constexpr (MXS) {
-        // this lane's E8M0 byte: K block 2 s + g of its row, byte 2 (s % 2) + g
-        // of the row's dword of the pair (16-byte rows: dword (s / 2) % 4)
-        const uint8_t* sp;
-        int rs;  // bytes per row
+      if constexpr (MXS && P == 0) {
+        // the row's dword of the pair s / 2 (16-byte rows: dword (s / 2) % 4),
+        // shifted so this lane's K block 2 s + g sits in byte 0 and 2 s + 2 + g
+        // in byte 2
+        const uint32_t* dp;
+        int rs;  // dwords per row
         if (scl16) {
-          sp = reinterpret_cast<const uint8_t*>(&s_scl[((s >> 3) & 1) * 4 * (BM + BN)]) + 4 * (int)((s >> 1) & 3);
-          rs = 16;
-        } else {
-          sp = reinterpret_cast<const uint8_t*>(&s_scl[((s >> 1) & 3) * (BM + BN)]);
+          dp = &s_scl[((s >> 3) & 1) * 4 * (BM + BN) + (int)((s >> 1) & 3)];
           rs = 4;
+        } else {
+          dp = &s_scl[((s >> 1) & 3) * (BM + BN)];
+          rs = 1;
         }
-        sp += 2 * (int)(s & 1) + lg;
+        const int sh = 8 * lg;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) sa[i] = sp[rs * (wm * TM + 32 * i + lrow)];
+        for (int i = 0; i < MI; ++i) sa[i] = (int)(dp[rs * (wm * TM + 32 * i + lrow)] >> sh);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) sb[j] = sp[rs * (BM + wn * TN + 32 * j + lrow)];
+        for (int j = 0; j < NI; ++j) sb[j] = (int)(dp[rs * (BM + wn * TN + 32 * j + lrow)] >> sh);
       }
     };
     // MX: the scale operands take their final values here, in the memory
@@ -271,7 +286,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    auto mma = [&]() {
+    auto mma = [&](auto par) {
+      constexpr int SEL = decltype(par)::value ? 2 : 0;  // MX: byte of the scale operands
       __builtin_amdgcn_s_setprio(1);
       if constexpr (EX) {
         // decode, two wait states (a VALU write right before a matrix-core
@@ -306,21 +322,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
         for (int j = 0; j < NI; ++j)
           if constexpr (MXS)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AE5 ? 1 : 0,
-                                                                        BE5 ? 1 : 0, 0, sa[i], 0, sb[j]);
+                                                                        BE5 ? 1 : 0, SEL, sa[i], SEL, sb[j]);
           else
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AE5 ? 1 : 0,
                                                                         BE5 ? 1 : 0, 0, 127, 0, 127);
+      if constexpr (SEL == 0 && MXS) {
+        // an even stage's products stay before the barrier that follows: they
+        // have no side effects, and the compiler would otherwise sink them
+        // into the odd stage's compute phase (their first use)
+        asm volatile(""
+                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[2][0]),
+                       "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]));
+      }
       __builtin_amdgcn_s_setprio(0);
     };
     // this wave's loads of stage u + 1 have landed: those issued after it
     // (stages u + 2 .. min(u + 3, nk - 1); one of two consecutive stages is
     // even and carries a scale load) may stay in flight
-    // (16-byte scale rows: a scale load rides with one stage in 8; waiting as
-    // if none were in flight waits at most one load longer)
+    // (16-byte scale rows: a scale load rides with the stages s, s % 8 == 0,
+    // so it is among the later ones when u % 8 is 5 or 6; counting it there
+    // keeps the wait from taking one of stage u + 2's loads early, which cost
+    // about a tenth of the MX GEMM's time on the Llama-4-style MoE shape)
     auto wait_next = [&](int64_t u) {
       if (u + 3 < nk) {
-        if (scl16) wait_vm_lgkm_and_barrier<2 * DH>();
-        else wait_vm_lgkm_and_barrier<2 * DH + X>();
+        if (scl16) {
+          if ((u & 7) == 5 || (u & 7) == 6) wait_vm_lgkm_and_barrier<2 * DH + 1>();
+          else wait_vm_lgkm_and_barrier<2 * DH>();
+        } else {
+          wait_vm_lgkm_and_barrier<2 * DH + X>();
+        }
       } else if (u + 2 < nk) {
         wait_vm_lgkm_and_barrier<DH>();  // stage nk - 1 is odd
       } else {
@@ -342,15 +372,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
     // (reads of stage u, loads of stage u + 3, own loads of stage u + 1
     // landed), barrier, compute phase (MFMAs of stage u), barrier
     if (grp == 1) wait_vm_lgkm_and_barrier<63>();
-    for (int64_t u = 0; u < nk; ++u) {
-      read(u);
+    auto phase = [&](int64_t u, auto par) {
+      read(u, par);
       if (u + 3 < nk) issue(u + 3);
       pin_scales();
       wait_next(u);
       __builtin_amdgcn_sched_barrier(0);
-      mma();
+      mma(par);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
+    };
+    if constexpr (MXS) {
+      // stage pairs (nk is even): the odd stage reuses the pair's scale dwords
+      for (int64_t u = 0; u < nk; u += 2) {
+        phase(u, std::integral_constant<int, 0>{});
+        phase(u + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      for (int64_t u = 0; u < nk; ++u) phase(u, std::integral_constant<int, 0>{});
     }
     if (grp == 0) asm volatile("s_barrier" ::: "memory");
 
