@@ -337,15 +337,25 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_pipe(const uint16_t* __restric
     const int64_t me = m_end - m_beg;
     // stages of 32 rows (even count: whole steady pairs); dense: M % 64 == 0
     const int64_t nk = GR ? ((me + 2 * MS - 1) / (2 * MS)) * 2 : M / MS;
-    const int64_t g = t / (kGroupM * tk), rem = t % (kGroupM * tk);
+    // (the column-tile count opaque per tile, so the divisions form their
+    // reciprocal here rather than hold it in a register across the loop)
+    int64_t tk_t = tk;
+    asm volatile("" : "+s"(tk_t));
+    const int64_t g = t / (kGroupM * tk_t), rem = t % (kGroupM * tk_t);
     const int64_t gm = (tn - g * kGroupM) < kGroupM ? (tn - g * kGroupM) : kGroupM;
     const int64_t n0 = uniform64((g * kGroupM + rem % gm) * BN), k0 = uniform64((rem / gm) * BK);
     const int64_t col0 = loads_g ? n0 : k0;
     uint32_t off[D];
+    // the lane id opaque per tile: the offsets below (products row * ld
+    // among them) are then formed per tile; hoisted out of the tile loop they
+    // were spilled and each tile's reload waited for the previous tile's
+    // stores
+    int32_t ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int row = 2 * (q0 + d) + (lane >> 5);
-      const int c = (lane & 31) ^ ((row & 7) << 2);
+      const int row = 2 * (q0 + d) + (ln >> 5);
+      const int c = (ln & 31) ^ ((row & 7) << 2);
       int64_t cc = col0 / 8 + c;
       cc = cc < nchunk ? cc : nchunk - 1;  // columns past N (or K) load a valid chunk
       off[d] = (uint32_t)((row * ld + 8 * cc) * 2);
