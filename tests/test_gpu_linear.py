@@ -50,15 +50,15 @@ def test_linear_tensorwise_forward_fp32(f, fast):
     check_gemm(y.cpu().numpy(), ref, S, False, "tensorwise linear fwd (fp32 out)", exact=not fast)
 
 
-@pytest.mark.parametrize("recipe", ["rowwise", "tensorwise"])
+@pytest.mark.parametrize("recipe,M", [("rowwise", 200), ("rowwise", 201), ("tensorwise", 208)])
 @pytest.mark.parametrize("K,N", [(384, 272), (256, 384)])
-def test_linear_small_fwd_bwd(f, recipe, K, N):
+def test_linear_small_fwd_bwd(f, recipe, M, K, N):
     """(384, 272): the rowwise forward's weight k-packed, its backward's row-major;
-    (256, 384): both k-packed (N % 128 == 0)."""
+    (256, 384): both k-packed (N % 128 == 0). Rowwise takes any M (201: odd, and the
+    weight gradient's row count not a multiple of its 64-row pipeline step); the
+    all-FP8 tensorwise backward needs M % 16 == 0."""
     import torch
     e4, e5 = _names(f)
-    # rowwise takes any M; the all-FP8 tensorwise backward needs M % 16 == 0
-    M = 200 if recipe == "rowwise" else 208
     x = synth.normal_bf16((M, K), 801, 1.0)
     synth.add_outliers(x, 802, 0.01, 50.0)
     wt = synth.normal_bf16((N, K), 803, 0.02)
