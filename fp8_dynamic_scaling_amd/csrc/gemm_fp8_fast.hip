@@ -67,8 +67,8 @@ namespace fp8dyn {
 //    select picks it. A per-stage byte read and mask cost about a sixth of
 //    the MX GEMM's time on the Llama-4-style MoE shape.
 //  - EX (tensorwise and rowwise scales): full-precision accumulation. The
-//    compute phase decodes each pair of 32-byte fragments to bf16 and runs
-//    four v_mfma_f32_32x32x16_bf16 instead of one FP8 instruction: bytes
+//    compute phase decodes each 32-byte fragment to bf16 once and runs four
+//    v_mfma_f32_32x32x16_bf16 per pair instead of one FP8 instruction: bytes
 //    [8 q, 8 q + 8) of every lane feed instruction q, on both operands, so
 //    the four instructions together take each K of the stage exactly once.
 template <bool AE5, bool BE5, int SK, bool OF32, bool GR, bool PKB, bool EX = false>
@@ -286,33 +286,62 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // EX: the stage's B fragments and first A row block decoded to bf16 in
+    // the memory phase, where the converts overlap the other group's
+    // products; pinned there (converts have no side effects and would
+    // otherwise sink past the barrier into the compute phase)
+    v8bf bd[NI][4], ad[2][4];
+    auto predecode = [&]() {
+      if constexpr (EX) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bd[j][q] = bf16x8<BE5>(fb[j], q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ad[0][q] = bf16x8<AE5>(fa[0], q);
+        asm volatile("" : "+v"(ad[0][0]), "+v"(ad[0][1]), "+v"(ad[0][2]), "+v"(ad[0][3]));
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          asm volatile("" : "+v"(bd[j][0]), "+v"(bd[j][1]), "+v"(bd[j][2]), "+v"(bd[j][3]));
+      }
+    };
     auto mma = [&](auto par) {
       constexpr int SEL = decltype(par)::value ? 2 : 0;  // MX: byte of the scale operands
       __builtin_amdgcn_s_setprio(1);
       if constexpr (EX) {
-        // decode, two wait states (a VALU write right before a matrix-core
-        // read of the same register is not seen), four BF16 instructions;
-        // sources stay live past the instructions that read them
+        // Each fragment decoded once per stage: both B column blocks and the
+        // first A row block in the memory phase (predecode), then every
+        // further A row block between the previous one's eight instructions
+        // (two converts after each), into the other of two buffers, so the
+        // matrix core runs while the converts issue. Every decoded fragment
+        // stays live to the end of the phase, so no decode reuses a register
+        // an issued instruction may still read.
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i) {
+          const int b = i & 1;
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            v8bf ab[4], bb[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              ab[q] = bf16x8<AE5>(fa[i], q);
-              bb[q] = bf16x8<BE5>(fb[j], q);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_nop 1" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < NI; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[q], bb[q], acc[i][j], 0, 0, 0);
-            asm volatile("" ::"v"(ab[0]), "v"(ab[1]), "v"(ab[2]), "v"(ab[3]), "v"(bb[0]), "v"(bb[1]), "v"(bb[2]),
-                         "v"(bb[3]));
-            __builtin_amdgcn_sched_barrier(0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[b][q], bd[j][q], acc[i][j], 0, 0, 0);
+          if (i + 1 < MI) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ad[b ^ 1][q] = bf16x8<AE5>(fa[i + 1], q);
+            // 4 NI instructions, 16 converts
+#pragma unroll
+            for (int k = 0; k < 4 * NI; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("" ::"v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[0][2]), "v"(ad[0][3]), "v"(ad[1][0]), "v"(ad[1][1]),
+                     "v"(ad[1][2]), "v"(ad[1][3]));
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          asm volatile("" ::"v"(bd[j][0]), "v"(bd[j][1]), "v"(bd[j][2]), "v"(bd[j][3]));
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         return;
       }
@@ -376,6 +405,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_pp(GemmParams p) {
       read(u, par);
       if (u + 3 < nk) issue(u + 3);
       pin_scales();
+      predecode();
       wait_next(u);
       __builtin_amdgcn_sched_barrier(0);
       mma(par);
