@@ -16,6 +16,8 @@
 
 namespace fp8dyn {
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
 // Row groups. One workgroup of 256 threads per row; the row (up to
 // 2048 * J elements) stays in registers between amax and cast.
@@ -1327,7 +1329,11 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(const uint16_t* __restri
         t0 = __fmul_rn(__fmul_rn(bf16_lo(w[k]), rstd32), bf16_lo(gw[k]));
         t1 = __fmul_rn(__fmul_rn(bf16_hi(w[k]), rstd32), bf16_hi(gw[k]));
       }
-      o[k] = (uint32_t)f32_to_bf16_rne(t0) | ((uint32_t)f32_to_bf16_rne(t1) << 16);
+      // gfx950's packed convert, two values per instruction: round to
+      // nearest even, the same bits as f32_to_bf16_rne for every non-NaN
+      // value (subnormals included); a NaN stays a NaN
+      const bf16x2_t h = {(__bf16)t0, (__bf16)t1};
+      o[k] = __builtin_bit_cast(uint32_t, h);
     }
     v[j] = make_uint4(o[0], o[1], o[2], o[3]);
     m = amax8(v[j], m);
