@@ -71,6 +71,19 @@ struct TJobSpec {
 };
 hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps, uint32_t* amax_words,
                                        hipStream_t stream);
+// Tensorwise quantization of two tensors (row-major codes only) in two
+// launches: a per-workgroup amax pass into `partials`, then a cast pass that
+// reduces them; no word needs clearing first. n % 8 == 0 for both tensors.
+struct TPairSpec {
+  const uint16_t* x;
+  int64_t n;
+  uint8_t* q;
+  float* scale;
+  float* inv;  // or nullptr
+};
+constexpr int kPairMaxAmaxBlocks = 2048;  // per tensor
+hipError_t launch_quant_tensor_pair(const TPairSpec* specs, bool e5, double fmax, double eps, float* partials,
+                                    hipStream_t stream);
 hipError_t launch_quant_mx(const QuantArgs& a, uint8_t* e8m0, int mode);
 hipError_t launch_quant_mx_packed(const QuantArgs& a, uint8_t* e8m0, int mode, int group_rows);
 
@@ -101,6 +114,9 @@ struct GemmArgs {
 hipError_t launch_gemm_fp8(const GemmArgs& g);
 // the direct-to-LDS kernel (K % 128 == 0, aligned operands); launch_gemm_fp8 picks it
 bool gemm_fp8_fast_eligible(const GemmArgs& g);
+// dense tensorwise / rowwise outputs small enough for the 64 x 64 tile form
+// of the generic kernel (at most one tile per CU)
+bool gemm_fp8_small_dense(int64_t M, int64_t N);
 hipError_t launch_gemm_fp8_fast(const GemmArgs& g);
 
 struct WgradArgs {

@@ -20,6 +20,8 @@
 // Accumulation follows "FP8 Training: Quantization, Autograd, Torchao",
 // section 5: both backward GEMMs use full precision; the forward takes the
 // caller's choice (the pages' recipe: fast accumulation).
+#include <cmath>
+
 #include "../../include/fp8dyn.h"
 #include "internal.hpp"
 
@@ -38,7 +40,7 @@ struct Bump {
 };
 
 struct FwdLayout {
-  void *qx, *qw, *sx, *ix, *sw, *iw, *wsx, *wsw;
+  void *qx, *qw, *sx, *ix, *sw, *iw, *wsx, *wsw, *part;
 };
 FwdLayout fwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r, size_t* total) {
   Bump b{ws};
@@ -52,6 +54,8 @@ FwdLayout fwd_layout(uint8_t* ws, int64_t M, int64_t N, int64_t K, fp8_recipe r,
   L.iw = b.take(4 * (tw ? 1 : (size_t)N));
   L.wsx = b.take(256);
   L.wsw = b.take(256);
+  // tensorwise: per-workgroup amax partials of x and w
+  L.part = tw ? b.take(4 * 2 * (size_t)kPairMaxAmaxBlocks) : nullptr;
   *total = b.off;
   return L;
 }
@@ -90,11 +94,18 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Shapes whose rowwise weight operands go k-packed: the forward's w [N][K]
 // (fp8_quant_row_kpacked + fp8_scaled_mm_kpacked), the backward's w^T [K][N]
-// (fp8_quant_col_kpacked + fp8_scaled_mm_kpacked, contraction over N).
-bool fwd_kpacked(int64_t N, int64_t K) {
-  return K > 0 && N % 16 == 0 && K % 128 == 0 && K <= 16384 && N * K < ((int64_t)1 << 31);
+// (fp8_quant_col_kpacked + fp8_scaled_mm_kpacked, contraction over N). Outputs
+// small enough for the 64 x 64 tile GEMM ([M][N] forward, [M][K] grad-input)
+// keep the row-major operands, which that GEMM reads.
+bool fwd_kpacked(int64_t M, int64_t N, int64_t K) {
+  return K > 0 && N % 16 == 0 && K % 128 == 0 && K <= 16384 && N * K < ((int64_t)1 << 31) &&
+         !gemm_fp8_small_dense(M, N);
 }
-bool bwd_kpacked(int64_t N, int64_t K) { return N % 128 == 0 && K % 16 == 0 && N * K < ((int64_t)1 << 30); }
+bool bwd_kpacked(int64_t M, int64_t N, int64_t K) {
+  return N % 128 == 0 && K % 16 == 0 && N * K < ((int64_t)1 << 30) && !gemm_fp8_small_dense(M, K);
+}
+
+bool bad_eps(double eps) { return !(std::isfinite(eps) && eps > 0.0); }
 
 }  // namespace
 
@@ -123,18 +134,32 @@ fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64
   FwdLayout L = fwd_layout((uint8_t*)ws, M, N, K, recipe, &need);
   const bool tw = recipe == FP8_RECIPE_TENSORWISE;
   fp8_status st;
-  if (tw) {
-    if ((st = fp8_quant_tensor(x, M * K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, L.wsx, 256,
+  if (tw && K > 0) {
+    // x and w in one amax launch and one cast launch
+    if (bad_eps(eps)) return FP8_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(w, 16)) return FP8_ERR_ALIGNMENT;
+    fp8_format e4f, e5f;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8_ERR_DEVICE;
+    if ((st = fp8_probe(dev, &e4f, &e5f)) != FP8_OK) return st;
+    const TPairSpec jobs[2] = {{x, M * K, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix},
+                               {w, N * K, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw}};
+    if ((st = as_status(launch_quant_tensor_pair(jobs, false, fp8_format_max(e4f), eps, (float*)L.part,
+                                                 (hipStream_t)stream))) != FP8_OK)
+      return st;
+  } else if (tw) {
+    // no contraction terms: empty-tensor scales, then the zero output
+    if ((st = fp8_quant_tensor(x, 0, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, L.wsx, 256,
                                stream)) != FP8_OK)
       return st;
-    if ((st = fp8_quant_tensor(w, N * K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw, L.wsw, 256,
+    if ((st = fp8_quant_tensor(w, 0, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw, L.wsw, 256,
                                stream)) != FP8_OK)
       return st;
   } else {
     if ((st = fp8_quant_row(x, 1, M, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qx, (float*)L.sx, (float*)L.ix, stream)) !=
         FP8_OK)
       return st;
-    if (fwd_kpacked(N, K)) {
+    if (fwd_kpacked(M, N, K)) {
       if ((st = fp8_quant_row_kpacked(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qw, (float*)L.sw, (float*)L.iw,
                                       stream)) != FP8_OK)
         return st;
@@ -166,7 +191,7 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
     if (!aligned(z, 4)) return FP8_ERR_ALIGNMENT;
     return as_status(launch_zero_fill(z, n * 2, (hipStream_t)stream));
   }
-  if (!gy || !x || !w || !gx || !gw) return FP8_ERR_INVALID_ARGUMENT;
+  if (!gy || !x || !w || !gx || !gw || bad_eps(eps)) return FP8_ERR_INVALID_ARGUMENT;
   if (N % 16 != 0 || K % 16 != 0) return FP8_ERR_ALIGNMENT;
   size_t need = 0;
   bwd_layout(nullptr, M, N, K, recipe, &need);
@@ -197,7 +222,7 @@ fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t*
         FP8_OK)
       return st;
     const size_t colws = quant_col_ws_bytes(1, N, K) > 0 ? quant_col_ws_bytes(1, N, K) : 256;
-    if (bwd_kpacked(N, K)) {
+    if (bwd_kpacked(M, N, K)) {
       // w^T k-packed as the grad-input GEMM's B operand
       if ((st = fp8_quant_col_kpacked(w, 1, N, K, FP8_E4M3_NATIVE, eps, (uint8_t*)L.qwt, (float*)L.swc, (float*)L.iwc,
                                       L.wscol, colws, stream)) != FP8_OK)

@@ -1074,6 +1074,96 @@ hipError_t launch_quant_tensor_multi_t(const TJobSpec* specs, int n, double eps,
 }
 
 // ---------------------------------------------------------------------------
+// Tensorwise quantization of two tensors in two launches with no cleared word
+// (the Linear forward's x and w: "FP8 Training: Quantization, Autograd,
+// Torchao", section 4, one scale per tensor from its amax; Figure 4 of "FP8
+// training on AMD GPUs with TorchTitan and TorchAO" names the same pairing of
+// two tensors in one kernel):
+//  - k_amax_pair: the maximum of each workgroup's range into partials[block];
+//  - k_cast_pair: each workgroup takes the maximum over its tensor's partials
+//    (maxima of non-NaN magnitudes: the same value in any order, so the scale
+//    is bit for bit the one of the single-tensor path), the tensor's first
+//    workgroup writes scale and inverse, and every workgroup casts its share.
+// For small layers the launch gaps dominate: this is two launches where the
+// single-tensor path takes three per tensor.
+struct PJob {
+  const uint16_t* x;  // n elements, n % 8 == 0
+  int64_t n;
+  uint8_t* q;
+  float* scale;
+  float* inv;         // or nullptr
+  int64_t amax_blk0, amax_blks, cast_blk0, cast_blks;
+};
+struct PJobs {
+  PJob j[2];
+  float* part;        // amax_blks of job 0, then of job 1
+  double fmax, eps;
+};
+
+__global__ __launch_bounds__(256) void k_amax_pair(const PJobs js) {
+  __shared__ float red[4];
+  const PJob& J = js.j[blockIdx.x >= js.j[1].amax_blk0 ? 1 : 0];
+  float m = amax_vec_range(J.x, J.n / 8, blockIdx.x - J.amax_blk0, J.amax_blks);
+  m = block_max<256>(m, red);
+  if (threadIdx.x == 0) js.part[blockIdx.x] = m;
+}
+
+template <bool E5>
+__global__ __launch_bounds__(256) void k_cast_pair(const PJobs js) {
+  __shared__ float red[4];
+  const PJob& J = js.j[blockIdx.x >= js.j[1].cast_blk0 ? 1 : 0];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < J.amax_blks; i += 256) m = fmaxf(m, js.part[J.amax_blk0 + i]);
+  m = block_max<256>(m, red);
+  float s, iv;
+  scale_from_amax(m, js.fmax, js.eps, s, iv);
+  const int64_t lb = blockIdx.x - J.cast_blk0;
+  if (lb == 0 && threadIdx.x == 0) {
+    J.scale[0] = s;
+    if (J.inv) J.inv[0] = iv;
+  }
+  const float fm = (float)js.fmax;
+  const int64_t nvec = J.n / 8;
+  const int64_t stride = J.cast_blks * 256;
+  for (int64_t i = lb * 256 + threadIdx.x; i < nvec; i += stride) st_nt8(J.q + 8 * i, quant8<E5>(ld_nt16(J.x + 8 * i), s, fm));
+}
+
+// partials: 2 * kPairMaxAmaxBlocks floats
+hipError_t launch_quant_tensor_pair(const TPairSpec* specs, bool e5, double fmax, double eps, float* partials,
+                                    hipStream_t stream) {
+  PJobs js{};
+  js.part = partials;
+  js.fmax = fmax;
+  js.eps = eps;
+  int64_t ab = 0, cb = 0;
+  for (int i = 0; i < 2; ++i) {
+    const TPairSpec& t = specs[i];
+    if (t.n <= 0 || t.n % 8 != 0) return hipErrorInvalidValue;
+    PJob& J = js.j[i];
+    J.x = t.x;
+    J.n = t.n;
+    J.q = t.q;
+    J.scale = t.scale;
+    J.inv = t.inv;
+    const int64_t nvec = t.n / 8;
+    J.amax_blk0 = ab;
+    J.amax_blks = amax_blocks(nvec);  // at most kPairMaxAmaxBlocks
+    ab += J.amax_blks;
+    int64_t cblocks = (nvec + 255) / 256;
+    if (cblocks > 4096) cblocks = 4096;
+    J.cast_blk0 = cb;
+    J.cast_blks = cblocks;
+    cb += cblocks;
+  }
+  hipLaunchKernelGGL(k_amax_pair, dim3((unsigned)ab), dim3(256), 0, stream, js);
+  if (e5)
+    hipLaunchKernelGGL(k_cast_pair<true>, dim3((unsigned)cb), dim3(256), 0, stream, js);
+  else
+    hipLaunchKernelGGL(k_cast_pair<false>, dim3((unsigned)cb), dim3(256), 0, stream, js);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Normalization fused with the rowwise quantization of its output ("FP8
 // Training: Quantization, Autograd, Torchao", section 8: the norm's output
 // write and the next layer's amax pass become one memory pass). One

@@ -395,10 +395,14 @@ FP8DYN_API fp8_status fp8_grouped_wgrad_bf16(const uint16_t* gy, const uint16_t*
  * scale each; ROWWISE: per row of x and of w, e4m3), then the scaled GEMM
  * with the accumulation use_fast_accum selects (as for fp8_scaled_mm; the
  * pages' recipe runs the forward with fast accumulation [P-TAO section 5]);
- * y [M][N] bf16 or fp32. ROWWISE
- * with N % 16 == 0, K % 128 == 0 and K <= 16384 writes w k-packed
- * (fp8_quant_row_kpacked, fp8_scaled_mm_kpacked). ws:
- * fp8_linear_ws_bytes(M, N, K, recipe) bytes. */
+ * y [M][N] bf16 or fp32. TENSORWISE quantizes x and w together, one amax
+ * launch and one cast launch for both (same codes and scales as two
+ * fp8_quant_tensor calls); x and w 16-byte aligned (else FP8_ERR_ALIGNMENT).
+ * ROWWISE with N % 16 == 0, K % 128 == 0 and K <= 16384 writes w k-packed
+ * (fp8_quant_row_kpacked, fp8_scaled_mm_kpacked), except for outputs of at
+ * most one 64 x 64 tile per compute unit, which the GEMM's small-output form
+ * takes row-major. eps as for the quantizers (else FP8_ERR_INVALID_ARGUMENT).
+ * ws: fp8_linear_ws_bytes(M, N, K, recipe) bytes. */
 FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                      int64_t K, fp8_recipe recipe, double eps, fp8_out out_type,
                                      int use_fast_accum, void* y, void* ws, size_t ws_bytes, void* stream);
@@ -414,7 +418,9 @@ FP8DYN_API fp8_status fp8_linear_fwd(const uint16_t* x, const uint16_t* w, int64
  *  - ROWWISE_BF16_WGRAD: the BF16 GEMM gy^T x ["FP8 training on AMD GPUs
  *    with TorchTitan and TorchAO" Figure 1 caption]; with N % 128 == 0 and
  *    K % 16 == 0 w^T is written k-packed (fp8_quant_col_kpacked) for the
- *    grad-input GEMM.
+ *    grad-input GEMM, unless gx has at most one 64 x 64 tile per compute
+ *    unit (then row-major, as in the forward).
+ * eps as for the quantizers (else FP8_ERR_INVALID_ARGUMENT).
  * Both FP8 GEMMs of the backward use full-precision accumulation [P-TAO
  * section 5]. */
 FP8DYN_API fp8_status fp8_linear_bwd(const uint16_t* gy, const uint16_t* x, const uint16_t* w,

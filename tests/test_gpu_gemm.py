@@ -44,12 +44,27 @@ def _host(out):
     return out.float().cpu().numpy().astype(np.float64)
 
 
+# Zero rows appended to A so that the output has more than 256 tiles of 64 x 64
+# (the dense GEMM's small-output form takes up to one such tile per compute
+# unit): the padded calls run the 256 x 256 ping-pong kernel, the unpadded ones
+# the small-output form, and the tests below pin both.
+PAD_ROWS = 64 * 257
+
+
+def _pad_rows(a, pad):
+    if not pad:
+        return a
+    return np.concatenate([a, np.zeros((PAD_ROWS, a.shape[1]), a.dtype)], axis=0)
+
+
+@pytest.mark.parametrize("pad", [False, True])
 @pytest.mark.parametrize("fast", [True, False])
-def test_code_pair_product_table(f, fast):
+def test_code_pair_product_table(f, fast, pad):
     """The exhaustive code-pair table through the matrix cores: row a of A holds code a
     at all 128 K positions, row b of B code b, so out[a][b] = 128 dec(a) dec(b), exactly
     (equal products need no alignment; the value fits fp32), for every pair of finite
-    codes: A in e4m3 and in e5m2, B in e4m3. Both accumulation modes."""
+    codes: A in e4m3 and in e5m2, B in e4m3. Both accumulation modes, both dense
+    kernels (pad: zero rows after the table, which must come out zero)."""
     import torch
     e4, e5 = _names(f)
     tb = oracle.decode(e4, np.arange(256))
@@ -59,22 +74,25 @@ def test_code_pair_product_table(f, fast):
     for fa, name in ((f.E4M3_NATIVE, e4), (f.E5M2_NATIVE, e5)):
         ta = oracle.decode(name, np.arange(256))
         fa_ok = np.isfinite(ta)
-        a = np.repeat(np.where(fa_ok, np.arange(256), 0).astype(np.uint8)[:, None], 128, axis=1)
-        out = _out((256, 256), True)
+        a = _pad_rows(np.repeat(np.where(fa_ok, np.arange(256), 0).astype(np.uint8)[:, None], 128, axis=1), pad)
+        out = _out((a.shape[0], 256), True)
         f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
                         use_fast_accum=fast)
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         want = 128.0 * np.outer(np.where(fa_ok, ta, 0.0), np.where(fb, tb, 0.0))
-        assert np.array_equal(got, want), (name, fast, int(np.sum(got != want)))
+        assert np.array_equal(got[:256], want), (name, fast, int(np.sum(got[:256] != want)))
+        assert not np.any(got[256:])
 
 
+@pytest.mark.parametrize("pad", [False, True])
 @pytest.mark.parametrize("fast", [True, False])
-def test_matrix_core_decodes_every_code(f, fast):
+def test_matrix_core_decodes_every_code(f, fast, pad):
     """A has code c at k = 0 of row c (zeros elsewhere); B row 0 holds the code of 1.0.
     out[c][0] must be exactly the oracle's value of code c, for all finite codes, both
     formats on the A side and the e4m3 format on the B side; both accumulation modes
-    (the full-precision one decodes the codes to bf16 with gfx950's converts)."""
+    (the full-precision one decodes the codes to bf16 with gfx950's converts), both
+    dense kernels (pad: zero rows after the codes)."""
     import torch
     e4, e5 = _names(f)
     one_b = oracle.encode(e4, [1.0])[0]
@@ -84,24 +102,25 @@ def test_matrix_core_decodes_every_code(f, fast):
         a[:, 0] = np.arange(256)
         fin = np.isfinite(tab)
         a[~fin, 0] = 0
+        a = _pad_rows(a, pad)
         b = np.zeros((16, 128), np.uint8)
         b[0, 0] = one_b
-        out = _out((256, 16), True)
+        out = _out((a.shape[0], 16), True)
         one = torch.ones(1, dtype=torch.float32, device="cuda:0")
         f.fp8_scaled_mm(to_dev(a), fa, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
                         use_fast_accum=fast)
         torch.cuda.synchronize()
-        got = out.cpu().numpy()[:, 0].astype(np.float64)
+        got = out.cpu().numpy()[:256, 0].astype(np.float64)
         assert np.array_equal(got[fin], tab[fin]), name
-        assert np.all(out.cpu().numpy()[:, 1:] == 0)
+        assert np.all(out.cpu().numpy()[:, 1:] == 0) and not np.any(out.cpu().numpy()[256:])
     # and e4m3 codes on the B side
     tab = oracle.decode(e4, np.arange(256))
     fin = np.isfinite(tab)
     b = np.zeros((256, 128), np.uint8)
     b[:, 0] = np.where(fin, np.arange(256), 0)
-    a = np.zeros((16, 128), np.uint8)
+    a = _pad_rows(np.zeros((16, 128), np.uint8), pad)
     a[0, 0] = one_b
-    out = _out((16, 256), True)
+    out = _out((a.shape[0], 256), True)
     one = torch.ones(1, dtype=torch.float32, device="cuda:0")
     f.fp8_scaled_mm(to_dev(a), f.E4M3_NATIVE, to_dev(b), f.E4M3_NATIVE, f.SCALE_TENSOR, one, one, f.OUT_F32, out,
                     use_fast_accum=fast)
@@ -125,8 +144,12 @@ def test_small_integer_products_are_exact(f):
     assert np.array_equal(out.cpu().numpy().astype(np.float64), av.astype(np.float64) @ bv.T.astype(np.float64))
 
 
+# up to 256 output tiles of 64 x 64: the small-output form; more: the ping-pong
+# kernel where K % 128 == 0 (1100 x 1040: 306 tiles, ragged in both), else the
+# generic 128 x 128 tiles (1100 x 1040 x 272)
 @pytest.mark.parametrize("M,N,K", [(256, 512, 512), (1, 16, 16), (100, 72, 48), (300, 200, 384), (513, 260, 1040),
-                                   (300, 520, 1152), (64, 64, 128), (200, 136, 256), (2100, 8200, 128)])
+                                   (300, 520, 1152), (64, 64, 128), (200, 136, 256), (1024, 1024, 256),
+                                   (1100, 1040, 384), (1100, 1040, 272), (2100, 8200, 128)])
 @pytest.mark.parametrize("scaling", ["tensor", "row"])
 @pytest.mark.parametrize("out_f32", [True, False])
 @pytest.mark.parametrize("fast", [True, False])

@@ -50,13 +50,17 @@ def test_linear_tensorwise_forward_fp32(f, fast):
     check_gemm(y.cpu().numpy(), ref, S, False, "tensorwise linear fwd (fp32 out)", exact=not fast)
 
 
-@pytest.mark.parametrize("recipe,M", [("rowwise", 200), ("rowwise", 201), ("tensorwise", 208)])
-@pytest.mark.parametrize("K,N", [(384, 272), (256, 384)])
+@pytest.mark.parametrize("recipe,M,K,N", [(r, m, k, n) for r, m in (("rowwise", 200), ("rowwise", 201), ("tensorwise", 208))
+                                           for k, n in ((384, 272), (256, 384))] +
+                         [("rowwise", 2752, 384, 384), ("rowwise", 2753, 384, 272), ("tensorwise", 2752, 384, 384)])
 def test_linear_small_fwd_bwd(f, recipe, M, K, N):
-    """(384, 272): the rowwise forward's weight k-packed, its backward's row-major;
-    (256, 384): both k-packed (N % 128 == 0). Rowwise takes any M (201: odd, and the
-    weight gradient's row count not a multiple of its 64-row pipeline step); the
-    all-FP8 tensorwise backward needs M % 16 == 0."""
+    """M about 200: outputs of at most 256 tiles of 64 x 64, so both GEMMs of the
+    rowwise recipe take row-major weights (the small-output GEMM). M 2752 / 2753:
+    more tiles, so the rowwise forward's weight goes k-packed (N % 16 == 0, K %
+    128 == 0) and so does the backward's w^T when N % 128 == 0 (384; with 272 it
+    stays row-major). Rowwise takes any M (201, 2753: odd, and the weight
+    gradient's row count not a multiple of its 64-row pipeline step); the all-FP8
+    tensorwise backward needs M % 16 == 0."""
     import torch
     e4, e5 = _names(f)
     x = synth.normal_bf16((M, K), 801, 1.0)
@@ -102,6 +106,32 @@ def test_linear_small_fwd_bwd(f, recipe, M, K, N):
     for name, got, ref, S, ex in (("y", y, ref_y, S_y, False), ("gx", gx, ref_gx, S_gx, True),
                                   ("gw", gw, ref_gw, S_gw, True)):
         check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}", exact=ex)
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 512, 512), (2048, 1024, 1536), (8192, 4096, 1024), (48, 16, 8)])
+def test_linear_tensorwise_fwd_matches_separate_quantizers(f, M, K, N):
+    """The tensorwise forward quantizes x and w in one amax launch (maxima per
+    workgroup) and one cast launch; its output must equal, bit for bit, two
+    fp8_quant_tensor calls (one atomic amax word each) followed by fp8_scaled_mm on
+    the same shape: equal codes and inverse scales give the same GEMM. 8192 x 4096:
+    x takes the full 2048 amax workgroups; 48 x 16 x 8: one workgroup each."""
+    import torch
+    x = synth.normal_bf16((M, K), 811, 1.0)
+    synth.add_outliers(x, 812, 0.001, 50.0)
+    wt = synth.normal_bf16((N, K), 813, 0.02)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(wt)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_linear_fwd(xd, wd, f.RECIPE_TENSORWISE, EPS, f.OUT_BF16, y, _ws(f, M, N, K, f.RECIPE_TENSORWISE))
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
+    qw = torch.empty((N, K), dtype=torch.uint8, device="cuda:0")
+    sx, ix, sw, iw = (torch.empty(1, dtype=torch.float32, device="cuda:0") for _ in range(4))
+    ws = torch.empty(f.fp8_quant_tensor_ws_bytes(), dtype=torch.uint8, device="cuda:0")
+    f.fp8_quant_tensor(xd, f.E4M3_NATIVE, EPS, qx, sx, ix, ws)
+    f.fp8_quant_tensor(wd, f.E4M3_NATIVE, EPS, qw, sw, iw, ws)
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    f.fp8_scaled_mm(qx, f.E4M3_NATIVE, qw, f.E4M3_NATIVE, f.SCALE_TENSOR, ix, iw, f.OUT_BF16, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
 def test_linear_tensorwise_bwd_needs_m_multiple_of_16(f):
