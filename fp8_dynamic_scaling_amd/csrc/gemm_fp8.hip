@@ -318,9 +318,13 @@ static hipError_t launch_cfg(const GemmArgs& g) {
   GemmParams p{g.a, g.b, g.sa, g.sb, g.offsets, g.E, g.M, g.N, g.K, g.out};
   const int64_t nt = (g.N + BN - 1) / BN;
   const int64_t tiles_ub = g.offsets ? ((g.M + BM - 1) / BM + g.E) * nt : ((g.M + BM - 1) / BM) * nt;
+  // fewer tiles than CUs: one workgroup per tile (the kernel then deals tiles
+  // by workgroup index); else a persistent grid, a multiple of the XCD count
   int64_t grid = device_cus();
-  if (tiles_ub < grid) grid = tiles_ub;
-  if (grid >= kNumXcd) grid -= grid % kNumXcd;
+  if (tiles_ub < grid)
+    grid = tiles_ub;
+  else if (grid >= kNumXcd)
+    grid -= grid % kNumXcd;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((k_gemm_fp8<BM, BN, WM, WN, AE5, BE5, SK, OF32, EX>), dim3((unsigned)grid),
                      dim3(WM * WN * 64), 0, g.stream, p);
