@@ -108,18 +108,31 @@ def test_linear_small_fwd_bwd(f, recipe, M, K, N):
         check_gemm(got.float().cpu().numpy(), ref, S, True, f"{recipe} {name}", exact=ex)
 
 
-@pytest.mark.parametrize("M,K,N", [(256, 512, 512), (2048, 1024, 1536), (8192, 4096, 1024), (48, 16, 8)])
-def test_linear_tensorwise_fwd_matches_separate_quantizers(f, M, K, N):
+@pytest.mark.parametrize("M,K,N,special", [(256, 512, 512, None), (2048, 1024, 1536, None),
+                                           (8192, 4096, 1024, None), (48, 16, 8, None),
+                                           (256, 512, 512, "zero_x"), (256, 512, 512, "inf_w"),
+                                           (256, 512, 512, "nan_x")])
+def test_linear_tensorwise_fwd_matches_separate_quantizers(f, M, K, N, special):
     """The tensorwise forward quantizes x and w in one amax launch (maxima per
     workgroup) and one cast launch; its output must equal, bit for bit, two
     fp8_quant_tensor calls (one atomic amax word each) followed by fp8_scaled_mm on
     the same shape: equal codes and inverse scales give the same GEMM. 8192 x 4096:
-    x takes the full 2048 amax workgroups; 48 x 16 x 8: one workgroup each."""
+    x takes the full 2048 amax workgroups; 48 x 16 x 8: one workgroup each.
+    Degenerate inputs: an all-zero x (amax 0: the eps-clamped scale), an infinity in
+    w (scale 0, so inf * 0 codes and NaN outputs), NaNs in x (dropped by the amax,
+    cast to NaN codes)."""
     import torch
     x = synth.normal_bf16((M, K), 811, 1.0)
     synth.add_outliers(x, 812, 0.001, 50.0)
     wt = synth.normal_bf16((N, K), 813, 0.02)
     xd, wd = to_dev_bf16(x), to_dev_bf16(wt)
+    if special == "zero_x":
+        xd.zero_()
+    elif special == "inf_w":
+        wd[3, 100] = float("inf")
+    elif special == "nan_x":
+        xd[7, 9] = float("nan")
+        xd[200, 511] = float("nan")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     f.fp8_linear_fwd(xd, wd, f.RECIPE_TENSORWISE, EPS, f.OUT_BF16, y, _ws(f, M, N, K, f.RECIPE_TENSORWISE))
     qx = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
